@@ -1,0 +1,169 @@
+"""Seeded synthetic inputs for the attention forward path (shared by tests and bench).
+
+This module holds NO attention arithmetic: only random-number generation, shapes and the
+block-sparse index-list generator. Both the oracle side and the GPU side consume its outputs.
+
+Recipe:
+* Q/K/V: torch CPU generator seeded per tensor, float32 N(0, 1) samples rounded to bfloat16
+  with round-to-nearest-even (torch's `.to(torch.bfloat16)`), contiguous [B, L, H, D].
+* Workload k uses seeds 1000*k + {0: Q, 1: K, 2: V, 3: index lists, 4: sampled rows}.
+* Block-sparse lists (per query head, 64x64 blocks), following the A-shape / vertical-slash /
+  block-sparse pattern vocabulary of the MInference article and the per-head dynamic patterns
+  of the SparseAccelerate page: key block 0 (the "first block"), the local band of the 64 key
+  blocks kb in [qb-63, qb] (diagonal included), each remaining causal block kb <= qb chosen
+  independently with probability 0.03, and 1000 vertical key columns drawn uniformly without
+  replacement over [0, L) per head. Lists are sorted and unique.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "randn_bf16",
+    "make_qkv",
+    "make_blocksparse_lists",
+    "sampled_rows",
+    "dense_causal_lists",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # seed base = 1000 * index
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    Dqk: int
+    Dv: int
+    causal: bool
+    scale: float
+    kind: str           # "prefill" | "decode" | "mla_decode" | "blocksparse"
+    mla: bool = False   # V is the first Dv columns of K (no separate V tensor)
+
+
+WORKLOADS = {
+    "tiny_causal": Workload("tiny_causal", 1, B=1, Hq=2, Hkv=2, Lq=256, Lk=256, Dqk=64, Dv=64,
+                            causal=True, scale=1.0 / math.sqrt(64), kind="prefill"),
+    "gqa_prefill_8k": Workload("gqa_prefill_8k", 2, B=1, Hq=32, Hkv=8, Lq=8192, Lk=8192, Dqk=128,
+                               Dv=128, causal=True, scale=1.0 / math.sqrt(128), kind="prefill"),
+    "gqa_decode_4k": Workload("gqa_decode_4k", 3, B=16, Hq=32, Hkv=8, Lq=1, Lk=4096, Dqk=128,
+                              Dv=128, causal=False, scale=1.0 / math.sqrt(128), kind="decode"),
+    "mla_decode_64k": Workload("mla_decode_64k", 4, B=8, Hq=16, Hkv=1, Lq=1, Lk=65536, Dqk=576,
+                               Dv=512, causal=False, scale=1.0 / math.sqrt(192), kind="mla_decode",
+                               mla=True),
+    "blocksparse_128k": Workload("blocksparse_128k", 5, B=1, Hq=32, Hkv=8, Lq=131072, Lk=131072,
+                                 Dqk=128, Dv=128, causal=True, scale=1.0 / math.sqrt(128),
+                                 kind="blocksparse"),
+}
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def randn_bf16(shape, seed: int) -> torch.Tensor:
+    """float32 N(0,1) from a seeded CPU generator, rounded to bf16 (RNE). CPU tensor."""
+    return torch.randn(tuple(shape), generator=_gen(seed), dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_qkv(w: Workload, b=None, lq=None, lk=None):
+    """Q [B, Lq, Hq, Dqk], K [B, Lk, Hkv, Dqk], V [B, Lk, Hkv, Dv] (V is None for MLA) on CPU.
+
+    b / lq / lk optionally override the sizes (for reduced-size parity cases of the same recipe).
+    """
+    B = w.B if b is None else b
+    Lq = w.Lq if lq is None else lq
+    Lk = w.Lk if lk is None else lk
+    base = 1000 * w.index
+    q = randn_bf16((B, Lq, w.Hq, w.Dqk), base + 0)
+    k = randn_bf16((B, Lk, w.Hkv, w.Dqk), base + 1)
+    v = None if w.mla else randn_bf16((B, Lk, w.Hkv, w.Dv), base + 2)
+    return q, k, v
+
+
+def make_blocksparse_lists(B, Hq, Lq, Lk, seed, block=64, local_blocks=64, p_extra=0.03,
+                           n_cols=1000, first_block=True):
+    """CSR index lists over (b, h, qb) -> key-block ids and over (b, h) -> key columns.
+
+    Returns int32 numpy arrays (blk_ptr [B*Hq*nqb+1], blk_idx, col_ptr [B*Hq+1], col_idx).
+    Sorted, unique, every block id < ceil(Lk/64), every column < Lk.
+    The local band is aligned bottom-right: query block qb ends at query row
+    min((qb+1)*64, Lq) - 1, which sees keys up to that row + Lk - Lq.
+    """
+    g = _gen(seed)
+    nqb = -(-Lq // block)
+    nkb = -(-Lk // block)
+    off = Lk - Lq
+    ptr = [0]
+    idx_parts = []
+    col_ptr = [0]
+    col_parts = []
+    qb_ar = np.arange(nqb)
+    # last visible key block of each query block (bottom-right causal)
+    last_row = np.minimum((qb_ar + 1) * block, Lq) - 1
+    diag_kb = np.minimum((last_row + off) // block, nkb - 1)
+    for _b in range(B):
+        for _h in range(Hq):
+            extra = torch.rand((nqb, nkb), generator=g).numpy() < p_extra
+            kb = np.arange(nkb)[None, :]
+            causal_blk = kb <= diag_kb[:, None]
+            local = (kb <= diag_kb[:, None]) & (kb > diag_kb[:, None] - local_blocks)
+            sel = local | (extra & causal_blk)
+            if first_block:
+                sel[:, 0] = True
+            for qb in range(nqb):
+                ids = np.nonzero(sel[qb])[0].astype(np.int32)
+                idx_parts.append(ids)
+                ptr.append(ptr[-1] + ids.size)
+            nc = min(n_cols, Lk)
+            cols = torch.randperm(Lk, generator=g)[:nc].numpy().astype(np.int32)
+            cols.sort()
+            col_parts.append(cols)
+            col_ptr.append(col_ptr[-1] + nc)
+    blk_idx = np.concatenate(idx_parts) if idx_parts else np.zeros(0, np.int32)
+    col_idx = np.concatenate(col_parts) if col_parts else np.zeros(0, np.int32)
+    return (np.asarray(ptr, np.int32), blk_idx.astype(np.int32),
+            np.asarray(col_ptr, np.int32), col_idx.astype(np.int32))
+
+
+def dense_causal_lists(B, Hq, Lq, Lk, block=64):
+    """Lists that name every causal key block and no column (block-sparse == dense causal)."""
+    nqb = -(-Lq // block)
+    nkb = -(-Lk // block)
+    off = Lk - Lq
+    ptr = [0]
+    parts = []
+    for _ in range(B * Hq):
+        for qb in range(nqb):
+            last_row = min((qb + 1) * block, Lq) - 1
+            d = min((last_row + off) // block, nkb - 1)
+            ids = np.arange(0, d + 1, dtype=np.int32)
+            parts.append(ids)
+            ptr.append(ptr[-1] + ids.size)
+    return (np.asarray(ptr, np.int32), np.concatenate(parts).astype(np.int32),
+            np.zeros(B * Hq + 1, np.int32), np.zeros(0, np.int32))
+
+
+def sampled_rows(L, n, seed, edge=64):
+    """Query rows used for sampled parity at full size: the first `edge` rows, the last `edge`
+    rows, and n - 2*edge rows drawn uniformly without replacement from the rest. Sorted."""
+    if n >= L:
+        return np.arange(L)
+    head = np.arange(0, edge)
+    tail = np.arange(L - edge, L)
+    mid_pool = L - 2 * edge
+    m = n - 2 * edge
+    mid = torch.randperm(mid_pool, generator=_gen(seed))[:m].numpy() + edge
+    return np.sort(np.concatenate([head, mid, tail]))
