@@ -1,0 +1,152 @@
+/*
+ * attn.h — C ABI of libattn.so: fused, tiled softmax-attention forward for AMD MI355X (gfx950).
+ *
+ *   O = softmax(scale · Q·Kᵀ + mask) · V, computed tile by tile with an online (running max /
+ *   running sum) softmax, so the score matrix S and the weights P never reach HBM.
+ *
+ * Sources of the operation (cited by page title and section):
+ *   - "Resumen Técnico: FlashMLA-ETAP", section "Mecanismo Central": the standard flow
+ *     S = Q·Kᵀ, P = softmax(S), O = P·V that every entry point computes.
+ *   - "Activar Flash Attention con llama.cpp para optimizar la inferencia", section
+ *     "¿Qué es Flash Attention y por qué es crucial para llama.cpp?": tiling with iterative,
+ *     local updates in on-chip memory instead of materialising the intermediates in HBM.
+ *   - Same page, FAQ entry on Grouped Query Attention: K/V shared by groups of query heads.
+ *   - "Resumen Técnico: FlashMLA-ETAP", sections "Planteamiento del Problema" and "Detalles de
+ *     Implementación": MLA decode — 16 query heads, head dim 576 over one jointly compressed
+ *     latent KV, very short queries against a KV context of up to 64K.
+ *   - MInference article (7minutos.es), paragraphs on the A-shape, vertical-slash and
+ *     block-sparse patterns and the dynamically built sparse indices; "SparseAccelerate:
+ *     Acelerando Modelos de Lenguaje", section "Patrones de Atención Dispersa Dinámicos".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors. Q is [B, Lq, Hq, Dqk], K is [B, Lk, Hkv, Dqk], V is [B, Lk, Hkv, Dv], O is
+ *   [B, Lq, Hq, Dv], all bfloat16, described by attn_tensor_t: a DEVICE pointer plus element
+ *   strides for the batch, sequence and head dimensions; the head-dim stride is 1. The data
+ *   pointer must be 16-byte aligned and every stride a multiple of 8 elements. Contiguous
+ *   [B, L, H, D] has stride_h = D, stride_l = H·D, stride_b = L·H·D.
+ * LSE. Optional fp32 log-sum-exp of each query row, natural log of Σ_j exp(scale·q·k_j) over
+ *   the visible keys, DEVICE pointer, contiguous [B, Hq, Lq]. Pass NULL to skip it. A row with
+ *   no visible key gets O = 0 and LSE = -inf.
+ * GQA. Hq must be a multiple of Hkv; query head h reads KV head h / (Hq / Hkv).
+ * MLA. Pass v with the same data pointer and strides as k and Dv = 512 < Dqk = 576: V is then
+ *   the first 512 columns of the latent K, read from the same memory (no copy).
+ * Causal masking is aligned bottom-right: query row i sees key j iff j <= i + Lk - Lq. With
+ *   Lq = 1 the single query sees the whole cache. Rows with i + Lk - Lq < 0 see nothing.
+ * Arithmetic. bf16 inputs, fp32 accumulation (MFMA) and fp32 softmax statistics; O is
+ *   rounded to bf16 with round-to-nearest-even.
+ * Streams. `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *   asynchronously; the library never synchronises. Calls on one stream run in order.
+ * Ownership. The caller allocates and owns every buffer (including split-KV partials). The
+ *   library allocates no device memory, keeps no pointer after returning, and is re-entrant.
+ * Errors. Every entry point returns ATTN_OK (0) or a negative attn_status. On an error nothing
+ *   is launched and no output is written; attn_last_error() then holds a message (per thread).
+ *   Asynchronous device faults surface at the caller's next synchronisation.
+ */
+#ifndef SPARSE_ATTN_AMD_ATTN_H_
+#define SPARSE_ATTN_AMD_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_tensor {
+  void* data;         /* device pointer to bf16 elements (const for inputs) */
+  int64_t stride_b;   /* element stride between batch entries */
+  int64_t stride_l;   /* element stride between sequence positions */
+  int64_t stride_h;   /* element stride between heads; the head-dim stride is 1 */
+} attn_tensor_t;
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,  /* a size, stride, alignment, pointer or scale is invalid */
+  ATTN_ERR_UNSUPPORTED = -2,  /* valid arguments that this build has no kernel for */
+  ATTN_ERR_WORKSPACE = -3,    /* split-KV partial buffers missing */
+  ATTN_ERR_LAUNCH = -4        /* the HIP runtime refused the launch (message in last_error) */
+} attn_status_t;
+
+/*
+ * attn_fwd — dense attention forward (prefill; any Lq, Lk).
+ * Supported head dims: (Dqk, Dv) = (64, 64) or (128, 128).
+ * Errors: INVALID_ARG if any of B, Hq, Hkv, Lq, Lk < 1, Hq % Hkv != 0, scale not finite, a
+ * NULL q/k/v/o pointer, misalignment; UNSUPPORTED for other head dims; LAUNCH on HIP failure.
+ */
+int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o, float* lse,
+             int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal, float scale,
+             void* stream);
+
+/*
+ * Split-KV decode: attn_fwd_splitkv writes per-split partials, attn_combine_lse merges them.
+ * Split s covers keys [s·C, min((s+1)·C, Lk)) with C = 64·ceil(ceil(Lk / S) / 64); a split
+ * with no visible key writes O_s = 0 and LSE_s = -inf (weight 0 in the merge). The merge is
+ * M = max_s LSE_s, w_s = exp(LSE_s - M), LSE = M + ln Σ w_s, O = Σ w_s O_s / Σ w_s.
+ * Sizes: o_part is fp32 [S, B, Hq, Lq, Dv], lse_part is fp32 [S, B, Hq, Lq], both contiguous
+ * DEVICE buffers owned by the caller. num_splits must lie in [1, ceil(Lk / 64)].
+ * Supported head dims: (64, 64), (128, 128) and the MLA latent (576, 512).
+ */
+
+/* Split count the library would pick for MI355X (256 CUs): enough workgroups to fill the chip
+ * while each split keeps at least a few 64-key tiles. Pure function of its arguments; returns
+ * a value in [1, ceil(Lk/64)], or ATTN_ERR_INVALID_ARG for sizes < 1. */
+int attn_splitkv_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
+
+/* Bytes of o_part plus lse_part for these sizes (0 on invalid sizes). */
+size_t attn_splitkv_workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits);
+
+/* Errors: as attn_fwd, plus INVALID_ARG for num_splits out of range and WORKSPACE when
+ * o_part or lse_part is NULL or not 16-byte aligned. */
+int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v,
+                     float* o_part, float* lse_part, int num_splits,
+                     int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal,
+                     float scale, void* stream);
+
+/* Merges the partials into O (bf16, strided like attn_fwd's O) and LSE (fp32 [B, Hq, Lq] or
+ * NULL). Errors: INVALID_ARG for sizes < 1, NULL or misaligned pointers, Dv not in
+ * {64, 128, 512}; WORKSPACE when o_part or lse_part is NULL. */
+int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits,
+                     attn_tensor_t o, float* lse, int B, int Hq, int Lq, int Dv, void* stream);
+
+/*
+ * attn_fwd_blocksparse — attention over a per-query-head union of listed key blocks and
+ * vertical key columns (the block-sparse / A-shape / vertical-slash index lists), with the
+ * causal mask applied on top when `causal` is set. Each key is counted once even when it is
+ * both inside a listed block and listed as a column.
+ *
+ *   blk_ptr [B·Hq·nqb + 1], blk_idx — CSR over (b, h, qb) row-major, nqb = ceil(Lq / 64):
+ *       blk_idx[blk_ptr[r] .. blk_ptr[r+1]) are the key-block ids (key block kb = keys
+ *       [64·kb, 64·kb + 64)) visible to the 64 query rows [64·qb, 64·qb + 64).
+ *   col_ptr [B·Hq + 1], col_idx — CSR over (b, h): key positions visible to every row of
+ *       that head (subject to the causal mask).
+ * All four are DEVICE int32 arrays; blk_idx (col_idx) may be NULL only when every block
+ * (column) list is empty. Each list must be sorted ascending without duplicates,
+ * block ids in [0, ceil(Lk/64)), columns in [0, Lk). Their contents are NOT checked on the
+ * device (that would need a host copy): call attn_blocksparse_check on host copies.
+ * block_m and block_n must both be 64. Supported head dims: (64, 64), (128, 128).
+ */
+int attn_fwd_blocksparse(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                         float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                         int causal, float scale, int block_m, int block_n,
+                         const int32_t* blk_ptr, const int32_t* blk_idx,
+                         const int32_t* col_ptr, const int32_t* col_idx, void* stream);
+
+/* Validates block-sparse index lists given as HOST pointers (same layout as above):
+ * monotone pointers starting at 0, sorted unique ids, ids in range. Returns ATTN_OK or
+ * ATTN_ERR_INVALID_ARG with a message naming the first bad entry. Touches no GPU. */
+int attn_blocksparse_check(const int32_t* blk_ptr, const int32_t* blk_idx,
+                           const int32_t* col_ptr, const int32_t* col_idx,
+                           int B, int Hq, int Lq, int Lk, int block_m, int block_n);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). Valid until the next call. */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_AMD_ATTN_H_ */

@@ -46,6 +46,7 @@ import numpy as np
 __all__ = [
     "attention",
     "attention_rows",
+    "attention_query_rows",
     "attention_transposed",
     "blocksparse_row_mask",
     "combine_lse",
@@ -140,10 +141,18 @@ def attention_rows(q, k, v, scale, causal, b, h, rows, allowed=None):
     [len(rows), Lk] of extra visibility (block-sparse union), ANDed with the causal mask.
     Returns (O [len(rows), Dv] fp64, LSE [len(rows)] fp64).
     """
-    _, lq, hq, _, lk, hkv, _ = _check_shapes(q, k, v)
+    _, lq, hq, _, _, _, _ = _check_shapes(q, k, v)
+    rows = np.asarray(rows, dtype=np.int64)
+    return attention_query_rows(q[b, rows, h, :], k, v, scale, causal, b, h, rows, lq, hq, allowed)
+
+
+def attention_query_rows(q_rows, k, v, scale, causal, b, h, rows, lq, hq, allowed=None):
+    """As `attention_rows`, with the query rows given directly: q_rows [len(rows), Dqk] holds
+    Q[b, rows, h, :] of a query tensor with Lq = lq positions and Hq = hq heads."""
+    lk, hkv = k.shape[1], k.shape[2]
     rows = np.asarray(rows, dtype=np.int64)
     kvh = kv_head_of(h, hq, hkv)
-    qr = np.asarray(q[b, rows, h, :], dtype=np.float64)
+    qr = np.asarray(q_rows, dtype=np.float64)
     kr = np.asarray(k[b, :, kvh, :], dtype=np.float64)
     vr = np.asarray(v[b, :, kvh, :], dtype=np.float64)
     s = _scores(qr, kr, np.float64(scale))

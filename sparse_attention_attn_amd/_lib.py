@@ -1,0 +1,253 @@
+"""ctypes marshalling for libattn.so (see include/attn.h for the contract of each call)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_LAUNCH = -4
+
+# Every function include/attn.h declares.
+EXPORTED_SYMBOLS = (
+    "attn_fwd",
+    "attn_splitkv_num_splits",
+    "attn_splitkv_workspace_bytes",
+    "attn_fwd_splitkv",
+    "attn_combine_lse",
+    "attn_fwd_blocksparse",
+    "attn_blocksparse_check",
+    "attn_status_string",
+    "attn_last_error",
+)
+
+
+class AttnError(RuntimeError):
+    """A library call returned a negative attn_status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        self.status = status
+        super().__init__(f"{fn} failed with {_status_name(status)} ({status}): {message}")
+
+
+class AttnTensorC(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_l", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+    ]
+
+
+def lib_path() -> str:
+    return os.environ.get("ATTN_LIB", os.path.join(_PKG_DIR, "libattn.so"))
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libattn.so once. Raises RuntimeError if it is missing (no fallback exists)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build the HIP library first "
+            "(python -m sparse_attention_attn_amd.build)")
+    lib = ctypes.CDLL(path)
+    T = AttnTensorC
+    i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    fp = ctypes.POINTER(ctypes.c_float)
+    ip = ctypes.c_void_p
+    lib.attn_fwd.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_splitkv_num_splits.argtypes = [i32] * 7
+    lib.attn_splitkv_num_splits.restype = i32
+    lib.attn_splitkv_workspace_bytes.argtypes = [i32] * 5
+    lib.attn_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_splitkv.argtypes = [T, T, T, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                     f32, vp]
+    lib.attn_fwd_splitkv.restype = i32
+    lib.attn_combine_lse.argtypes = [vp, vp, i32, T, vp, i32, i32, i32, i32, vp]
+    lib.attn_combine_lse.restype = i32
+    lib.attn_fwd_blocksparse.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                         f32, i32, i32, ip, ip, ip, ip, vp]
+    lib.attn_fwd_blocksparse.restype = i32
+    lib.attn_blocksparse_check.argtypes = [ip, ip, ip, ip, i32, i32, i32, i32, i32, i32]
+    lib.attn_blocksparse_check.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    del fp, i64
+    _LIB = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def attn_last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def _check(fn: str, status: int):
+    if status != ATTN_OK:
+        raise AttnError(fn, status, attn_last_error())
+
+
+# ------------------------------------------------------------------------------------ helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _tensor_desc(t, name):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, L, H, D], got shape {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous head dimension")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return AttnTensorC(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _opt_ptr(t, name, dtype_name="float32"):
+    if t is None:
+        return None
+    torch = _torch()
+    if t.dtype != getattr(torch, dtype_name):
+        raise TypeError(f"{name} must be {dtype_name}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ------------------------------------------------------------------------------- entry points
+def attn_fwd(q, k, v, o, lse=None, causal=True, scale=None, stream=None):
+    """Dense attention forward: O (and LSE [B, Hq, Lq] fp32 if given) from Q, K, V."""
+    B, Lq, Hq, Dqk = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    if scale is None:
+        scale = Dqk ** -0.5
+    st = load_library().attn_fwd(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
+        _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
+        _stream(stream, q.device))
+    _check("attn_fwd", st)
+    return o
+
+
+def attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv) -> int:
+    return int(load_library().attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv))
+
+
+def attn_splitkv_workspace_bytes(B, Hq, Lq, Dv, num_splits) -> int:
+    return int(load_library().attn_splitkv_workspace_bytes(B, Hq, Lq, Dv, num_splits))
+
+
+def attn_fwd_splitkv(q, k, v, o_part, lse_part, causal=False, scale=None, stream=None):
+    """Per-split partials: o_part fp32 [S, B, Hq, Lq, Dv], lse_part fp32 [S, B, Hq, Lq]."""
+    B, Lq, Hq, Dqk = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    S = o_part.shape[0]
+    if scale is None:
+        scale = Dqk ** -0.5
+    st = load_library().attn_fwd_splitkv(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"),
+        _opt_ptr(o_part, "o_part"), _opt_ptr(lse_part, "lse_part"), S, B, Hq, Hkv, Lq, Lk, Dqk,
+        Dv, int(bool(causal)), float(scale), _stream(stream, q.device))
+    _check("attn_fwd_splitkv", st)
+    return o_part, lse_part
+
+
+def attn_combine_lse(o_part, lse_part, o, lse=None, stream=None):
+    """Merge split partials into O (bf16 [B, Lq, Hq, Dv], strided) and LSE."""
+    S, B, Hq, Lq, Dv = o_part.shape
+    st = load_library().attn_combine_lse(
+        _opt_ptr(o_part, "o_part"), _opt_ptr(lse_part, "lse_part"), S, _tensor_desc(o, "o"),
+        _opt_ptr(lse, "lse"), B, Hq, Lq, Dv, _stream(stream, o.device))
+    _check("attn_combine_lse", st)
+    return o
+
+
+def splitkv_decode(q, k, v, o, lse=None, causal=False, scale=None, num_splits=None, stream=None,
+                   workspace=None):
+    """Convenience: allocate partials (unless given) and run attn_fwd_splitkv + attn_combine_lse.
+
+    The MLA latent shape passes v = k[..., :512] (a view of k: same pointer and strides)."""
+    torch = _torch()
+    B, Lq, Hq, Dqk = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    S = num_splits or attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv)
+    if workspace is None:
+        o_part = torch.empty((S, B, Hq, Lq, Dv), dtype=torch.float32, device=q.device)
+        lse_part = torch.empty((S, B, Hq, Lq), dtype=torch.float32, device=q.device)
+    else:
+        o_part, lse_part = workspace
+    attn_fwd_splitkv(q, k, v, o_part, lse_part, causal=causal, scale=scale, stream=stream)
+    attn_combine_lse(o_part, lse_part, o, lse, stream=stream)
+    return o
+
+
+def _int_ptr(a, name):
+    """Device int32 tensor -> pointer (the kernel reads the lists on the GPU)."""
+    torch = _torch()
+    if a.dtype != torch.int32 or not a.is_cuda or not a.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    return ctypes.c_void_p(a.data_ptr())
+
+
+def attn_fwd_blocksparse(q, k, v, o, blk_ptr, blk_idx, col_ptr, col_idx, lse=None, causal=True,
+                         scale=None, block_m=64, block_n=64, stream=None):
+    """Block-sparse forward over CSR lists (int32 GPU tensors, layout in include/attn.h)."""
+    B, Lq, Hq, Dqk = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    if scale is None:
+        scale = Dqk ** -0.5
+    st = load_library().attn_fwd_blocksparse(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
+        _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
+        block_m, block_n, _int_ptr(blk_ptr, "blk_ptr"), _int_ptr(blk_idx, "blk_idx"),
+        _int_ptr(col_ptr, "col_ptr"), _int_ptr(col_idx, "col_idx"), _stream(stream, q.device))
+    _check("attn_fwd_blocksparse", st)
+    return o
+
+
+def attn_blocksparse_check(blk_ptr, blk_idx, col_ptr, col_idx, B, Hq, Lq, Lk, block_m=64,
+                           block_n=64) -> int:
+    """Validate HOST index lists (numpy int32 arrays). Returns ATTN_OK or raises AttnError."""
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+            for x in (blk_ptr, blk_idx, col_ptr, col_idx)]
+    ptrs = [ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(None) for a in arrs]
+    st = load_library().attn_blocksparse_check(*ptrs, B, Hq, Lq, Lk, block_m, block_n)
+    _check("attn_blocksparse_check", st)
+    return st

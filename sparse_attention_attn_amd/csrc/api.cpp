@@ -1,0 +1,178 @@
+// api.cpp — the extern "C" entry points of libattn.so: validate on the host, then launch.
+// Nothing here allocates device memory or synchronises; see include/attn.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <exception>
+#include <string>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+#include "validate.hpp"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int launch_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  return attn::fail(ATTN_ERR_LAUNCH, fn, hipGetErrorString(e));
+}
+
+void fill_fwd(attn::FwdArgs& a, const attn_tensor_t& q, const attn_tensor_t& k,
+              const attn_tensor_t& v, const attn_tensor_t& o, float* lse, int B, int Hq, int Hkv,
+              int Lq, int Lk, int causal, float scale) {
+  a.q = static_cast<const uint16_t*>(q.data);
+  a.k = static_cast<const uint16_t*>(k.data);
+  a.v = static_cast<const uint16_t*>(v.data);
+  a.o = static_cast<uint16_t*>(o.data);
+  a.lse = lse;
+  a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
+  a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
+  a.v_sb = v.stride_b; a.v_sl = v.stride_l; a.v_sh = v.stride_h;
+  a.o_sb = o.stride_b; a.o_sl = o.stride_l; a.o_sh = o.stride_h;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.off = Lk - Lq;
+  a.sl2 = scale * kLog2e;
+  a.xcd_remap = 0;
+  a.blk_ptr = a.blk_idx = a.col_ptr = a.col_idx = nullptr;
+  a.nkb = (Lk + 63) / 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o, float* lse,
+             int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal, float scale,
+             void* stream) {
+  static const char* fn = "attn_fwd";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_attention_args(fn, attn::Op::kDense, q, k, v, &o, lse, B, Hq, Hkv, Lq,
+                                        Lk, Dqk, Dv, scale);
+    if (st != ATTN_OK) return st;
+    attn::FwdArgs a;
+    fill_fwd(a, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, causal, scale);
+    a.n_qtiles = (Lq + attn::kDenseBlockM - 1) / attn::kDenseBlockM;
+    return launch_status(fn, attn::launch_fwd_dense(a, Dqk, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_splitkv_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
+  return attn::pick_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv);
+}
+
+size_t attn_splitkv_workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits) {
+  return attn::workspace_bytes(B, Hq, Lq, Dv, num_splits);
+}
+
+int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o_part,
+                     float* lse_part, int num_splits, int B, int Hq, int Hkv, int Lq, int Lk,
+                     int Dqk, int Dv, int causal, float scale, void* stream) {
+  static const char* fn = "attn_fwd_splitkv";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_attention_args(fn, attn::Op::kSplit, q, k, v, nullptr, nullptr, B, Hq,
+                                        Hkv, Lq, Lk, Dqk, Dv, scale);
+    if (st != ATTN_OK) return st;
+    if ((st = attn::check_num_splits(fn, num_splits, Lk)) != ATTN_OK) return st;
+    if (o_part == nullptr || lse_part == nullptr)
+      return attn::fail(ATTN_ERR_WORKSPACE, fn, "o_part / lse_part is NULL");
+    if ((reinterpret_cast<uintptr_t>(o_part) & 15u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+      return attn::fail(ATTN_ERR_WORKSPACE, fn, "o_part must be 16-byte and lse_part 4-byte aligned");
+    attn::SplitArgs a;
+    a.q = static_cast<const uint16_t*>(q.data);
+    a.k = static_cast<const uint16_t*>(k.data);
+    a.v = static_cast<const uint16_t*>(v.data);
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
+    a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
+    a.v_sb = v.stride_b; a.v_sl = v.stride_l; a.v_sh = v.stride_h;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.off = Lk - Lq;
+    a.sl2 = scale * kLog2e;
+    a.num_splits = num_splits;
+    a.chunk = attn::split_chunk(Lk, num_splits);
+    a.ncolblk = (a.g * Lq + attn::kSplitCols - 1) / attn::kSplitCols;
+    return launch_status(fn, attn::launch_splitkv(a, Dqk, Dv, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits, attn_tensor_t o,
+                     float* lse, int B, int Hq, int Lq, int Dv, void* stream) {
+  static const char* fn = "attn_combine_lse";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_combine_args(fn, o_part, lse_part, num_splits, o, lse, B, Hq, Lq, Dv);
+    if (st != ATTN_OK) return st;
+    attn::CombineArgs a;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.o = static_cast<uint16_t*>(o.data);
+    a.lse = lse;
+    a.o_sb = o.stride_b; a.o_sl = o.stride_l; a.o_sh = o.stride_h;
+    a.B = B; a.Hq = Hq; a.Lq = Lq; a.S = num_splits;
+    return launch_status(fn, attn::launch_combine(a, Dv, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_fwd_blocksparse(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                         float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                         int causal, float scale, int block_m, int block_n,
+                         const int32_t* blk_ptr, const int32_t* blk_idx, const int32_t* col_ptr,
+                         const int32_t* col_idx, void* stream) {
+  static const char* fn = "attn_fwd_blocksparse";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_attention_args(fn, attn::Op::kSparse, q, k, v, &o, lse, B, Hq, Hkv, Lq,
+                                        Lk, Dqk, Dv, scale);
+    if (st != ATTN_OK) return st;
+    if (block_m != 64 || block_n != 64)
+      return attn::fail(ATTN_ERR_UNSUPPORTED, fn, "block_m and block_n must be 64");
+    // blk_idx / col_idx may be NULL when every list is empty: the kernel then never reads them.
+    if (blk_ptr == nullptr || col_ptr == nullptr)
+      return attn::fail(ATTN_ERR_INVALID_ARG, fn, "blk_ptr / col_ptr is NULL");
+    attn::FwdArgs a;
+    fill_fwd(a, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, causal, scale);
+    a.n_qtiles = (Lq + attn::kSparseBlockM - 1) / attn::kSparseBlockM;
+    a.blk_ptr = blk_ptr;
+    a.blk_idx = blk_idx;
+    a.col_ptr = col_ptr;
+    a.col_idx = col_idx;
+    return launch_status(fn, attn::launch_fwd_blocksparse(a, Dqk, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_blocksparse_check(const int32_t* blk_ptr, const int32_t* blk_idx, const int32_t* col_ptr,
+                           const int32_t* col_idx, int B, int Hq, int Lq, int Lk, int block_m,
+                           int block_n) {
+  attn::clear_last_error();
+  return attn::check_blocksparse_lists("attn_blocksparse_check", blk_ptr, blk_idx, col_ptr,
+                                       col_idx, B, Hq, Lq, Lk, block_m, block_n);
+}
+
+const char* attn_status_string(int status) { return attn::status_string(status); }
+
+const char* attn_last_error(void) { return attn::last_error_cstr(); }
+
+}  // extern "C"

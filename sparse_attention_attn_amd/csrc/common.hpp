@@ -1,0 +1,128 @@
+// common.hpp — device-side building blocks for the gfx950 attention kernels.
+//
+// Lane layouts used here were measured on MI355X (gfx950) with an in-bounds probe of the
+// compiler builtins, and are restated where used:
+//
+//  v_mfma_f32_32x32x16_bf16  A[32x16], B[16x32], D[32x32]
+//    A: lane l holds row m = l%32, k = 8*(l/32) + i (i = 0..7)
+//    B: lane l holds col n = l%32, k = 8*(l/32) + i
+//    D: lane l holds col n = l%32, rows m = 8*(j/4) + 4*(l/32) + j%4 (j = 0..15)
+//  v_mfma_f32_16x16x32_bf16  A[16x32], B[32x16], D[16x16]
+//    A: lane l holds row m = l%16, k = 8*(l/16) + i
+//    B: lane l holds col n = l%16, k = 8*(l/16) + i
+//    D: lane l holds col n = l%16, rows m = 4*(l/16) + j (j = 0..3)
+//  ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives in slot j the element
+//    (i % 4) of the 8-byte row addressed by lane 4*j + i/4 of the same group.
+//  global_load_lds_dwordx4: lane l's 16 bytes land at LDS (M0 base) + 16*l.
+//
+// Because a contraction is a sum over k, any permutation of the k index is allowed as long
+// as both operands use the same one; the kernels exploit that to feed the score accumulator
+// registers straight back into the P·V product without a trip through LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bf16_t;  // storage type of bf16 in memory
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global load reinterpreted as 8 bf16.
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+}
+// 16-byte LDS read (ds_read_b128).
+__device__ __forceinline__ bf16x8 lds_read_bf16x8(const char* lds_base, uint32_t byte_off) {
+  uint4 u = *reinterpret_cast<const uint4*>(lds_base + byte_off);
+  return __builtin_bit_cast(bf16x8, u);
+}
+// Two transposed 8-byte LDS reads -> one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const char* lds_base, uint32_t off_lo,
+                                                   uint32_t off_hi) {
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_base + off_lo));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_base + off_hi));
+  uint2 ulo = __builtin_bit_cast(uint2, lo);
+  uint2 uhi = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+}
+
+// Asynchronous 16-byte global -> LDS copy. lds_wave_base must be identical across the wave;
+// lane l's bytes land at lds_wave_base + 16*l.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const gbl_void_t*)gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// fp32 -> bf16 bits, round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a;
+  __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7) {
+  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3),
+                                               pack_bf16x2(a4, a5), pack_bf16x2(a6, a7)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// ------------------------------------------------------------------------------------------
+// Swizzled LDS tile layout. A tile holds ROWS rows of D bf16 (CPR = D/8 chunks of 16 bytes
+// per row). Row r's chunk c is stored in 16-byte slot r*CPR + (c ^ swz(r)); the XOR only
+// touches the low bits of c, so it stays inside the row. The swizzle makes both readers
+// conflict-free on the 64 x 4-byte LDS banks: the MFMA K-operand read (16 consecutive rows,
+// one chunk each) and the transposed V read (4..16 rows x 2..4 chunks per instruction).
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct Swz;
+template <>
+struct Swz<64> {  // 8 chunks per row
+  static __device__ __forceinline__ uint32_t f(uint32_t r) {
+    return (((r >> 1) & 1u) << 2) | ((r >> 2) & 3u);
+  }
+};
+template <>
+struct Swz<128> {  // 16 chunks per row
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r & 3u) << 2) | ((r >> 2) & 3u); }
+};
+template <>
+struct Swz<576> {  // 72 chunks per row: XOR inside aligned groups of 8 chunks
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return (r >> 1) & 7u; }
+};
+
+template <int D>
+__device__ __forceinline__ uint32_t slot_of(uint32_t r, uint32_t c) {
+  return r * (D / 8) + (c ^ Swz<D>::f(r));
+}
+// byte offset of element (r, e) of a D-wide tile (e must stay inside one 16-byte chunk group)
+template <int D>
+__device__ __forceinline__ uint32_t elem_off(uint32_t r, uint32_t e) {
+  return slot_of<D>(r, e >> 3) * 16u + (e & 7u) * 2u;
+}
+
+}  // namespace attn

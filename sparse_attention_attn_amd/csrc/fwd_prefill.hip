@@ -1,0 +1,448 @@
+// fwd_prefill.hip — fused attention forward for prefill (dense, causal or not, GQA) and for
+// block-sparse index lists, on gfx950.
+//
+// What is computed: O = softmax(scale·Q·Kᵀ + mask)·V and LSE per query row ("Resumen Técnico:
+// FlashMLA-ETAP", section "Mecanismo Central"), tile by tile with running softmax statistics
+// kept on chip ("Activar Flash Attention con llama.cpp para optimizar la inferencia", section
+// "¿Qué es Flash Attention y por qué es crucial para llama.cpp?"). The block-sparse variant
+// visits only the listed key blocks plus the listed vertical key columns of each query head
+// (MInference article, paragraphs on the A-shape / vertical-slash / block-sparse patterns and
+// the dynamically built sparse indices).
+//
+// Work decomposition: one workgroup owns 32*NW query rows of one (batch, query head); each
+// wave owns 32 rows. Keys stream through LDS in 64-key tiles (K tile + V tile), copied by
+// gfx950's asynchronous global->LDS loads into a two-stage ring so the copy of tile t+1
+// overlaps the math on tile t.
+//
+// Per tile and wave, the product is formed transposed, Sᵀ = K·Qᵀ, with 32x32x16 bf16 MFMA:
+// K (64 keys x D) is the A operand read from LDS, Qᵀ is the B operand held in registers for
+// the whole loop. In the Sᵀ accumulator each lane holds 16 keys of ONE query, so the row max
+// and row sum need only in-lane math plus one exchange between lanes l and l^32, and the
+// same registers, rounded to bf16, are directly the B operand Pᵀ of Oᵀ += Vᵀ·Pᵀ. Vᵀ comes
+// from the row-major V tile via the LDS transpose read. (The transposition here serves
+// register layout; the M-padding reason the FlashMLA-ETAP page gives for its transposed flow
+// does not arise with 32- or 16-row MFMA tiles.)
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int BN = 64;  // keys per tile
+
+// Tile source: where the 64 key rows of a tile come from.
+enum TileKind : int { kDenseTile = 0, kColumnTile = 1 };
+
+template <int D>
+struct TileCfg {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * D * 2;      // one K or V tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K + V
+  static constexpr int INSTR = TILE_BYTES / 1024;    // 1 KiB DMA instructions per tile
+  static constexpr int KSTEPS = D / 16;              // 32x32x16 MFMA steps over the head dim
+  static constexpr int DVB = D / 32;                 // 32-wide output column blocks
+};
+
+// Issue the asynchronous copy of one K tile and one V tile into LDS stage `st`.
+// key_of(r) must return a valid key row index (callers clamp), so every load is in bounds.
+template <int D, int NW, class KeyOf>
+__device__ __forceinline__ void issue_tile(const FwdArgs& a, char* st, const uint16_t* kbase,
+                                           const uint16_t* vbase, KeyOf key_of, int w, int l) {
+  using C = TileCfg<D>;
+  static_assert(C::INSTR % NW == 0, "tile copy must split evenly over the waves");
+#pragma unroll
+  for (int ii = 0; ii < C::INSTR / NW; ++ii) {
+    const int i = w + NW * ii;
+    const uint32_t slot = (uint32_t)i * 64u + (uint32_t)l;
+    const uint32_t r = slot / C::CPR;
+    const uint32_t c = (slot % C::CPR) ^ Swz<D>::f(r);
+    const int key = key_of((int)r);
+    dma16(kbase + (int64_t)key * a.k_sl + c * 8, st + i * 1024);
+    dma16(vbase + (int64_t)key * a.v_sl + c * 8, st + C::TILE_BYTES + i * 1024);
+  }
+}
+
+template <int D>
+struct WaveState {
+  bf16x8 qop[TileCfg<D>::KSTEPS];
+  f32x16 acc[TileCfg<D>::DVB];
+  float m;     // running max of scale*log2(e)*s (same in lanes l and l^32)
+  float lsum;  // lane-partial running sum of exp2(t - m)
+};
+
+// Math of one tile for one wave. kidx(local key) gives the key position (or -1 if the slot
+// holds no key); need_mask selects the masked path.
+template <int D, class KeyIdx>
+__device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, const char* st,
+                                          int row, bool need_mask, KeyIdx kidx, int l) {
+  using C = TileCfg<D>;
+  const char* kt = st;
+  const char* vt = st + C::TILE_BYTES;
+  const int h = l >> 5;
+  const uint32_t rr = (uint32_t)(l & 31);
+
+  // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks)
+  f32x16 s0 = {}, s1 = {};
+  const uint32_t sw0 = Swz<D>::f(rr), sw1 = Swz<D>::f(rr + 32);
+#pragma unroll
+  for (int s = 0; s < C::KSTEPS; ++s) {
+    const uint32_t c = (uint32_t)(2 * s + h);
+    const bf16x8 k0 = lds_read_bf16x8(kt, (rr * C::CPR + (c ^ sw0)) * 16u);
+    const bf16x8 k1 = lds_read_bf16x8(kt, ((rr + 32) * C::CPR + (c ^ sw1)) * 16u);
+    s0 = mfma32(k0, ws.qop[s], s0);
+    s1 = mfma32(k1, ws.qop[s], s1);
+  }
+
+  // ---- mask: slot (block kb, j) holds local key 32*kb + 8*(j/4) + 4*h + j%4
+  if (need_mask) {
+    const int lim = a.causal ? row + a.off : 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kl = 8 * (j >> 2) + 4 * h + (j & 3);
+      const int k0i = kidx(kl);
+      const int k1i = kidx(kl + 32);
+      if (k0i < 0 || k0i > lim) s0[j] = -INFINITY;
+      if (k1i < 0 || k1i > lim) s1[j] = -INFINITY;
+    }
+  }
+
+  // ---- online softmax (exp2 domain)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+  mx = fmaxf(mx, xor_shuffle(mx, 32));
+  const float mnew = fmaxf(ws.m, mx * a.sl2);
+  const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+  const float alpha = fast_exp2(ws.m - muse);
+  ws.m = mnew;
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s0[j] = fast_exp2(fmaf(s0[j], a.sl2, -muse));
+    s1[j] = fast_exp2(fmaf(s1[j], a.sl2, -muse));
+    psum += s0[j] + s1[j];
+  }
+  ws.lsum = ws.lsum * alpha + psum;
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int b = 0; b < C::DVB; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ws.acc[b][j] *= alpha;
+  }
+
+  // ---- Pᵀ operands: k-step ks covers local keys 16*ks .. 16*ks+15
+  bf16x8 pop[4];
+  pop[0] = pack_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
+  pop[1] = pack_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
+  pop[2] = pack_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
+  pop[3] = pack_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+
+  // ---- Oᵀ += Vᵀ·Pᵀ. Operand slot i of lane l covers key 16*ks + 8*(i/4) + 4*(l/32) + i%4,
+  // fetched with two transposed reads: lane 4j+c of each 16-lane group addresses
+  // row 16*ks + 4*(l/32) + j (+8 for the second read) at column dv0 + 4c.
+  const int G = l >> 4;
+  const int jj = (l & 15) >> 2;
+  const int cc = l & 3;
+  const int hh = G >> 1;
+#pragma unroll
+  for (int b = 0; b < C::DVB; ++b) {
+    const uint32_t dv = (uint32_t)(32 * b + 16 * (G & 1) + 4 * cc);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t rlo = (uint32_t)(16 * ks + 4 * hh + jj);
+      const bf16x8 vop = lds_read_tr_pair(vt, elem_off<D>(rlo, dv), elem_off<D>(rlo + 8, dv));
+      ws.acc[b] = mfma32(vop, pop[ks], ws.acc[b]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const FwdArgs& a, WaveState<D>& ws, int b, int hq, int row,
+                                       int l) {
+  using C = TileCfg<D>;
+  const int h = l >> 5;
+  if (row < a.Lq) {
+    const uint16_t* qr = a.q + (int64_t)b * a.q_sb + (int64_t)row * a.q_sl + (int64_t)hq * a.q_sh;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) ws.qop[s] = load_bf16x8(qr + 16 * s + 8 * h);
+  } else {
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) ws.qop[s] = zero_bf16x8();
+  }
+#pragma unroll
+  for (int bb = 0; bb < C::DVB; ++bb) ws.acc[bb] = f32x16{};
+  ws.m = -INFINITY;
+  ws.lsum = 0.f;
+}
+
+template <int D>
+__device__ __forceinline__ void store_out(const FwdArgs& a, const WaveState<D>& ws, int b, int hq,
+                                          int row, int l) {
+  using C = TileCfg<D>;
+  const int h = l >> 5;
+  const float tot = ws.lsum + xor_shuffle(ws.lsum, 32);
+  if (row >= a.Lq) return;
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  uint16_t* orow = a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_sl + (int64_t)hq * a.o_sh;
+#pragma unroll
+  for (int bb = 0; bb < C::DVB; ++bb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int dv = 32 * bb + 8 * u + 4 * h;
+      uint2 pk;
+      pk.x = pack_bf16x2(ws.acc[bb][4 * u + 0] * inv, ws.acc[bb][4 * u + 1] * inv);
+      pk.y = pack_bf16x2(ws.acc[bb][4 * u + 2] * inv, ws.acc[bb][4 * u + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + dv) = pk;
+    }
+  }
+  if (a.lse != nullptr && h == 0) {
+    a.lse[((int64_t)b * a.Hq + hq) * a.Lq + row] =
+        tot > 0.f ? ws.m * kLn2 + logf(tot) : -INFINITY;
+  }
+}
+
+// Maps blockIdx.x to a logical tile id so that consecutive logical ids run on one XCD (the
+// hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+__device__ __forceinline__ int logical_block(int xcd_remap) {
+  const int bid = (int)blockIdx.x;
+  const int n = (int)gridDim.x;
+  return xcd_remap ? ((bid & 7) * (n >> 3) + (bid >> 3)) : bid;
+}
+
+// ------------------------------------------------------------------------------------------
+// Dense forward. Logical order: (b, kv head) major so one XCD keeps one KV head's K/V in its
+// L2, then query tiles longest-first (causal work grows with the tile index), then the g
+// query heads of the group.
+// ------------------------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_dense_kernel(const FwdArgs a) {
+  using C = TileCfg<D>;
+  constexpr int BM = 32 * NW;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+
+  const int tid = (int)threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  int lid = logical_block(a.xcd_remap);
+  const int hg = lid % a.g;
+  lid /= a.g;
+  const int qt = a.n_qtiles - 1 - (lid % a.n_qtiles);
+  lid /= a.n_qtiles;
+  const int hkv = lid % a.Hkv;
+  const int b = lid / a.Hkv;
+  const int hq = hkv * a.g + hg;
+
+  const int q0 = qt * BM;
+  const int qw0 = q0 + 32 * w;                // first row of this wave
+  const int row = qw0 + (l & 31);             // this lane's query row
+  const int qlast = min(q0 + BM, a.Lq) - 1;   // last row of the workgroup
+  const int qwlast = min(qw0 + 31, a.Lq - 1); // last row of the wave
+  int klimit = a.Lk;                          // keys [0, klimit) can be visible
+  if (a.causal) klimit = min(a.Lk, qlast + a.off + 1);
+  const int ntiles = klimit > 0 ? (klimit + BN - 1) / BN : 0;
+
+  WaveState<D> ws;
+  load_q<D>(a, ws, b, hq, row, l);
+
+  const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+  const int lkm1 = a.Lk - 1;
+
+  if (ntiles > 0) {
+    issue_tile<D, NW>(a, smem, kb, vb, [&](int r) { return min(r, lkm1); }, w, l);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    wait_dma_all();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      const int base = (t + 1) * BN;
+      issue_tile<D, NW>(a, smem + ((t + 1) & 1) * C::STAGE_BYTES, kb, vb,
+                        [&](int r) { return min(base + r, lkm1); }, w, l);
+    }
+    const int base = t * BN;
+    // wave-uniform: skip tiles entirely beyond this wave's causal horizon
+    if (a.causal && base > qwlast + a.off) continue;
+    bool need_mask = (base + BN > a.Lk);
+    if (a.causal && base + BN - 1 > qw0 + a.off) need_mask = true;
+    tile_math<D>(a, ws, smem + (t & 1) * C::STAGE_BYTES, row, need_mask,
+                 [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
+  }
+  store_out<D>(a, ws, b, hq, row, l);
+}
+
+// ------------------------------------------------------------------------------------------
+// Block-sparse forward: one workgroup per (b, query head, 64-row query block).
+// Phase 1 walks the listed key blocks; phase 2 gathers the head's vertical columns that are
+// causally visible to the block and not already inside a listed block (so a key is never
+// counted twice), 64 at a time, in ascending key order.
+// ------------------------------------------------------------------------------------------
+constexpr int kSeg = 1024;          // columns examined per compaction pass
+constexpr int kMaxBitmapWords = 1024;  // listed-block bitmap: up to 32768 key blocks (2M keys)
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
+  using C = TileCfg<D>;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+  __shared__ uint32_t bitmap[kMaxBitmapWords];
+  __shared__ int kept[kSeg];
+  __shared__ int wave_cnt[NW];
+
+  const int tid = (int)threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int nqb = a.n_qtiles;
+  int lid = logical_block(a.xcd_remap);
+  const int hg = lid % a.g;
+  lid /= a.g;
+  const int qb = nqb - 1 - (lid % nqb);
+  lid /= nqb;
+  const int hkv = lid % a.Hkv;
+  const int b = lid / a.Hkv;
+  const int hq = hkv * a.g + hg;
+
+  const int q0 = qb * 64;
+  const int qw0 = q0 + 32 * w;
+  const int row = qw0 + (l & 31);
+  const int qlast = min(q0 + 64, a.Lq) - 1;
+  const int qwlast = min(qw0 + 31, a.Lq - 1);
+  const int klim = a.causal ? min(a.Lk - 1, qlast + a.off) : a.Lk - 1;  // last visible key
+  const int lkm1 = a.Lk - 1;
+
+  const int bh = b * a.Hq + hq;
+  const int64_t lrow = (int64_t)bh * nqb + qb;
+  const int bstart = a.blk_ptr[lrow];
+  const int nb = a.blk_ptr[lrow + 1] - bstart;
+  const int nwords = (a.nkb + 31) >> 5;
+
+  for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < nb; i += NT) {
+    const int kbk = a.blk_idx[bstart + i];
+    if (kbk >= 0 && kbk < a.nkb) atomicOr(&bitmap[kbk >> 5], 1u << (kbk & 31));
+  }
+  // (the barrier at the top of the tile loop orders these writes before any read)
+
+  WaveState<D> ws;
+  load_q<D>(a, ws, b, hq, row, l);
+  const uint16_t* kbp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const uint16_t* vbp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+  // ---- phase 1: listed key blocks
+  auto blk_base = [&](int i) -> int {
+    const int kbk = a.blk_idx[bstart + i];
+    return (kbk >= 0 && kbk < a.nkb) ? kbk * BN : -1;  // -1: invalid id, fully masked
+  };
+  if (nb > 0) {
+    const int base0 = blk_base(0);
+    issue_tile<D, NW>(a, smem, kbp, vbp,
+                      [&](int r) { return base0 < 0 ? 0 : min(base0 + r, lkm1); }, w, l);
+  }
+  for (int t = 0; t < nb; ++t) {
+    wait_dma_all();
+    __syncthreads();
+    if (t + 1 < nb) {
+      const int bn1 = blk_base(t + 1);
+      issue_tile<D, NW>(a, smem + ((t + 1) & 1) * C::STAGE_BYTES, kbp, vbp,
+                        [&](int r) { return bn1 < 0 ? 0 : min(bn1 + r, lkm1); }, w, l);
+    }
+    const int base = blk_base(t);
+    if (base < 0) continue;
+    if (a.causal && base > qwlast + a.off) continue;
+    bool need_mask = (base + BN > a.Lk);
+    if (a.causal && base + BN - 1 > qw0 + a.off) need_mask = true;
+    tile_math<D>(a, ws, smem + (t & 1) * C::STAGE_BYTES, row, need_mask,
+                 [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
+  }
+  __syncthreads();  // stage buffers free before phase 2 reuses them
+
+  // ---- phase 2: vertical columns
+  const int cstart = a.col_ptr[bh];
+  const int cend = a.col_ptr[bh + 1];
+  for (int seg = cstart; seg < cend; seg += kSeg) {
+    if (a.col_idx[seg] > klim) break;  // sorted: nothing further is visible
+    const int segend = min(seg + kSeg, cend);
+    int cnt = 0;
+    for (int rr = 0; rr < segend - seg; rr += NT) {
+      const int idx = seg + rr + tid;
+      bool keep = false;
+      int col = 0;
+      if (idx < segend) {
+        col = a.col_idx[idx];
+        if (col >= 0 && col <= klim) {
+          const int kbk = col >> 6;
+          keep = ((bitmap[kbk >> 5] >> (kbk & 31)) & 1u) == 0u;
+        }
+      }
+      const uint64_t mask = __ballot(keep);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      if (l == 0) wave_cnt[w] = __popcll(mask);
+      __syncthreads();
+      int woff = 0, tot = 0;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const int cw = wave_cnt[ww];
+        woff += (ww < w) ? cw : 0;
+        tot += cw;
+      }
+      if (keep) kept[cnt + woff + below] = col;
+      cnt += tot;
+      __syncthreads();
+    }
+    const int nch = (cnt + BN - 1) / BN;
+    if (nch > 0) {
+      issue_tile<D, NW>(a, smem, kbp, vbp,
+                        [&](int r) { return kept[r < cnt ? r : 0]; }, w, l);
+    }
+    for (int t = 0; t < nch; ++t) {
+      wait_dma_all();
+      __syncthreads();
+      if (t + 1 < nch) {
+        const int cb1 = (t + 1) * BN;
+        issue_tile<D, NW>(a, smem + ((t + 1) & 1) * C::STAGE_BYTES, kbp, vbp,
+                          [&](int r) { return kept[cb1 + r < cnt ? cb1 + r : 0]; }, w, l);
+      }
+      const int cb = t * BN;
+      // columns are ascending: skip if even the first one is beyond this wave's horizon
+      if (a.causal && kept[cb] > qwlast + a.off) continue;
+      tile_math<D>(a, ws, smem + (t & 1) * C::STAGE_BYTES, row, true,
+                   [&](int kl) { return cb + kl < cnt ? kept[cb + kl] : -1; }, l);
+    }
+    __syncthreads();  // kept[] and the stages are rewritten by the next segment
+  }
+  store_out<D>(a, ws, b, hq, row, l);
+}
+
+template <int D, int NW>
+hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
+  const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
+  FwdArgs aa = a;
+  aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_dense_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, stream, aa);
+  return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
+  const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
+  FwdArgs aa = a;
+  aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_sparse_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, stream, aa);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_dense_t<128, 4>(a, stream);
+  return launch_dense_t<64, 4>(a, stream);
+}
+
+hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_sparse_t<128, 2>(a, stream);
+  return launch_sparse_t<64, 2>(a, stream);
+}
+
+}  // namespace attn

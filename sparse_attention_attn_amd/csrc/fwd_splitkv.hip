@@ -1,0 +1,311 @@
+// fwd_splitkv.hip — split-KV decode partials and their log-sum-exp combine, on gfx950.
+//
+// Decode has very few query rows (Lq = 1..2) against a long KV cache ("Resumen Técnico:
+// FlashMLA-ETAP", section "Planteamiento del Problema": 1–2 query tokens, KV up to 64K, and
+// memory-bandwidth pressure from the long context). The kernel is therefore built so that the
+// HBM read of the KV cache is the bound:
+//
+//  * Work decomposition: one 4-wave workgroup per (batch, KV head, 16-column query block,
+//    split). The query columns are all (query head of the GQA group, query position) pairs
+//    that share the KV head, so the cache is read once per KV head, not once per query head.
+//    For the MLA shape (16 heads over one latent KV head, "Detalles de Implementación" and
+//    "Limitaciones Notadas por los Autores") the 16 heads fill one 16-column MFMA block.
+//  * Keys stream through an NST-stage LDS ring filled by asynchronous global->LDS copies;
+//    each tile is waited for with a counted vmcnt so NST-1 tiles stay in flight.
+//  * Each wave forms the whole score tile Sᵀ = K·Qᵀ (16x16x32 bf16 MFMA, keys as rows, query
+//    columns as N) and its softmax statistics, then accumulates its own quarter of the output
+//    columns, Oᵀ += Vᵀ·Pᵀ. For MLA, V is the first 512 columns of the same LDS tile that fed
+//    K, so the latent cache is read from HBM once.
+//  * Every split writes its normalised partial O_s (fp32) and LSE_s; attn_combine_lse merges
+//    them with weights exp(LSE_s - max LSE).
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    // gfx9 encoding: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14, expcnt 6:4 and
+    // lgkmcnt 11:8 left at their maxima (no wait on them).
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+}
+
+template <int DQK, int DV, int BNK, int NST>
+struct SplitCfg {
+  static constexpr bool MLA = (DQK != DV);          // V is the first DV columns of the K tile
+  static constexpr int KT_BYTES = BNK * DQK * 2;
+  static constexpr int VT_BYTES = MLA ? 0 : BNK * DV * 2;
+  static constexpr int STAGE = KT_BYTES + VT_BYTES;
+  static constexpr int KINSTR = KT_BYTES / 1024;
+  static constexpr int NINSTR = (KT_BYTES + VT_BYTES) / 1024;
+  static constexpr int IPW = NINSTR / 4;            // DMA instructions per wave per tile
+  static constexpr int QSTEPS = DQK / 32;
+  static constexpr int KBLK = BNK / 16;
+  static constexpr int DVW = DV / 4;                // output columns per wave
+  static constexpr int DVB = DVW / 16;
+  static constexpr int PVSTEPS = BNK / 32;
+  static constexpr int VW = MLA ? DQK : DV;         // row width of the tile V is read from
+  static_assert(NINSTR % 4 == 0, "tile must split evenly over 4 waves");
+  static_assert(KT_BYTES % 1024 == 0, "K tile must be whole KiB");
+};
+
+template <int DQK, int DV, int BNK, int NST>
+__global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
+  using C = SplitCfg<DQK, DV, BNK, NST>;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE];
+
+  const int tid = (int)threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  int lid = (int)blockIdx.x;
+  const int sp = lid % a.num_splits;
+  lid /= a.num_splits;
+  const int cb = lid % a.ncolblk;
+  lid /= a.ncolblk;
+  const int hkv = lid % a.Hkv;
+  const int b = lid / a.Hkv;
+
+  const int ncols = a.g * a.Lq;
+  const int col = cb * 16 + (l & 15);
+  const bool col_ok = col < ncols;
+  const int pos = col_ok ? col / a.g : 0;
+  const int hq = hkv * a.g + (col_ok ? col % a.g : 0);
+
+  // keys of this split, cut by the causal horizon of the block's last column
+  const int kstart = sp * a.chunk;
+  int kend = min(a.Lk, kstart + a.chunk);
+  const int last_col = min(ncols, cb * 16 + 16) - 1;
+  const int first_pos = (cb * 16) / a.g;
+  const int last_pos = last_col / a.g;
+  if (a.causal) kend = min(kend, last_pos + a.off + 1);
+  const int ntiles = kend > kstart ? (kend - kstart + BNK - 1) / BNK : 0;
+
+  // Qᵀ operand: lane l holds column l%16, head-dim elements 32*s + 8*(l/16) .. +7
+  bf16x8 qop[C::QSTEPS];
+  {
+    const uint16_t* qr = a.q + (int64_t)b * a.q_sb + (int64_t)pos * a.q_sl + (int64_t)hq * a.q_sh;
+#pragma unroll
+    for (int s = 0; s < C::QSTEPS; ++s)
+      qop[s] = col_ok ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
+  }
+
+  const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+  const int kmax = kend - 1;
+
+  auto issue = [&](int t) {
+    char* st = smem + (t % NST) * C::STAGE;
+    const int base = kstart + t * BNK;
+#pragma unroll
+    for (int ii = 0; ii < C::IPW; ++ii) {
+      const int i = w + 4 * ii;
+      if (C::MLA || i < C::KINSTR) {
+        const uint32_t slot = (uint32_t)i * 64u + (uint32_t)l;
+        const uint32_t r = slot / (DQK / 8);
+        const uint32_t c = (slot % (DQK / 8)) ^ Swz<DQK>::f(r);
+        const int key = min(base + (int)r, kmax);
+        dma16(kb + (int64_t)key * a.k_sl + c * 8, st + i * 1024);
+      } else {
+        if constexpr (!C::MLA) {
+          const int iv = i - C::KINSTR;
+          const uint32_t slot = (uint32_t)iv * 64u + (uint32_t)l;
+          const uint32_t r = slot / (DV / 8);
+          const uint32_t c = (slot % (DV / 8)) ^ Swz<DV>::f(r);
+          const int key = min(base + (int)r, kmax);
+          dma16(vb + (int64_t)key * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
+        }
+      }
+    }
+  };
+
+  f32x4 acc[C::DVB];
+#pragma unroll
+  for (int i = 0; i < C::DVB; ++i) acc[i] = f32x4{};
+  float m = -INFINITY, lsum = 0.f;
+
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < ntiles) issue(p);
+
+  const int G = l >> 4;
+  const int jj = (l & 15) >> 2;
+  const int cc = l & 3;
+  const int lim = a.causal ? pos + a.off : 0x7fffffff;
+
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + NST - 2 < ntiles) wait_vmcnt<C::IPW * (NST - 2)>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    if (t + NST - 1 < ntiles) issue(t + NST - 1);
+
+    const char* kt = smem + (t % NST) * C::STAGE;
+    const char* vt = C::MLA ? kt : kt + C::KT_BYTES;
+    const int base = kstart + t * BNK;
+
+    // ---- Sᵀ: KBLK blocks of 16 keys x 16 columns
+    f32x4 st[C::KBLK];
+#pragma unroll
+    for (int k = 0; k < C::KBLK; ++k) st[k] = f32x4{};
+#pragma unroll
+    for (int k = 0; k < C::KBLK; ++k) {
+      const uint32_t r = (uint32_t)(16 * k + (l & 15));
+      const uint32_t sw = Swz<DQK>::f(r);
+#pragma unroll
+      for (int s = 0; s < C::QSTEPS; ++s) {
+        const uint32_t c = (uint32_t)(4 * s + G);
+        const bf16x8 kop = lds_read_bf16x8(kt, (r * (DQK / 8) + (c ^ sw)) * 16u);
+        st[k] = mfma16(kop, qop[s], st[k]);
+      }
+    }
+    // ---- mask: slot (k, j) holds key base + 16*k + 4*(l/16) + j
+    const bool need_mask = (base + BNK > kend) || (a.causal && base + BNK - 1 > first_pos + a.off);
+    if (need_mask) {
+#pragma unroll
+      for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = base + 16 * k + 4 * G + j;
+          if (key >= kend || key > lim) st[k][j] = -INFINITY;
+        }
+    }
+    // ---- online softmax over this tile's keys for each column
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, st[k][j]);
+    mx = fmaxf(mx, xor_shuffle(mx, 16));
+    mx = fmaxf(mx, xor_shuffle(mx, 32));
+    const float mnew = fmaxf(m, mx * a.sl2);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = fast_exp2(m - muse);
+    m = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        st[k][j] = fast_exp2(fmaf(st[k][j], a.sl2, -muse));
+        psum += st[k][j];
+      }
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < C::DVB; ++i) acc[i] *= alpha;
+
+    // ---- Oᵀ += Vᵀ·Pᵀ over 32-key steps. Operand slot i of lane l covers key
+    // 32*ps + 16*(i/4) + 4*(l/16) + i%4 (blocks 2ps and 2ps+1 of Sᵀ).
+#pragma unroll
+    for (int ps = 0; ps < C::PVSTEPS; ++ps) {
+      const f32x4& x0 = st[2 * ps];
+      const f32x4& x1 = st[2 * ps + 1];
+      const bf16x8 pop = pack_bf16x8(x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]);
+      const uint32_t rlo = (uint32_t)(32 * ps + 4 * G + jj);
+#pragma unroll
+      for (int i = 0; i < C::DVB; ++i) {
+        const uint32_t dv = (uint32_t)(w * C::DVW + 16 * i + 4 * cc);
+        const bf16x8 vop =
+            lds_read_tr_pair(vt, elem_off<C::VW>(rlo, dv), elem_off<C::VW>(rlo + 16, dv));
+        acc[i] = mfma16(vop, pop, acc[i]);
+      }
+    }
+  }
+
+  // ---- partial outputs of this split
+  float tot = lsum + xor_shuffle(lsum, 16);
+  tot = tot + xor_shuffle(tot, 32);
+  if (!col_ok) return;
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq) * a.Lq + pos;
+  float* op = a.o_part + prow * DV;
+#pragma unroll
+  for (int i = 0; i < C::DVB; ++i) {
+    const int dv = w * C::DVW + 16 * i + 4 * G;
+    *reinterpret_cast<float4*>(op + dv) =
+        make_float4(acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv);
+  }
+  if (w == 0 && G == 0) a.lse_part[prow] = tot > 0.f ? m * kLn2 + logf(tot) : -INFINITY;
+}
+
+// ------------------------------------------------------------------------------------------
+// Combine: M = max_s LSE_s, w_s = exp(LSE_s - M), LSE = M + ln Σ w_s, O = Σ w_s O_s / Σ w_s.
+// One wave per output row; lane l owns DV/64 consecutive columns.
+// ------------------------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+  constexpr int E = DV / 64;
+  const int w = (int)threadIdx.x >> 6;
+  const int l = (int)threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.lse_part[(int64_t)s * rows + row]);
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float den = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < a.S; ++s) {
+      const float ls = a.lse_part[(int64_t)s * rows + row];
+      const float ws = (ls == -INFINITY) ? 0.f : expf(ls - mx);
+      den += ws;
+      const float* src = a.o_part + ((int64_t)s * rows + row) * DV + l * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] += ws * src[e];
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const int pos = (int)(row % a.Lq);
+  const int hq = (int)((row / a.Lq) % a.Hq);
+  const int b = (int)(row / ((int64_t)a.Lq * a.Hq));
+  uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)pos * a.o_sl + (int64_t)hq * a.o_sh + l * E;
+#pragma unroll
+  for (int e = 0; e < E; e += 2) {
+    if (e + 1 < E) {
+      *reinterpret_cast<uint32_t*>(dst + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+    } else {
+      __bf16 x = (__bf16)(o[e] * inv);
+      dst[e] = __builtin_bit_cast(uint16_t, x);
+    }
+  }
+  if (a.lse != nullptr && l == 0) a.lse[row] = den > 0.f ? mx + logf(den) : -INFINITY;
+}
+
+template <int DQK, int DV, int BNK, int NST>
+hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
+  const int64_t nwg = (int64_t)a.B * a.Hkv * a.ncolblk * a.num_splits;
+  hipLaunchKernelGGL((splitkv_kernel<DQK, DV, BNK, NST>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DV>
+hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream) {
+  if (dqk == 576) return launch_split_t<576, 512, 32, 3>(a, stream);
+  if (dqk == 128) return launch_split_t<128, 128, 64, 3>(a, stream);
+  return launch_split_t<64, 64, 64, 4>(a, stream);
+}
+
+hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream) {
+  if (dv == 512) return launch_combine_t<512>(a, stream);
+  if (dv == 128) return launch_combine_t<128>(a, stream);
+  return launch_combine_t<64>(a, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,74 @@
+// kernels.hpp — argument blocks and launchers shared by the host API and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Dense and block-sparse forward (one launch writes O and LSE).
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // [B, Hq, Lq] or nullptr
+  int64_t q_sb, q_sl, q_sh;
+  int64_t k_sb, k_sl, k_sh;
+  int64_t v_sb, v_sl, v_sh;
+  int64_t o_sb, o_sl, o_sh;
+  int B, Hq, Hkv, Lq, Lk, g;
+  int causal;
+  int off;        // Lk - Lq (bottom-right causal alignment)
+  float sl2;      // scale * log2(e)
+  int n_qtiles;   // query tiles per (b, hq)
+  int xcd_remap;  // grid size divisible by 8: group consecutive logical tiles per XCD
+  // block-sparse lists (device pointers), unused by the dense kernel
+  const int32_t* blk_ptr;
+  const int32_t* blk_idx;
+  const int32_t* col_ptr;
+  const int32_t* col_idx;
+  int nkb;        // ceil(Lk / 64)
+};
+
+// Split-KV partials.
+struct SplitArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o_part;    // [S, B, Hq, Lq, Dv]
+  float* lse_part;  // [S, B, Hq, Lq]
+  int64_t q_sb, q_sl, q_sh;
+  int64_t k_sb, k_sl, k_sh;
+  int64_t v_sb, v_sl, v_sh;
+  int B, Hq, Hkv, Lq, Lk, g;
+  int causal;
+  int off;
+  float sl2;
+  int num_splits;
+  int chunk;        // keys per split (multiple of 64)
+  int ncolblk;      // ceil(g * Lq / 16)
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  uint16_t* o;
+  float* lse;
+  int64_t o_sb, o_sl, o_sh;
+  int B, Hq, Lq, S;
+};
+
+hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);
+
+// Query rows per workgroup of the dense forward kernel.
+constexpr int kDenseBlockM = 128;
+// Query rows per workgroup of the block-sparse kernel (one 64-row query block).
+constexpr int kSparseBlockM = 64;
+// Query columns ((head, position) pairs of one KV head) per split-KV workgroup.
+constexpr int kSplitCols = 16;
+
+}  // namespace attn

@@ -1,0 +1,221 @@
+// validate.cpp — host-side argument checks of the C ABI (pure C++, no HIP).
+#include "validate.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <limits>
+#include <sstream>
+
+namespace attn {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_tensor(const char* fn, const char* name, const attn_tensor_t& t) {
+  if (t.data == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, std::string(name) + " is NULL");
+  if (!aligned16(t.data))
+    return fail(ATTN_ERR_INVALID_ARG, fn, std::string(name) + " data is not 16-byte aligned");
+  if (t.stride_b < 0 || t.stride_l < 0 || t.stride_h < 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn, std::string(name) + " has a negative stride");
+  if ((t.stride_b % 8) != 0 || (t.stride_l % 8) != 0 || (t.stride_h % 8) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn,
+                std::string(name) + " strides must be multiples of 8 elements (16 bytes)");
+  return ATTN_OK;
+}
+
+bool dims_ok(Op op, int Dqk, int Dv) {
+  if ((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128)) return true;
+  return op == Op::kSplit && Dqk == 576 && Dv == 512;
+}
+}  // namespace
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+void clear_last_error() { g_last_error.clear(); }
+const char* last_error_cstr() { return g_last_error.c_str(); }
+
+int fail(int status, const char* fn, const std::string& msg) {
+  g_last_error = std::string(fn) + ": " + msg;
+  return status;
+}
+
+int check_attention_args(const char* fn, Op op, const attn_tensor_t& q, const attn_tensor_t& k,
+                         const attn_tensor_t& v, const attn_tensor_t* o, const float* lse, int B,
+                         int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1) {
+    std::ostringstream s;
+    s << "sizes must be >= 1 (B=" << B << " Hq=" << Hq << " Hkv=" << Hkv << " Lq=" << Lq
+      << " Lk=" << Lk << ")";
+    return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+  }
+  if (Hq % Hkv != 0) {
+    std::ostringstream s;
+    s << "Hq (" << Hq << ") must be a multiple of Hkv (" << Hkv << ")";
+    return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+  }
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, fn, "scale is not finite");
+  if (!dims_ok(op, Dqk, Dv)) {
+    std::ostringstream s;
+    s << "head dims (Dqk=" << Dqk << ", Dv=" << Dv << ") not supported; supported: (64,64), (128,128)"
+      << (op == Op::kSplit ? ", (576,512)" : "");
+    return fail(ATTN_ERR_UNSUPPORTED, fn, s.str());
+  }
+  int st;
+  if ((st = check_tensor(fn, "q", q)) != ATTN_OK) return st;
+  if ((st = check_tensor(fn, "k", k)) != ATTN_OK) return st;
+  if ((st = check_tensor(fn, "v", v)) != ATTN_OK) return st;
+  if (o != nullptr && (st = check_tensor(fn, "o", *o)) != ATTN_OK) return st;
+  if (lse != nullptr && !aligned4(lse))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "lse is not 4-byte aligned");
+  if (Dqk != Dv && (v.data != k.data || v.stride_b != k.stride_b || v.stride_l != k.stride_l ||
+                    v.stride_h != k.stride_h)) {
+    return fail(ATTN_ERR_UNSUPPORTED, fn,
+                "the (576, 512) latent shape requires v to alias k (same pointer and strides)");
+  }
+  // grid sizes and index arithmetic stay within 31 bits for the launch dimensions
+  const int64_t rows = (int64_t)B * Hq * Lq;
+  if (rows > (int64_t)std::numeric_limits<int>::max() / 4)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "B*Hq*Lq too large");
+  if (op == Op::kSparse && Lk > kSparseMaxLk) {
+    std::ostringstream s;
+    s << "Lk=" << Lk << " exceeds the block-sparse limit of " << kSparseMaxLk;
+    return fail(ATTN_ERR_UNSUPPORTED, fn, s.str());
+  }
+  return ATTN_OK;
+}
+
+int check_num_splits(const char* fn, int num_splits, int Lk) {
+  const int maxs = (Lk + 63) / 64;
+  if (num_splits < 1 || num_splits > maxs) {
+    std::ostringstream s;
+    s << "num_splits=" << num_splits << " outside [1, ceil(Lk/64)=" << maxs << "]";
+    return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+  }
+  return ATTN_OK;
+}
+
+int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
+  (void)Dv;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  constexpr int kCUs = 256;  // MI355X
+  const int g = Hq / Hkv;
+  const int64_t colblk = ((int64_t)g * Lq + 15) / 16;
+  const int64_t units = (int64_t)B * Hkv * colblk;
+  const int wg_per_cu = (Dqk == 64) ? 2 : 1;  // LDS ring: 64 KiB (D=64), 96-108 KiB otherwise
+  int64_t s = (kCUs * wg_per_cu + units - 1) / units;
+  const int64_t max_by_len = std::max<int64_t>(1, Lk / 256);  // at least 256 keys per split
+  const int64_t max_s = (Lk + 63) / 64;
+  s = std::min(s, max_by_len);
+  s = std::min(s, max_s);
+  s = std::max<int64_t>(s, 1);
+  return (int)s;
+}
+
+int split_chunk(int Lk, int num_splits) {
+  const int per = (Lk + num_splits - 1) / num_splits;
+  return 64 * ((per + 63) / 64);
+}
+
+size_t workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits) {
+  if (B < 1 || Hq < 1 || Lq < 1 || Dv < 1 || num_splits < 1) return 0;
+  const size_t rows = (size_t)num_splits * B * Hq * Lq;
+  return rows * (size_t)Dv * sizeof(float) + rows * sizeof(float);
+}
+
+int check_combine_args(const char* fn, const float* o_part, const float* lse_part, int num_splits,
+                       const attn_tensor_t& o, const float* lse, int B, int Hq, int Lq, int Dv) {
+  if (B < 1 || Hq < 1 || Lq < 1 || num_splits < 1)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "sizes and num_splits must be >= 1");
+  if (Dv != 64 && Dv != 128 && Dv != 512) {
+    std::ostringstream s;
+    s << "Dv=" << Dv << " not supported (64, 128, 512)";
+    return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+  }
+  if (o_part == nullptr || lse_part == nullptr)
+    return fail(ATTN_ERR_WORKSPACE, fn, "o_part / lse_part is NULL");
+  if (!aligned16(o_part) || !aligned4(lse_part))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "o_part must be 16-byte and lse_part 4-byte aligned");
+  if (o.data == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "o is NULL");
+  if (!aligned16(o.data) || (o.stride_b % 8) || (o.stride_l % 8) || (o.stride_h % 8) ||
+      o.stride_b < 0 || o.stride_l < 0 || o.stride_h < 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "o must be 16-byte aligned with strides multiple of 8");
+  if (lse != nullptr && !aligned4(lse))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "lse is not 4-byte aligned");
+  return ATTN_OK;
+}
+
+int check_blocksparse_lists(const char* fn, const int32_t* blk_ptr, const int32_t* blk_idx,
+                            const int32_t* col_ptr, const int32_t* col_idx, int B, int Hq, int Lq,
+                            int Lk, int block_m, int block_n) {
+  if (B < 1 || Hq < 1 || Lq < 1 || Lk < 1)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "sizes must be >= 1");
+  if (block_m != 64 || block_n != 64)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "block_m and block_n must be 64");
+  if (blk_ptr == nullptr || col_ptr == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "blk_ptr / col_ptr is NULL");
+  const int64_t nqb = (Lq + 63) / 64;
+  const int64_t nkb = (Lk + 63) / 64;
+  const int64_t nrows = (int64_t)B * Hq * nqb;
+  if (blk_ptr[0] != 0) return fail(ATTN_ERR_INVALID_ARG, fn, "blk_ptr[0] must be 0");
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int32_t lo = blk_ptr[r], hi = blk_ptr[r + 1];
+    if (hi < lo) {
+      std::ostringstream s;
+      s << "blk_ptr decreases at row " << r;
+      return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+    }
+    if (hi > lo && blk_idx == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "blk_idx is NULL");
+    for (int32_t i = lo; i < hi; ++i) {
+      const int32_t x = blk_idx[i];
+      if (x < 0 || x >= nkb) {
+        std::ostringstream s;
+        s << "blk_idx[" << i << "]=" << x << " outside [0, " << nkb << ")";
+        return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+      }
+      if (i > lo && blk_idx[i - 1] >= x) {
+        std::ostringstream s;
+        s << "blk_idx not strictly increasing at " << i;
+        return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+      }
+    }
+  }
+  if (col_ptr[0] != 0) return fail(ATTN_ERR_INVALID_ARG, fn, "col_ptr[0] must be 0");
+  for (int64_t r = 0; r < (int64_t)B * Hq; ++r) {
+    const int32_t lo = col_ptr[r], hi = col_ptr[r + 1];
+    if (hi < lo) {
+      std::ostringstream s;
+      s << "col_ptr decreases at head row " << r;
+      return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+    }
+    if (hi > lo && col_idx == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "col_idx is NULL");
+    for (int32_t i = lo; i < hi; ++i) {
+      const int32_t x = col_idx[i];
+      if (x < 0 || x >= Lk) {
+        std::ostringstream s;
+        s << "col_idx[" << i << "]=" << x << " outside [0, " << Lk << ")";
+        return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+      }
+      if (i > lo && col_idx[i - 1] >= x) {
+        std::ostringstream s;
+        s << "col_idx not strictly increasing at " << i;
+        return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+      }
+    }
+  }
+  return ATTN_OK;
+}
+
+const char* status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+}  // namespace attn

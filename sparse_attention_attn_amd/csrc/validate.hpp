@@ -1,0 +1,52 @@
+// validate.hpp — host-side argument checks of the C ABI. Pure C++: no HIP dependency, so the
+// same code is unit-tested on a machine without a GPU (and under host sanitizers).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/attn.h"
+
+namespace attn {
+
+// Thread-local message of the last failed call.
+void set_last_error(const std::string& msg);
+void clear_last_error();
+const char* last_error_cstr();
+
+// Records `msg` (prefixed with the entry point name) and returns `status`.
+int fail(int status, const char* fn, const std::string& msg);
+
+enum class Op { kDense, kSplit, kSparse };
+
+// Common checks of sizes, head dims, scale, pointers, alignment and strides.
+int check_attention_args(const char* fn, Op op, const attn_tensor_t& q, const attn_tensor_t& k,
+                         const attn_tensor_t& v, const attn_tensor_t* o, const float* lse, int B,
+                         int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, float scale);
+
+int check_num_splits(const char* fn, int num_splits, int Lk);
+
+// Split count heuristic for a 256-CU MI355X (pure function).
+int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
+
+// Keys per split: 64 * ceil(ceil(Lk / S) / 64).
+int split_chunk(int Lk, int num_splits);
+
+size_t workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits);
+
+int check_combine_args(const char* fn, const float* o_part, const float* lse_part, int num_splits,
+                       const attn_tensor_t& o, const float* lse, int B, int Hq, int Lq, int Dv);
+
+// CSR index-list structure check on HOST arrays.
+int check_blocksparse_lists(const char* fn, const int32_t* blk_ptr, const int32_t* blk_idx,
+                            const int32_t* col_ptr, const int32_t* col_idx, int B, int Hq, int Lq,
+                            int Lk, int block_m, int block_n);
+
+// Largest key length the block-sparse kernel's listed-block bitmap covers.
+constexpr int kSparseMaxLk = 1 << 21;
+
+const char* status_string(int status);
+
+}  // namespace attn

@@ -1,0 +1,169 @@
+"""CPU-only checks of the C ABI: libattn.so loads, exports every function include/attn.h
+declares, and its host-side validation returns the documented status codes without touching a
+GPU (every call below fails validation before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_attention_attn_amd as S
+from sparse_attention_attn_amd._lib import AttnTensorC
+from workloads import dense_causal_lists, make_blocksparse_lists
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _lib():
+    return S.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_functions() == sorted(S.EXPORTED_SYMBOLS)
+
+
+@pytest.mark.parametrize("name", sorted(S.EXPORTED_SYMBOLS))
+def test_library_exports_symbol(name):
+    assert hasattr(_lib(), name), f"libattn.so does not export {name}"
+
+
+def test_status_strings():
+    assert S.attn_status_string(0) == "ATTN_OK"
+    assert S.attn_status_string(-1) == "ATTN_ERR_INVALID_ARG"
+    assert S.attn_status_string(-2) == "ATTN_ERR_UNSUPPORTED"
+    assert S.attn_status_string(-3) == "ATTN_ERR_WORKSPACE"
+    assert S.attn_status_string(-4) == "ATTN_ERR_LAUNCH"
+
+
+# Fake, aligned, never-dereferenced device addresses: validation rejects these calls first.
+FAKE = 0x10000
+
+
+def _t(ptr=FAKE, sb=8 * 64 * 4 * 128, sl=4 * 128, sh=128):
+    return AttnTensorC(ptr, sb, sl, sh)
+
+
+def _fwd(q=None, k=None, v=None, o=None, lse=None, B=1, Hq=4, Hkv=2, Lq=64, Lk=64, Dqk=128,
+         Dv=128, causal=1, scale=0.1):
+    return _lib().attn_fwd(q or _t(), k or _t(), v or _t(), o or _t(), lse, B, Hq, Hkv, Lq, Lk,
+                           Dqk, Dv, causal, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(B=0), S.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(Lq=0), S.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(Lk=-3), S.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(Hq=6, Hkv=4), S.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(scale=float("nan")), S.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("inf")), S.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(Dqk=96, Dv=96), S.ATTN_ERR_UNSUPPORTED, "head dims"),
+    (dict(Dqk=576, Dv=512), S.ATTN_ERR_UNSUPPORTED, "head dims"),   # latent shape: split-KV only
+    (dict(q=_t(ptr=0)), S.ATTN_ERR_INVALID_ARG, "q is NULL"),
+    (dict(k=_t(ptr=FAKE + 2)), S.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(v=_t(sl=4 * 128 + 4)), S.ATTN_ERR_INVALID_ARG, "multiples of 8"),
+    (dict(o=_t(sh=-128)), S.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(lse=ctypes.c_void_p(FAKE + 2)), S.ATTN_ERR_INVALID_ARG, "lse"),
+])
+def test_attn_fwd_validation(kw, code, frag):
+    st = _fwd(**kw)
+    assert st == code
+    assert frag in S.attn_last_error()
+    assert S.attn_last_error().startswith("attn_fwd:")
+
+
+def _split(num_splits=2, o_part=FAKE, lse_part=FAKE, Dqk=128, Dv=128, v=None, k=None, Lk=4096):
+    return _lib().attn_fwd_splitkv(_t(), k or _t(), v or _t(), o_part, lse_part, num_splits, 2, 8,
+                                   2, 1, Lk, Dqk, Dv, 0, ctypes.c_float(0.1), None)
+
+
+def test_splitkv_validation():
+    assert _split(num_splits=0) == S.ATTN_ERR_INVALID_ARG
+    assert _split(num_splits=65) == S.ATTN_ERR_INVALID_ARG          # > ceil(4096/64)
+    assert "num_splits" in S.attn_last_error()
+    assert _split(o_part=None) == S.ATTN_ERR_WORKSPACE
+    assert _split(lse_part=None) == S.ATTN_ERR_WORKSPACE
+    assert _split(o_part=FAKE + 4) == S.ATTN_ERR_WORKSPACE
+    # latent shape needs V to alias K
+    assert _split(Dqk=576, Dv=512, v=_t(ptr=FAKE + 4096)) == S.ATTN_ERR_UNSUPPORTED
+    assert "alias" in S.attn_last_error()
+
+
+def test_combine_validation():
+    lib = _lib()
+    f = lambda **kw: lib.attn_combine_lse(kw.get("op", FAKE), kw.get("lp", FAKE), kw.get("S", 2),
+                                         kw.get("o", _t()), kw.get("lse"), 1, 4, 1,
+                                         kw.get("Dv", 128), None)
+    assert f(S=0) == S.ATTN_ERR_INVALID_ARG
+    assert f(Dv=96) == S.ATTN_ERR_INVALID_ARG
+    assert f(op=None) == S.ATTN_ERR_WORKSPACE
+    assert f(o=_t(ptr=0)) == S.ATTN_ERR_INVALID_ARG
+
+
+def test_blocksparse_entry_validation():
+    lib = _lib()
+    f = lambda bm=64, bn=64, ptr=FAKE, Lk=4096: lib.attn_fwd_blocksparse(
+        _t(), _t(), _t(), _t(), None, 1, 4, 2, 4096, Lk, 128, 128, 1, ctypes.c_float(0.1), bm, bn,
+        ptr, FAKE, FAKE, FAKE, None)
+    assert f(bm=128) == S.ATTN_ERR_UNSUPPORTED
+    assert f(ptr=None) == S.ATTN_ERR_INVALID_ARG
+    assert "blk_ptr / col_ptr" in S.attn_last_error()
+    assert f(Lk=(1 << 21) + 64) == S.ATTN_ERR_UNSUPPORTED
+
+
+def test_num_splits_heuristic_is_pure_and_in_range():
+    # the decode workloads: 128 (b, kv-head) units -> 2 splits; 8 units of MLA -> 32 splits
+    assert S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128) == 2
+    assert S.attn_splitkv_num_splits(8, 16, 1, 1, 65536, 576, 512) == 32
+    for args in [(1, 1, 1, 1, 1, 64, 64), (1, 8, 1, 1, 100, 128, 128), (64, 64, 8, 1, 30, 64, 64),
+                 (1, 16, 1, 2, 1 << 20, 576, 512)]:
+        s = S.attn_splitkv_num_splits(*args)
+        assert 1 <= s <= -(-args[4] // 64)
+    assert S.attn_splitkv_num_splits(0, 1, 1, 1, 1, 64, 64) == S.ATTN_ERR_INVALID_ARG
+
+
+def test_workspace_bytes():
+    assert S.attn_splitkv_workspace_bytes(8, 16, 1, 512, 32) == 32 * 8 * 16 * (512 + 1) * 4
+    assert S.attn_splitkv_workspace_bytes(0, 16, 1, 512, 32) == 0
+
+
+def test_blocksparse_check_accepts_generated_lists():
+    lists = make_blocksparse_lists(2, 3, 1000, 1000, 5, local_blocks=4, p_extra=0.1, n_cols=77)
+    assert S.attn_blocksparse_check(*lists, 2, 3, 1000, 1000) == S.ATTN_OK
+    lists = dense_causal_lists(1, 2, 300, 300)
+    assert S.attn_blocksparse_check(*lists, 1, 2, 300, 300) == S.ATTN_OK
+
+
+@pytest.mark.parametrize("mutate,frag", [
+    (lambda bp, bi, cp, ci: bi.__setitem__(bp[-2] + 1, bi[bp[-2]]), "strictly increasing"),
+    (lambda bp, bi, cp, ci: bi.__setitem__(0, 99), "outside"),
+    (lambda bp, bi, cp, ci: bp.__setitem__(2, bp[1] - 1), "decreases"),
+    (lambda bp, bi, cp, ci: ci.__setitem__(0, 1000), "outside"),
+    (lambda bp, bi, cp, ci: ci.__setitem__(1, ci[0]), "strictly increasing"),
+    (lambda bp, bi, cp, ci: bp.__setitem__(0, 1), "blk_ptr[0]"),
+])
+def test_blocksparse_check_rejects(mutate, frag):
+    bp, bi, cp, ci = [np.array(x) for x in
+                      make_blocksparse_lists(1, 2, 1000, 1000, 6, local_blocks=4, p_extra=0.1,
+                                             n_cols=50)]
+    mutate(bp, bi, cp, ci)
+    with pytest.raises(S.AttnError) as e:
+        S.attn_blocksparse_check(bp, bi, cp, ci, 1, 2, 1000, 1000)
+    assert e.value.status == S.ATTN_ERR_INVALID_ARG
+    assert frag in str(e.value)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import sparse_attention_attn_amd._lib as L
+    monkeypatch.setattr(L, "_LIB", None)
+    monkeypatch.setenv("ATTN_LIB", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        L.load_library()

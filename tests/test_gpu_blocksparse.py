@@ -1,0 +1,163 @@
+"""GPU parity of attn_fwd_blocksparse against the fp64 oracle (lists -> mask by np.repeat of a
+block bitmap OR a column bitmap: no code shared with the kernel's walk/gather/de-dup)."""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from tests.helpers import check_parity, say, to_f64
+from workloads import (WORKLOADS, dense_causal_lists, make_blocksparse_lists, make_qkv,
+                       randn_bf16, sampled_rows)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _run(q, k, v, lists, causal, scale):
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Lq, Hq, _ = q.shape
+    o = torch.empty((B, Lq, Hq, v.shape[3]), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=DEV)
+    dl = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(DEV) for x in lists]
+    S.attn_fwd_blocksparse(q, k, v, o, *dl, lse=lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle(q, k, v, lists, causal, scale):
+    B, Lq, Hq, _ = q.shape
+    Lk = k.shape[1]
+    fn = A.csr_allowed_fn(*lists, hq=Hq, nqb=-(-Lq // 64), lk=Lk)
+    return A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(scale), causal,
+                       allowed_fn=fn)
+
+
+CASES = [
+    # B, Hq, Hkv, L, D, local, p_extra, n_cols
+    (1, 4, 2, 1000, 128, 4, 0.10, 50),
+    (2, 4, 1, 777, 64, 3, 0.20, 120),
+    (1, 8, 2, 2048, 128, 8, 0.05, 300),
+    (1, 2, 2, 130, 128, 1, 0.00, 40),    # columns only (plus the diagonal)
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_blocksparse_small(case):
+    B, Hq, Hkv, L, D, local, p, ncols = case
+    say(f"blocksparse {case}")
+    seed = 9000 + sum(case[:5])
+    q = randn_bf16((B, L, Hq, D), seed)
+    k = randn_bf16((B, L, Hkv, D), seed + 1)
+    v = randn_bf16((B, L, Hkv, D), seed + 2)
+    lists = make_blocksparse_lists(B, Hq, L, L, seed + 3, local_blocks=local, p_extra=p,
+                                   n_cols=ncols)
+    import sparse_attention_attn_amd as S
+    S.attn_blocksparse_check(*lists, B, Hq, L, L)
+    o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
+    o_ref, lse_ref = _oracle(q, k, v, lists, True, D ** -0.5)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"sparse{case}")
+
+
+def test_blocksparse_all_blocks_equals_dense():
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Hq, Hkv, L, D = 1, 4, 2, 700, 128
+    say("blocksparse all blocks == dense causal")
+    q, k, v = (randn_bf16((B, L, Hq, D), 9100), randn_bf16((B, L, Hkv, D), 9101),
+               randn_bf16((B, L, Hkv, D), 9102))
+    lists = dense_causal_lists(B, Hq, L, L)
+    o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
+    od = torch.empty_like(o)
+    ld = torch.empty_like(lse)
+    S.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), od, ld, causal=True, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5), True)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "sparse-all")
+    check_parity(to_f64(od), o_ref, to_f64(ld), lse_ref, "dense")
+
+
+def test_blocksparse_noncausal_and_empty_rows():
+    """Non-causal lists, a query block with no block and no column (O = 0, LSE = -inf)."""
+    B, Hq, Hkv, L, D = 1, 2, 1, 256, 64
+    say("blocksparse non-causal + empty rows")
+    q, k, v = (randn_bf16((B, L, Hq, D), 9200), randn_bf16((B, L, Hkv, D), 9201),
+               randn_bf16((B, L, Hkv, D), 9202))
+    # head 0: qb0 -> {3}, qb1 -> {}, qb2 -> {0, 2}, qb3 -> {1, 3}; columns {5, 70}
+    # head 1: every query block empty, no columns
+    blk_ptr = np.array([0, 1, 1, 3, 5, 5, 5, 5, 5], np.int32)
+    blk_idx = np.array([3, 0, 2, 1, 3], np.int32)
+    col_ptr = np.array([0, 2, 2], np.int32)
+    col_idx = np.array([5, 70], np.int32)
+    lists = (blk_ptr, blk_idx, col_ptr, col_idx)
+    o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, False, 0.125)
+    o_ref, lse_ref = _oracle(q, k, v, lists, False, 0.125)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "sparse-noncausal")
+    assert np.all(np.isneginf(to_f64(lse)[0, 1]))
+
+
+def test_planted_columns_counted_once():
+    """Planted keys make each column carry a large weight: a column counted twice (it is also
+    inside a listed block), a missed column, or a column past the causal horizon that leaks in
+    would move O by far more than the tolerance."""
+    import torch
+    B, Hq, Hkv, L, D = 1, 1, 1, 512, 64
+    say("planted columns")
+    q = randn_bf16((B, L, Hq, D), 9300).float()
+    k = randn_bf16((B, L, Hkv, D), 9301).float() * 0.05
+    v = randn_bf16((B, L, Hkv, D), 9302).float()
+    cols = [10, 100, 130, 300, 450]
+    probe = q[0, 400, 0]
+    for c in cols:
+        k[0, c, 0] = probe * 0.5
+        v[0, c, 0] = 2.0 + c / 300.0   # |O| < 4: output rounding stays far inside 1e-2
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    nqb = L // 64
+    # qb 6 (rows 384..447) lists block 1 (keys 64..127, contains column 100) and its diagonal
+    blk_ptr, blk_idx = [0], []
+    for qb in range(nqb):
+        ids = sorted({qb, 1} if qb >= 1 else {0})
+        blk_idx += ids
+        blk_ptr.append(len(blk_idx))
+    lists = (np.array(blk_ptr, np.int32), np.array(blk_idx, np.int32),
+             np.array([0, len(cols)], np.int32), np.array(cols, np.int32))
+    o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
+    o_ref, lse_ref = _oracle(q, k, v, lists, True, D ** -0.5)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "planted-cols")
+
+
+def test_blocksparse_workload_full_size_sampled_rows():
+    """The 128K block-sparse workload at full size (the launch the bench times); the oracle
+    checks 128 sampled rows (first 32, last 32, 64 seeded) of 8 query heads."""
+    w = WORKLOADS["blocksparse_128k"]
+    say(f"blocksparse_128k full size {w}")
+    q, k, v = make_qkv(w)
+    lists = make_blocksparse_lists(w.B, w.Hq, w.Lq, w.Lk, 1000 * w.index + 3)
+    o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, w.scale)
+    rows = sampled_rows(w.Lq, 128, 1000 * w.index + 4, edge=32)
+    qf, kf, vf = to_f64(q[:, rows]), to_f64(k), to_f64(v)
+    fn = A.csr_allowed_fn(*lists, hq=w.Hq, nqb=w.Lq // 64, lk=w.Lk)
+    sc = A.effective_scale(w.scale)
+    of = o[0, rows].float().cpu().numpy().astype(np.float64)
+    lf = lse[0][:, rows].cpu().numpy().astype(np.float64)
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for h in range(0, w.Hq, 4):
+        orow, lrow = A.attention_query_rows(qf[0, :, h], kf, vf, sc, True, 0, h, rows, w.Lq, w.Hq,
+                                            fn(0, h, rows))
+        got_o.append(of[:, h])
+        ref_o.append(orow)
+        got_l.append(lf[h])
+        ref_l.append(lrow)
+    check_parity(np.stack(got_o), np.stack(ref_o), np.stack(got_l), np.stack(ref_l), "sparse128k")
+
+
+def test_blocksparse_deterministic():
+    B, Hq, Hkv, L, D = 1, 4, 2, 1500, 128
+    say("determinism blocksparse")
+    q, k, v = (randn_bf16((B, L, Hq, D), 9400), randn_bf16((B, L, Hkv, D), 9401),
+               randn_bf16((B, L, Hkv, D), 9402))
+    lists = make_blocksparse_lists(B, Hq, L, L, 9403, local_blocks=4, p_extra=0.1, n_cols=200)
+    o1, l1 = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
+    o2, l2 = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
+    assert bool((o1 == o2).all()) and bool((l1 == l2).all())
