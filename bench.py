@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+Prints ONE JSON line. The headline is the Llama-3-8B-shaped causal GQA prefill
+(B=1, Hq=32, Hkv=8, D=128, L=8192) in attention TFLOP/s, with a roofline object for its
+kernel and the fp64 CPU oracle timed on a bounded sample of the same workload. The decode
+(GQA 4K, MLA 64K) and block-sparse (128K) workloads are timed in the same run and reported
+under "workloads" with their own units (KV-read GB/s, TFLOP/s).
+
+Timing: W untimed warm-up steps, then K steps bracketed by torch.cuda.synchronize(), with
+HIP events recorded on the stream the kernels are launched on (torch's current stream).
+Inputs are resident in HBM before the timed region starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+HEADLINE = "gqa_prefill_8k"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------ work counts
+def dense_causal_pairs(lq, lk, causal):
+    """Visible (query, key) pairs of one head under bottom-right causal masking."""
+    if not causal:
+        return lq * lk
+    off = lk - lq
+    tot = 0
+    # row i sees min(lk, max(0, i + off + 1)) keys
+    import numpy as np
+    i = np.arange(lq, dtype=np.int64)
+    return int(np.clip(i + off + 1, 0, lk).sum()) if lq else tot
+
+
+def blocksparse_pairs(lists, B, Hq, L):
+    """Exact visible pairs of the block/column union with causal masking (Lq == Lk == L)."""
+    import numpy as np
+    blk_ptr, blk_idx, col_ptr, col_idx = [np.asarray(x, np.int64) for x in lists]
+    nqb = -(-L // 64)
+    total = 0
+    for bh in range(B * Hq):
+        cols = col_idx[col_ptr[bh]:col_ptr[bh + 1]]
+        base = bh * nqb
+        for qb in range(nqb):
+            blks = blk_idx[blk_ptr[base + qb]:blk_ptr[base + qb + 1]]
+            r0, r1 = 64 * qb, min(64 * qb + 64, L)            # rows [r0, r1)
+            # listed blocks: keys [64kb, 64kb+64) ∩ [0, L), row i sees keys j <= i
+            k0 = 64 * blks
+            k1 = np.minimum(k0 + 64, L)
+            # pairs = sum over rows i of |[k0, k1) ∩ [0, i]|
+            rows = np.arange(r0, r1)[:, None]
+            total += int(np.clip(np.minimum(k1[None, :], rows + 1) - k0[None, :], 0, None).sum())
+            # columns not inside a listed block, each visible to rows i >= c
+            inblk = np.isin(cols // 64, blks)
+            c = cols[~inblk]
+            total += int(np.clip(r1 - np.maximum(c, r0), 0, None).sum())
+    return total
+
+
+# ------------------------------------------------------------------------------ timing
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------ workloads
+def bench_prefill(w, steps, warmup):
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import make_qkv
+    q, k, v = [t.to("cuda:0") for t in make_qkv(w)]
+    o = torch.empty((w.B, w.Lq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+    step = lambda: S.attn_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale)
+    ms, wall = time_steps(step, steps, warmup)
+    flops = 2 * (w.Dqk + w.Dv) * w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, w.causal)
+    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def bench_decode(w, steps, warmup):
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import make_qkv
+    q, k, v = make_qkv(w)
+    kv_bytes = k.numel() * 2 + (0 if w.mla else v.numel() * 2)
+    # rotate >= 1 GiB of KV copies so the 256 MiB Infinity Cache cannot serve repeats
+    ncopies = max(2, -(-(1 << 30) // kv_bytes))
+    qd = q.to("cuda:0")
+    ks = [k.to("cuda:0") for _ in range(ncopies)]
+    vs = [t[..., :w.Dv] for t in ks] if w.mla else [v.to("cuda:0") for _ in range(ncopies)]
+    o = torch.empty((w.B, w.Lq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+    nsp = S.attn_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.Dqk, w.Dv)
+    op = torch.empty((nsp, w.B, w.Hq, w.Lq, w.Dv), dtype=torch.float32, device="cuda:0")
+    lp = torch.empty((nsp, w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+    it = [0]
+
+    def step():
+        i = it[0] % ncopies
+        it[0] += 1
+        S.attn_fwd_splitkv(qd, ks[i], vs[i], op, lp, causal=w.causal, scale=w.scale)
+        S.attn_combine_lse(op, lp, o, lse)
+
+    ms, wall = time_steps(step, steps, warmup)
+    nbytes = kv_bytes + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4
+    return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "num_splits": nsp, "kv_copies": ncopies}
+
+
+def bench_blocksparse(w, steps, warmup):
+    import numpy as np
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import make_blocksparse_lists, make_qkv
+    q, k, v = [t.to("cuda:0") for t in make_qkv(w)]
+    lists = make_blocksparse_lists(w.B, w.Hq, w.Lq, w.Lk, 1000 * w.index + 3)
+    dl = [torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0") for x in lists]
+    o = torch.empty((w.B, w.Lq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+    step = lambda: S.attn_fwd_blocksparse(q, k, v, o, *dl, lse=lse, causal=True, scale=w.scale)
+    ms, wall = time_steps(step, steps, warmup)
+    pairs = blocksparse_pairs(lists, w.B, w.Hq, w.Lq)
+    flops = 2 * (w.Dqk + w.Dv) * pairs
+    dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
+    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            "density_vs_causal": pairs / dense}
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, as it stands, timed on a bounded sample of the headline workload:
+    whole query heads' worth of sampled rows, grown until about `budget_s` of CPU work."""
+    import numpy as np
+    from oracle import attention as A
+    from workloads import make_qkv, sampled_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = make_qkv(w)
+    qf = q.float().numpy().astype(np.float64)
+    kf = k.float().numpy().astype(np.float64)
+    vf = v.float().numpy().astype(np.float64)
+    sc = A.effective_scale(w.scale)
+    rows = sampled_rows(w.Lq, 512, 1000 * w.index + 4, edge=64)
+    per_row_pairs = np.clip(rows + (w.Lk - w.Lq) + 1, 0, w.Lk).sum()
+    t0 = time.perf_counter()
+    heads = 0
+    while True:
+        A.attention_rows(qf, kf, vf, sc, w.causal, 0, heads % w.Hq, rows)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s or heads >= w.Hq:
+            break
+    el = time.perf_counter() - t0
+    flops = 2 * (w.Dqk + w.Dv) * int(per_row_pairs) * heads
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} query head(s) x {len(rows)} sampled rows (first/last 64 + seeded) of "
+                      f"{w.name}, all visible keys, fp64 numpy; {el:.1f} s"}
+
+
+# ------------------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None, help="comma list of workloads to run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this attention path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from workloads import WORKLOADS
+
+    names = args.only.split(",") if args.only else list(WORKLOADS)
+    res = {}
+    for name in names:
+        w = WORKLOADS[name]
+        log(f"workload {name}: {w}")
+        if w.kind == "prefill":
+            res[name] = bench_prefill(w, args.steps if name == HEADLINE else max(3, args.steps // 4),
+                                      args.warmup)
+        elif w.kind in ("decode", "mla_decode"):
+            res[name] = bench_decode(w, args.steps * 5, args.warmup)
+        elif w.kind == "blocksparse":
+            res[name] = bench_blocksparse(w, max(3, args.steps // 4), min(args.warmup, 2))
+        log(f"  -> {res[name]}")
+
+    head = WORKLOADS[HEADLINE]
+    out = {
+        "metric": "attention TFLOP/s (prefill) and KV-read GB/s (decode), % of MI355X peak",
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+    }
+    if HEADLINE in res:
+        r = res[HEADLINE]
+        src_hash = kernel_source_hash(["fwd_prefill.hip", "common.hpp"])
+        out.update({
+            "value": round(r["tflops"], 3),
+            "ms_per_step": round(r["ms"], 4),
+            "config": {"workload": HEADLINE, "B": head.B, "Hq": head.Hq, "Hkv": head.Hkv,
+                       "seq_len": head.Lq, "head_dim": head.Dqk, "causal": head.causal,
+                       "flops_per_step": r["flops"]},
+            "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": load_traffic(HEADLINE, src_hash),
+                         "kernel": "fwd_dense_kernel<128,4>",
+                         "kernel_source_sha256_16": src_hash},
+        })
+    wl = {}
+    for name, r in res.items():
+        if "gbs" in r:
+            wl[name] = {"value": round(r["gbs"], 1), "unit": "GB/s", "ms": round(r["ms"], 4),
+                        "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                        "num_splits": r["num_splits"], "bytes": r["bytes"]}
+        else:
+            wl[name] = {"value": round(r["tflops"], 3), "unit": "TFLOP/s", "ms": round(r["ms"], 4),
+                        "frac_of_mfma_peak": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "flops": r["flops"]}
+            if "density_vs_causal" in r:
+                wl[name]["density_vs_causal"] = round(r["density_vs_causal"], 4)
+    out["workloads"] = wl
+    if not args.no_cpu_baseline and HEADLINE in res:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

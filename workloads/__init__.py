@@ -123,10 +123,9 @@ def make_blocksparse_lists(B, Hq, Lq, Lk, seed, block=64, local_blocks=64, p_ext
             sel = local | (extra & causal_blk)
             if first_block:
                 sel[:, 0] = True
-            for qb in range(nqb):
-                ids = np.nonzero(sel[qb])[0].astype(np.int32)
-                idx_parts.append(ids)
-                ptr.append(ptr[-1] + ids.size)
+            # row-major nonzero = per-query-block sorted key-block ids
+            idx_parts.append(np.nonzero(sel)[1].astype(np.int32))
+            ptr.extend((ptr[-1] + np.cumsum(sel.sum(axis=1))).tolist())
             nc = min(n_cols, Lk)
             cols = torch.randperm(Lk, generator=g)[:nc].numpy().astype(np.int32)
             cols.sort()
