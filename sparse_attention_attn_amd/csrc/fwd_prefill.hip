@@ -23,6 +23,8 @@
 // register layout; the M-padding reason the FlashMLA-ETAP page gives for its transposed flow
 // does not arise with 32- or 16-row MFMA tiles.)
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,6 +64,41 @@ __device__ __forceinline__ void issue_tile(const FwdArgs& a, char* st, const uin
     dma16(vbase + (int64_t)key * a.v_sl + c * 8, st + C::TILE_BYTES + i * 1024);
   }
 }
+
+// Per-lane element offsets (relative to a tile's first key row) of this wave's copy
+// instructions, for tiles whose 64 rows are consecutive keys all inside the sequence.
+template <int D, int NW>
+struct TileOffsets {
+  uint32_t k[TileCfg<D>::INSTR / NW];
+  uint32_t v[TileCfg<D>::INSTR / NW];
+  __device__ __forceinline__ void init(const FwdArgs& a, int w, int l) {
+    using C = TileCfg<D>;
+#pragma unroll
+    for (int ii = 0; ii < C::INSTR / NW; ++ii) {
+      const uint32_t slot = (uint32_t)(w + NW * ii) * 64u + (uint32_t)l;
+      const uint32_t r = slot / C::CPR;
+      const uint32_t c = (slot % C::CPR) ^ Swz<D>::f(r);
+      k[ii] = r * (uint32_t)a.k_sl + c * 8u;
+      v[ii] = r * (uint32_t)a.v_sl + c * 8u;
+    }
+  }
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_fast(char* st, const uint16_t* ktile,
+                                                const uint16_t* vtile, const TileOffsets<D, NW>& off,
+                                                int w) {
+  using C = TileCfg<D>;
+#pragma unroll
+  for (int ii = 0; ii < C::INSTR / NW; ++ii) {
+    const int i = w + NW * ii;
+    dma16(ktile + off.k[ii], st + i * 1024);
+    dma16(vtile + off.v[ii], st + C::TILE_BYTES + i * 1024);
+  }
+}
+
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 template <int D>
 struct WaveState {
@@ -216,10 +253,12 @@ __device__ __forceinline__ int logical_block(int xcd_remap) {
 // query heads of the group.
 // ------------------------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_dense_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_dense_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
   constexpr int BM = 32 * NW;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+  // One array per ring stage (see the split-KV kernel): stage indices are compile-time.
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
 
   const int tid = (int)threadIdx.x;
   const int w = tid >> 6;
@@ -244,29 +283,40 @@ __global__ __launch_bounds__(NW * 64) void fwd_dense_kernel(const FwdArgs a) {
 
   WaveState<D> ws;
   load_q<D>(a, ws, b, hq, row, l);
+  TileOffsets<D, NW> off;
+  off.init(a, w, l);
 
   const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
   const int lkm1 = a.Lk - 1;
 
-  if (ntiles > 0) {
-    issue_tile<D, NW>(a, smem, kb, vb, [&](int r) { return min(r, lkm1); }, w, l);
-  }
-  for (int t = 0; t < ntiles; ++t) {
+  auto issue = [&](auto S, int t) {
+    char* st = decltype(S)::value == 0 ? st0 : st1;
+    const int base = t * BN;
+    if (base + BN <= a.Lk) {
+      issue_tile_fast<D, NW>(st, kb + (int64_t)base * a.k_sl, vb + (int64_t)base * a.v_sl, off, w);
+    } else {
+      issue_tile<D, NW>(a, st, kb, vb, [&](int r) { return min(base + r, lkm1); }, w, l);
+    }
+  };
+  auto step = [&](auto S, int t) {
+    constexpr int s = decltype(S)::value;
     wait_dma_all();
     __syncthreads();
-    if (t + 1 < ntiles) {
-      const int base = (t + 1) * BN;
-      issue_tile<D, NW>(a, smem + ((t + 1) & 1) * C::STAGE_BYTES, kb, vb,
-                        [&](int r) { return min(base + r, lkm1); }, w, l);
-    }
+    if (t + 1 < ntiles) issue(ic<1 - s>{}, t + 1);
     const int base = t * BN;
     // wave-uniform: skip tiles entirely beyond this wave's causal horizon
-    if (a.causal && base > qwlast + a.off) continue;
+    if (a.causal && base > qwlast + a.off) return;
     bool need_mask = (base + BN > a.Lk);
     if (a.causal && base + BN - 1 > qw0 + a.off) need_mask = true;
-    tile_math<D>(a, ws, smem + (t & 1) * C::STAGE_BYTES, row, need_mask,
+    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, need_mask,
                  [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
+  };
+
+  if (ntiles > 0) issue(ic<0>{}, 0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(ic<0>{}, t);
+    if (t + 1 < ntiles) step(ic<1>{}, t + 1);
   }
   store_out<D>(a, ws, b, hq, row, l);
 }
@@ -284,7 +334,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
   __shared__ uint32_t bitmap[kMaxBitmapWords];
   __shared__ int kept[kSeg];
   __shared__ int wave_cnt[NW];
@@ -326,6 +377,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
 
   WaveState<D> ws;
   load_q<D>(a, ws, b, hq, row, l);
+  TileOffsets<D, NW> off;
+  off.init(a, w, l);
   const uint16_t* kbp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
@@ -334,26 +387,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
     const int kbk = a.blk_idx[bstart + i];
     return (kbk >= 0 && kbk < a.nkb) ? kbk * BN : -1;  // -1: invalid id, fully masked
   };
-  if (nb > 0) {
-    const int base0 = blk_base(0);
-    issue_tile<D, NW>(a, smem, kbp, vbp,
-                      [&](int r) { return base0 < 0 ? 0 : min(base0 + r, lkm1); }, w, l);
-  }
-  for (int t = 0; t < nb; ++t) {
+  auto issue_blk = [&](auto S, int i) {
+    char* st = decltype(S)::value == 0 ? st0 : st1;
+    const int base = blk_base(i);
+    if (base >= 0 && base + BN <= a.Lk) {
+      issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl, off, w);
+    } else {
+      issue_tile<D, NW>(a, st, kbp, vbp,
+                        [&](int r) { return base < 0 ? 0 : min(base + r, lkm1); }, w, l);
+    }
+  };
+  auto step_blk = [&](auto S, int t) {
+    constexpr int s = decltype(S)::value;
     wait_dma_all();
     __syncthreads();
-    if (t + 1 < nb) {
-      const int bn1 = blk_base(t + 1);
-      issue_tile<D, NW>(a, smem + ((t + 1) & 1) * C::STAGE_BYTES, kbp, vbp,
-                        [&](int r) { return bn1 < 0 ? 0 : min(bn1 + r, lkm1); }, w, l);
-    }
+    if (t + 1 < nb) issue_blk(ic<1 - s>{}, t + 1);
     const int base = blk_base(t);
-    if (base < 0) continue;
-    if (a.causal && base > qwlast + a.off) continue;
+    if (base < 0) return;
+    if (a.causal && base > qwlast + a.off) return;
     bool need_mask = (base + BN > a.Lk);
     if (a.causal && base + BN - 1 > qw0 + a.off) need_mask = true;
-    tile_math<D>(a, ws, smem + (t & 1) * C::STAGE_BYTES, row, need_mask,
+    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, need_mask,
                  [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
+  };
+  if (nb > 0) issue_blk(ic<0>{}, 0);
+  for (int t = 0; t < nb; t += 2) {
+    step_blk(ic<0>{}, t);
+    if (t + 1 < nb) step_blk(ic<1>{}, t + 1);
   }
   __syncthreads();  // stage buffers free before phase 2 reuses them
 
@@ -392,23 +452,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
       __syncthreads();
     }
     const int nch = (cnt + BN - 1) / BN;
-    if (nch > 0) {
-      issue_tile<D, NW>(a, smem, kbp, vbp,
-                        [&](int r) { return kept[r < cnt ? r : 0]; }, w, l);
-    }
-    for (int t = 0; t < nch; ++t) {
+    auto issue_col = [&](auto S, int t) {
+      char* st = decltype(S)::value == 0 ? st0 : st1;
+      const int cb = t * BN;
+      issue_tile<D, NW>(a, st, kbp, vbp, [&](int r) { return kept[cb + r < cnt ? cb + r : 0]; }, w, l);
+    };
+    auto step_col = [&](auto S, int t) {
+      constexpr int s = decltype(S)::value;
       wait_dma_all();
       __syncthreads();
-      if (t + 1 < nch) {
-        const int cb1 = (t + 1) * BN;
-        issue_tile<D, NW>(a, smem + ((t + 1) & 1) * C::STAGE_BYTES, kbp, vbp,
-                          [&](int r) { return kept[cb1 + r < cnt ? cb1 + r : 0]; }, w, l);
-      }
+      if (t + 1 < nch) issue_col(ic<1 - s>{}, t + 1);
       const int cb = t * BN;
       // columns are ascending: skip if even the first one is beyond this wave's horizon
-      if (a.causal && kept[cb] > qwlast + a.off) continue;
-      tile_math<D>(a, ws, smem + (t & 1) * C::STAGE_BYTES, row, true,
+      if (a.causal && kept[cb] > qwlast + a.off) return;
+      tile_math<D>(a, ws, s == 0 ? st0 : st1, row, true,
                    [&](int kl) { return cb + kl < cnt ? kept[cb + kl] : -1; }, l);
+    };
+    if (nch > 0) issue_col(ic<0>{}, 0);
+    for (int t = 0; t < nch; t += 2) {
+      step_col(ic<0>{}, t);
+      if (t + 1 < nch) step_col(ic<1>{}, t + 1);
     }
     __syncthreads();  // kept[] and the stages are rewritten by the next segment
   }

@@ -19,6 +19,8 @@
 //  * Every split writes its normalised partial O_s (fp32) and LSE_s; attn_combine_lse merges
 //    them with weights exp(LSE_s - max LSE).
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -58,10 +60,26 @@ struct SplitCfg {
   static_assert(KT_BYTES % 1024 == 0, "K tile must be whole KiB");
 };
 
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 template <int DQK, int DV, int BNK, int NST>
 __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   using C = SplitCfg<DQK, DV, BNK, NST>;
-  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE];
+  static_assert(NST >= 2 && NST <= 4, "2..4 stages");
+  // One array per ring stage: with the stage fixed at compile time the compiler can tell the
+  // stage being read from the stages still being filled, and does not wait for those copies.
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[NST > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NST > 3 ? C::STAGE : 16];
+  auto stage = [&](auto S) -> char* {
+    constexpr int s = decltype(S)::value;
+    if constexpr (s == 0) return st0;
+    else if constexpr (s == 1) return st1;
+    else if constexpr (s == 2) return st2;
+    else return st3;
+  };
 
   const int tid = (int)threadIdx.x;
   const int w = tid >> 6;
@@ -102,27 +120,49 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
   const int kmax = kend - 1;
 
-  auto issue = [&](int t) {
-    char* st = smem + (t % NST) * C::STAGE;
+  // Per-lane source offsets (elements, relative to the tile's first key row) of this wave's
+  // copy instructions; instruction ii of wave w is tile copy w + 4*ii.
+  uint32_t src_off[C::IPW];
+#pragma unroll
+  for (int ii = 0; ii < C::IPW; ++ii) {
+    const int i = w + 4 * ii;
+    if (C::MLA || i < C::KINSTR) {
+      const uint32_t slot = (uint32_t)i * 64u + (uint32_t)l;
+      const uint32_t r = slot / (DQK / 8);
+      const uint32_t c = (slot % (DQK / 8)) ^ Swz<DQK>::f(r);
+      src_off[ii] = r * (uint32_t)a.k_sl + c * 8u;
+    } else {
+      if constexpr (!C::MLA) {
+        const uint32_t slot = (uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l;
+        const uint32_t r = slot / (DV / 8);
+        const uint32_t c = (slot % (DV / 8)) ^ Swz<DV>::f(r);
+        src_off[ii] = r * (uint32_t)a.v_sl + c * 8u;
+      }
+    }
+  }
+
+  auto issue = [&](auto S, int t) {
+    char* st = stage(S);
     const int base = kstart + t * BNK;
+    const bool tail = base + BNK - 1 > kmax;
+    const uint16_t* kt = kb + (int64_t)base * a.k_sl;
+    const uint16_t* vt = vb + (int64_t)base * a.v_sl;
 #pragma unroll
     for (int ii = 0; ii < C::IPW; ++ii) {
       const int i = w + 4 * ii;
-      if (C::MLA || i < C::KINSTR) {
-        const uint32_t slot = (uint32_t)i * 64u + (uint32_t)l;
-        const uint32_t r = slot / (DQK / 8);
-        const uint32_t c = (slot % (DQK / 8)) ^ Swz<DQK>::f(r);
+      const bool is_k = C::MLA || i < C::KINSTR;
+      const int li = is_k ? i : i - C::KINSTR;
+      char* dst = st + (is_k ? 0 : C::KT_BYTES) + li * 1024;
+      if (!tail) {
+        dma16((is_k ? kt : vt) + src_off[ii], dst);
+      } else {  // last tile of the split: clamp rows past the end (masked later)
+        const uint32_t slot = (uint32_t)li * 64u + (uint32_t)l;
+        const int cpr = is_k ? DQK / 8 : DV / 8;
+        const uint32_t r = slot / cpr;
+        const uint32_t c = (slot % cpr) ^ (is_k ? Swz<DQK>::f(r) : Swz<(C::MLA ? DQK : DV)>::f(r));
         const int key = min(base + (int)r, kmax);
-        dma16(kb + (int64_t)key * a.k_sl + c * 8, st + i * 1024);
-      } else {
-        if constexpr (!C::MLA) {
-          const int iv = i - C::KINSTR;
-          const uint32_t slot = (uint32_t)iv * 64u + (uint32_t)l;
-          const uint32_t r = slot / (DV / 8);
-          const uint32_t c = (slot % (DV / 8)) ^ Swz<DV>::f(r);
-          const int key = min(base + (int)r, kmax);
-          dma16(vb + (int64_t)key * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
-        }
+        const uint16_t* src = is_k ? kb + (int64_t)key * a.k_sl : vb + (int64_t)key * a.v_sl;
+        dma16(src + c * 8, dst);
       }
     }
   };
@@ -132,39 +172,40 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   for (int i = 0; i < C::DVB; ++i) acc[i] = f32x4{};
   float m = -INFINITY, lsum = 0.f;
 
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < ntiles) issue(p);
-
   const int G = l >> 4;
   const int jj = (l & 15) >> 2;
   const int cc = l & 3;
   const int lim = a.causal ? pos + a.off : 0x7fffffff;
+  const uint32_t krow = (uint32_t)(l & 15);
 
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + NST - 2 < ntiles) wait_vmcnt<C::IPW * (NST - 2)>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-    if (t + NST - 1 < ntiles) issue(t + NST - 1);
-
-    const char* kt = smem + (t % NST) * C::STAGE;
+  auto compute = [&](auto S, int t) {
+    const char* kt = stage(S);
     const char* vt = C::MLA ? kt : kt + C::KT_BYTES;
     const int base = kstart + t * BNK;
 
-    // ---- Sᵀ: KBLK blocks of 16 keys x 16 columns
+    // ---- Sᵀ: KBLK blocks of 16 keys x 16 columns; K operands read one step ahead
     f32x4 st[C::KBLK];
-#pragma unroll
-    for (int k = 0; k < C::KBLK; ++k) st[k] = f32x4{};
+    bf16x8 kcur[C::KBLK], knxt[C::KBLK];
 #pragma unroll
     for (int k = 0; k < C::KBLK; ++k) {
-      const uint32_t r = (uint32_t)(16 * k + (l & 15));
-      const uint32_t sw = Swz<DQK>::f(r);
+      st[k] = f32x4{};
+      const uint32_t r = 16u * k + krow;
+      kcur[k] = lds_read_bf16x8(kt, (r * (DQK / 8) + ((uint32_t)G ^ Swz<DQK>::f(r))) * 16u);
+    }
 #pragma unroll
-      for (int s = 0; s < C::QSTEPS; ++s) {
-        const uint32_t c = (uint32_t)(4 * s + G);
-        const bf16x8 kop = lds_read_bf16x8(kt, (r * (DQK / 8) + (c ^ sw)) * 16u);
-        st[k] = mfma16(kop, qop[s], st[k]);
+    for (int s = 0; s < C::QSTEPS; ++s) {
+      if (s + 1 < C::QSTEPS) {
+#pragma unroll
+        for (int k = 0; k < C::KBLK; ++k) {
+          const uint32_t r = 16u * k + krow;
+          const uint32_t c = (uint32_t)(4 * (s + 1) + G);
+          knxt[k] = lds_read_bf16x8(kt, (r * (DQK / 8) + (c ^ Swz<DQK>::f(r))) * 16u);
+        }
       }
+#pragma unroll
+      for (int k = 0; k < C::KBLK; ++k) st[k] = mfma16(kcur[k], qop[s], st[k]);
+#pragma unroll
+      for (int k = 0; k < C::KBLK; ++k) kcur[k] = knxt[k];
     }
     // ---- mask: slot (k, j) holds key base + 16*k + 4*(l/16) + j
     const bool need_mask = (base + BNK > kend) || (a.causal && base + BNK - 1 > first_pos + a.off);
@@ -209,14 +250,35 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
       const f32x4& x1 = st[2 * ps + 1];
       const bf16x8 pop = pack_bf16x8(x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]);
       const uint32_t rlo = (uint32_t)(32 * ps + 4 * G + jj);
+      bf16x8 vop[C::DVB];
 #pragma unroll
       for (int i = 0; i < C::DVB; ++i) {
         const uint32_t dv = (uint32_t)(w * C::DVW + 16 * i + 4 * cc);
-        const bf16x8 vop =
-            lds_read_tr_pair(vt, elem_off<C::VW>(rlo, dv), elem_off<C::VW>(rlo + 16, dv));
-        acc[i] = mfma16(vop, pop, acc[i]);
+        vop[i] = lds_read_tr_pair(vt, elem_off<C::VW>(rlo, dv), elem_off<C::VW>(rlo + 16, dv));
       }
+#pragma unroll
+      for (int i = 0; i < C::DVB; ++i) acc[i] = mfma16(vop[i], pop, acc[i]);
     }
+  };
+
+  // One ring step: tile t sits in stage S; copies of the next NST-2 tiles may stay in flight.
+  auto step = [&](auto S, int t) {
+    constexpr int s = decltype(S)::value;
+    if (t + NST - 2 < ntiles) wait_vmcnt<C::IPW * (NST - 2)>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    if (t + NST - 1 < ntiles) issue(ic<(s + NST - 1) % NST>{}, t + NST - 1);
+    compute(S, t);
+  };
+
+  if (0 < ntiles) issue(ic<0>{}, 0);
+  if (NST > 2 && 1 < ntiles) issue(ic<1>{}, 1);
+  if (NST > 3 && 2 < ntiles) issue(ic<2 % NST>{}, 2);
+  for (int t = 0; t < ntiles; t += NST) {
+    step(ic<0>{}, t);
+    if (t + 1 < ntiles) step(ic<1>{}, t + 1);
+    if constexpr (NST > 2) { if (t + 2 < ntiles) step(ic<2 % NST>{}, t + 2); }
+    if constexpr (NST > 3) { if (t + 3 < ntiles) step(ic<3 % NST>{}, t + 3); }
   }
 
   // ---- partial outputs of this split
@@ -237,47 +299,44 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Combine: M = max_s LSE_s, w_s = exp(LSE_s - M), LSE = M + ln Σ w_s, O = Σ w_s O_s / Σ w_s.
-// One wave per output row; lane l owns DV/64 consecutive columns.
+// One thread per (output row, 4 consecutive output columns); the loop over splits issues
+// independent 16-byte loads.
 // ------------------------------------------------------------------------------------------
 template <int DV>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  constexpr int E = DV / 64;
-  const int w = (int)threadIdx.x >> 6;
-  const int l = (int)threadIdx.x & 63;
+  constexpr int TPR = DV / 4;  // threads per row
   const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
-  const int64_t row = (int64_t)blockIdx.x * 4 + w;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / TPR;
+  const int c4 = (int)(gid % TPR);
   if (row >= rows) return;
   float mx = -INFINITY;
   for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.lse_part[(int64_t)s * rows + row]);
-  float o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
   if (mx != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < a.S; ++s) {
       const float ls = a.lse_part[(int64_t)s * rows + row];
       const float ws = (ls == -INFINITY) ? 0.f : expf(ls - mx);
+      const float4 x = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
       den += ws;
-      const float* src = a.o_part + ((int64_t)s * rows + row) * DV + l * E;
-#pragma unroll
-      for (int e = 0; e < E; ++e) o[e] += ws * src[e];
+      o.x += ws * x.x;
+      o.y += ws * x.y;
+      o.z += ws * x.z;
+      o.w += ws * x.w;
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const int pos = (int)(row % a.Lq);
   const int hq = (int)((row / a.Lq) % a.Hq);
   const int b = (int)(row / ((int64_t)a.Lq * a.Hq));
-  uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)pos * a.o_sl + (int64_t)hq * a.o_sh + l * E;
-#pragma unroll
-  for (int e = 0; e < E; e += 2) {
-    if (e + 1 < E) {
-      *reinterpret_cast<uint32_t*>(dst + e) = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
-    } else {
-      __bf16 x = (__bf16)(o[e] * inv);
-      dst[e] = __builtin_bit_cast(uint16_t, x);
-    }
-  }
-  if (a.lse != nullptr && l == 0) a.lse[row] = den > 0.f ? mx + logf(den) : -INFINITY;
+  uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)pos * a.o_sl + (int64_t)hq * a.o_sh + 4 * c4;
+  uint2 pk;
+  pk.x = pack_bf16x2(o.x * inv, o.y * inv);
+  pk.y = pack_bf16x2(o.z * inv, o.w * inv);
+  *reinterpret_cast<uint2*>(dst) = pk;
+  if (a.lse != nullptr && c4 == 0) a.lse[row] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
 template <int DQK, int DV, int BNK, int NST>
@@ -289,8 +348,9 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
 
 template <int DV>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
-  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  const int64_t threads = (int64_t)a.B * a.Hq * a.Lq * (DV / 4);
+  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
