@@ -218,6 +218,8 @@ def main():
     ap.add_argument("--only", default=None, help="comma list of workloads to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -229,6 +231,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     from workloads import WORKLOADS
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read + {n} bytes written")
+        del src, dst
 
     names = args.only.split(",") if args.only else list(WORKLOADS)
     res = {}

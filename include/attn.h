@@ -122,7 +122,7 @@ int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits,
  *       that head (subject to the causal mask).
  * All four are DEVICE int32 arrays; blk_idx (col_idx) may be NULL only when every block
  * (column) list is empty. Each list must be sorted ascending without duplicates,
- * block ids in [0, ceil(Lk/64)), columns in [0, Lk). Their contents are NOT checked on the
+ * block ids in [0, ceil(Lk/64)), columns in [0, Lk). Lk may be at most 2^20. Their contents are NOT checked on the
  * device (that would need a host copy): call attn_blocksparse_check on host copies.
  * block_m and block_n must both be 64. Supported head dims: (64, 64), (128, 128).
  */

@@ -22,6 +22,17 @@
 // from the row-major V tile via the LDS transpose read. (The transposition here serves
 // register layout; the M-padding reason the FlashMLA-ETAP page gives for its transposed flow
 // does not arise with 32- or 16-row MFMA tiles.)
+//
+// LDS layout: K rows padded to 2D+16 bytes and V rows to 2D+64 bytes. With these strides the
+// K-operand read (16 consecutive rows, one 16-byte chunk each) and the transposed V read
+// (8 rows x 64 bytes) hit distinct banks, and every read address is a per-lane base plus a
+// compile-time offset. The copy engine writes 1 KiB per instruction, so the padding slots
+// are simply filled with a duplicate chunk that is never read.
+//
+// Softmax: scores live in the exp2 domain (t = s·scale·log2 e). Each row keeps a reference
+// maximum m, moved when a tile's maximum exceeds it by more than kRescaleSlack; weights are
+// exp2(t - m) <= 2^kRescaleSlack, and the same reference serves the accumulated output, the
+// row sum and the final LSE. The output rescale runs only when some row of the wave moved.
 
 #include <type_traits>
 
@@ -31,37 +42,55 @@
 namespace attn {
 namespace {
 
-constexpr int BN = 64;  // keys per tile
+constexpr int BN = 64;                 // keys per tile
+// Log2 headroom before the reference maximum moves. Zero keeps the eager running maximum: the
+// largest weight of every row is then exactly 1.0, which bf16 represents exactly; a stale
+// reference would let that weight pick up a bf16 rounding error of up to 2^-9 relative.
+constexpr float kRescaleSlack = 0.0f;
 
-// Tile source: where the 64 key rows of a tile come from.
-enum TileKind : int { kDenseTile = 0, kColumnTile = 1 };
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 template <int D>
 struct TileCfg {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BN * D * 2;      // one K or V tile
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K + V
-  static constexpr int INSTR = TILE_BYTES / 1024;    // 1 KiB DMA instructions per tile
-  static constexpr int KSTEPS = D / 16;              // 32x32x16 MFMA steps over the head dim
-  static constexpr int DVB = D / 32;                 // 32-wide output column blocks
+  static constexpr int CPR = D / 8;                   // 16-byte chunks of data per row
+  static constexpr int KROW = 2 * D + 16;             // padded K row (bytes)
+  static constexpr int VROW = 2 * D + 64;             // padded V row (bytes)
+  static constexpr int KSPR = KROW / 16;              // 16-byte slots per K row
+  static constexpr int VSPR = VROW / 16;
+  static constexpr int KT_BYTES = BN * KROW;
+  static constexpr int VT_BYTES = BN * VROW;
+  static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+  static constexpr int KINSTR = KT_BYTES / 1024;      // 1 KiB copy instructions per K tile
+  static constexpr int VINSTR = VT_BYTES / 1024;
+  static constexpr int KSTEPS = D / 16;               // 32x32x16 MFMA steps over the head dim
+  static constexpr int DVB = D / 32;                  // 32-wide output column blocks
+  static_assert(KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0, "whole KiB tiles");
 };
 
-// Issue the asynchronous copy of one K tile and one V tile into LDS stage `st`.
-// key_of(r) must return a valid key row index (callers clamp), so every load is in bounds.
-template <int D, int NW, class KeyOf>
-__device__ __forceinline__ void issue_tile(const FwdArgs& a, char* st, const uint16_t* kbase,
-                                           const uint16_t* vbase, KeyOf key_of, int w, int l) {
+// Row r and chunk c that copy slot `slot` of a padded tile holds (padding slots duplicate
+// chunk 0 of their row).
+template <int SPR, int CPR>
+__device__ __forceinline__ void slot_rc(uint32_t slot, uint32_t& r, uint32_t& c) {
+  r = slot / SPR;
+  const uint32_t cs = slot % SPR;
+  c = cs < (uint32_t)CPR ? cs : 0u;
+}
+
+// Copy instruction i (K instructions first, then V) of one tile. key_of(r) must return a valid
+// key row, so every load is in bounds.
+template <int D, class KeyOf>
+__device__ __forceinline__ void copy_instr_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
+                                                const uint16_t* vbase, KeyOf key_of, int i, int l) {
   using C = TileCfg<D>;
-  static_assert(C::INSTR % NW == 0, "tile copy must split evenly over the waves");
-#pragma unroll
-  for (int ii = 0; ii < C::INSTR / NW; ++ii) {
-    const int i = w + NW * ii;
-    const uint32_t slot = (uint32_t)i * 64u + (uint32_t)l;
-    const uint32_t r = slot / C::CPR;
-    const uint32_t c = (slot % C::CPR) ^ Swz<D>::f(r);
-    const int key = key_of((int)r);
-    dma16(kbase + (int64_t)key * a.k_sl + c * 8, st + i * 1024);
-    dma16(vbase + (int64_t)key * a.v_sl + c * 8, st + C::TILE_BYTES + i * 1024);
+  uint32_t r, c;
+  if (i < C::KINSTR) {
+    slot_rc<C::KSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+    dma16(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + i * 1024);
+  } else {
+    const int iv = i - C::KINSTR;
+    slot_rc<C::VSPR, C::CPR>((uint32_t)iv * 64u + (uint32_t)l, r, c);
+    dma16(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
   }
 }
 
@@ -69,70 +98,91 @@ __device__ __forceinline__ void issue_tile(const FwdArgs& a, char* st, const uin
 // instructions, for tiles whose 64 rows are consecutive keys all inside the sequence.
 template <int D, int NW>
 struct TileOffsets {
-  uint32_t k[TileCfg<D>::INSTR / NW];
-  uint32_t v[TileCfg<D>::INSTR / NW];
+  static constexpr int NI = (TileCfg<D>::KINSTR + TileCfg<D>::VINSTR + NW - 1) / NW;
+  uint32_t off[NI];
   __device__ __forceinline__ void init(const FwdArgs& a, int w, int l) {
     using C = TileCfg<D>;
 #pragma unroll
-    for (int ii = 0; ii < C::INSTR / NW; ++ii) {
-      const uint32_t slot = (uint32_t)(w + NW * ii) * 64u + (uint32_t)l;
-      const uint32_t r = slot / C::CPR;
-      const uint32_t c = (slot % C::CPR) ^ Swz<D>::f(r);
-      k[ii] = r * (uint32_t)a.k_sl + c * 8u;
-      v[ii] = r * (uint32_t)a.v_sl + c * 8u;
+    for (int ii = 0; ii < NI; ++ii) {
+      const int i = w + NW * ii;
+      uint32_t r, c;
+      if (i < C::KINSTR) {
+        slot_rc<C::KSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+        off[ii] = r * (uint32_t)a.k_sl + c * 8u;
+      } else {
+        slot_rc<C::VSPR, C::CPR>((uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l, r, c);
+        off[ii] = r * (uint32_t)a.v_sl + c * 8u;
+      }
     }
   }
 };
 
 template <int D, int NW>
 __device__ __forceinline__ void issue_tile_fast(char* st, const uint16_t* ktile,
-                                                const uint16_t* vtile, const TileOffsets<D, NW>& off,
+                                                const uint16_t* vtile, const TileOffsets<D, NW>& o,
                                                 int w) {
   using C = TileCfg<D>;
+  // the copy instruction index, the source tile and the LDS destination are wave-uniform
+  const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-  for (int ii = 0; ii < C::INSTR / NW; ++ii) {
-    const int i = w + NW * ii;
-    dma16(ktile + off.k[ii], st + i * 1024);
-    dma16(vtile + off.v[ii], st + C::TILE_BYTES + i * 1024);
+  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
+    const int i = wu + NW * ii;
+    if (i < C::KINSTR + C::VINSTR) {
+      const bool is_k = i < C::KINSTR;
+      const uint16_t* src = is_k ? ktile : vtile;
+      const int dst = is_k ? i * 1024 : C::KT_BYTES + (i - C::KINSTR) * 1024;
+      dma16(src + o.off[ii], st + dst);
+    }
   }
 }
 
-template <int N>
-using ic = std::integral_constant<int, N>;
+template <int D, int NW, class KeyOf>
+__device__ __forceinline__ void issue_tile_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
+                                                const uint16_t* vbase, KeyOf key_of, int w, int l) {
+  using C = TileCfg<D>;
+#pragma unroll
+  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
+    const int i = w + NW * ii;
+    if (i < C::KINSTR + C::VINSTR) copy_instr_slow<D>(a, st, kbase, vbase, key_of, i, l);
+  }
+}
 
 template <int D>
 struct WaveState {
   bf16x8 qop[TileCfg<D>::KSTEPS];
   f32x16 acc[TileCfg<D>::DVB];
-  float m;     // running max of scale*log2(e)*s (same in lanes l and l^32)
-  float lsum;  // lane-partial running sum of exp2(t - m)
+  float m;        // reference maximum in the exp2 domain (same in lanes l and l^32)
+  float lsum;     // lane-partial sum of exp2(t - m)
+  uint32_t kofs;  // lane byte offset of its K-operand reads inside a tile
+  uint32_t vofs;  // lane byte offset of its transposed V reads inside a tile
 };
 
-// Math of one tile for one wave. kidx(local key) gives the key position (or -1 if the slot
-// holds no key); need_mask selects the masked path.
+// Math of one tile for one wave. When `masked`, kidx(local key) gives the key position (or -1
+// if the slot holds no key) and invisible keys are masked; otherwise every key is visible.
+// MFMA groups run at raised wave priority so that, with two waves per SIMD, the wave feeding
+// the matrix core wins issue arbitration and the other wave's softmax fills the gaps.
 template <int D, class KeyIdx>
 __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, const char* st,
-                                          int row, bool need_mask, KeyIdx kidx, int l) {
+                                          int row, bool masked, KeyIdx kidx, int l) {
   using C = TileCfg<D>;
-  const char* kt = st;
-  const char* vt = st + C::TILE_BYTES;
+  const char* kt = st + ws.kofs;
+  const char* vt = st + C::KT_BYTES + ws.vofs;
   const int h = l >> 5;
-  const uint32_t rr = (uint32_t)(l & 31);
 
-  // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks)
+  // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks); k-step s reads chunk 2s + h
   f32x16 s0 = {}, s1 = {};
-  const uint32_t sw0 = Swz<D>::f(rr), sw1 = Swz<D>::f(rr + 32);
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int s = 0; s < C::KSTEPS; ++s) {
-    const uint32_t c = (uint32_t)(2 * s + h);
-    const bf16x8 k0 = lds_read_bf16x8(kt, (rr * C::CPR + (c ^ sw0)) * 16u);
-    const bf16x8 k1 = lds_read_bf16x8(kt, ((rr + 32) * C::CPR + (c ^ sw1)) * 16u);
+    const bf16x8 k0 = lds_read_bf16x8(kt, 32u * s);
+    const bf16x8 k1 = lds_read_bf16x8(kt, 32u * C::KROW + 32u * s);
     s0 = mfma32(k0, ws.qop[s], s0);
     s1 = mfma32(k1, ws.qop[s], s1);
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // ---- mask: slot (block kb, j) holds local key 32*kb + 8*(j/4) + 4*h + j%4
-  if (need_mask) {
+  if (masked) {
     const int lim = a.causal ? row + a.off : 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -144,15 +194,24 @@ __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, co
     }
   }
 
-  // ---- online softmax (exp2 domain)
+  // ---- online softmax (exp2 domain, lazily moved reference maximum)
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
   mx = fmaxf(mx, xor_shuffle(mx, 32));
-  const float mnew = fmaxf(ws.m, mx * a.sl2);
-  const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-  const float alpha = fast_exp2(ws.m - muse);
-  ws.m = mnew;
+  const float tmax = mx * a.sl2;
+  const bool move = tmax > ws.m + kRescaleSlack;  // false while the tile is fully masked
+  if (__any(move)) {
+    const float mnew = move ? tmax : ws.m;
+    const float alpha = move ? fast_exp2(ws.m - mnew) : 1.0f;  // exp2(-inf) = 0 on first use
+    ws.m = mnew;
+    ws.lsum *= alpha;
+#pragma unroll
+    for (int b = 0; b < C::DVB; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ws.acc[b][j] *= alpha;
+  }
+  const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -160,13 +219,7 @@ __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, co
     s1[j] = fast_exp2(fmaf(s1[j], a.sl2, -muse));
     psum += s0[j] + s1[j];
   }
-  ws.lsum = ws.lsum * alpha + psum;
-  if (__any(alpha != 1.0f)) {
-#pragma unroll
-    for (int b = 0; b < C::DVB; ++b)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ws.acc[b][j] *= alpha;
-  }
+  ws.lsum += psum;
 
   // ---- Pᵀ operands: k-step ks covers local keys 16*ks .. 16*ks+15
   bf16x8 pop[4];
@@ -177,21 +230,18 @@ __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, co
 
   // ---- Oᵀ += Vᵀ·Pᵀ. Operand slot i of lane l covers key 16*ks + 8*(i/4) + 4*(l/32) + i%4,
   // fetched with two transposed reads: lane 4j+c of each 16-lane group addresses
-  // row 16*ks + 4*(l/32) + j (+8 for the second read) at column dv0 + 4c.
-  const int G = l >> 4;
-  const int jj = (l & 15) >> 2;
-  const int cc = l & 3;
-  const int hh = G >> 1;
+  // row 16*ks + 4*(l/32) + j (+8 for the second read) at column 32*b + 16*((l/16)%2) + 4c.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int b = 0; b < C::DVB; ++b) {
-    const uint32_t dv = (uint32_t)(32 * b + 16 * (G & 1) + 4 * cc);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t rlo = (uint32_t)(16 * ks + 4 * hh + jj);
-      const bf16x8 vop = lds_read_tr_pair(vt, elem_off<D>(rlo, dv), elem_off<D>(rlo + 8, dv));
+      const uint32_t o = 16u * ks * C::VROW + 64u * b;
+      const bf16x8 vop = lds_read_tr_pair(vt, o, o + 8u * C::VROW);
       ws.acc[b] = mfma32(vop, pop[ks], ws.acc[b]);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D>
@@ -211,6 +261,12 @@ __device__ __forceinline__ void load_q(const FwdArgs& a, WaveState<D>& ws, int b
   for (int bb = 0; bb < C::DVB; ++bb) ws.acc[bb] = f32x16{};
   ws.m = -INFINITY;
   ws.lsum = 0.f;
+  // K operand: row l%32 (+32 for the second key block), chunk 2s + l/32
+  ws.kofs = (uint32_t)(l & 31) * C::KROW + (uint32_t)h * 16u;
+  // V operand: group G = l/16, row 4*(G/2) + (l%16)/4, column 16*(G%2) + 4*(l%4)
+  const int G = l >> 4;
+  ws.vofs = (uint32_t)(4 * (G >> 1) + ((l & 15) >> 2)) * C::VROW +
+            (uint32_t)(16 * (G & 1) + 4 * (l & 3)) * 2u;
 }
 
 template <int D>
@@ -256,7 +312,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_dense_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
   constexpr int BM = 32 * NW;
-  // One array per ring stage (see the split-KV kernel): stage indices are compile-time.
+  // One array per ring stage: with compile-time stage indices the compiler can tell the stage
+  // being read from the stage still being filled and does not wait for that copy.
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
 
@@ -290,14 +347,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dense_kernel(const FwdArgs a) 
   const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
   const int lkm1 = a.Lk - 1;
 
+  // Tiles [0, nfull) are complete and fully visible to every row of the workgroup; the rest
+  // (causal diagonal, ragged end) take the masked path.
+  int nfull = a.Lk / BN;
+  if (a.causal) nfull = min(nfull, max(0, (q0 + a.off + 1) / BN));
+  nfull = min(nfull, ntiles);
+  const int64_t kstep = (int64_t)BN * a.k_sl, vstep = (int64_t)BN * a.v_sl;
+  const uint16_t* knext = kb;  // first key row of the next tile to copy
+  const uint16_t* vnext = vb;
+
   auto issue = [&](auto S, int t) {
     char* st = decltype(S)::value == 0 ? st0 : st1;
     const int base = t * BN;
     if (base + BN <= a.Lk) {
-      issue_tile_fast<D, NW>(st, kb + (int64_t)base * a.k_sl, vb + (int64_t)base * a.v_sl, off, w);
+      issue_tile_fast<D, NW>(st, knext, vnext, off, w);
     } else {
-      issue_tile<D, NW>(a, st, kb, vb, [&](int r) { return min(base + r, lkm1); }, w, l);
+      issue_tile_slow<D, NW>(a, st, kb, vb, [&](int r) { return min(base + r, lkm1); }, w, l);
     }
+    knext += kstep;
+    vnext += vstep;
   };
   auto step = [&](auto S, int t) {
     constexpr int s = decltype(S)::value;
@@ -307,9 +375,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dense_kernel(const FwdArgs a) 
     const int base = t * BN;
     // wave-uniform: skip tiles entirely beyond this wave's causal horizon
     if (a.causal && base > qwlast + a.off) return;
-    bool need_mask = (base + BN > a.Lk);
-    if (a.causal && base + BN - 1 > qw0 + a.off) need_mask = true;
-    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, need_mask,
+    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, t >= nfull,
                  [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
   };
 
@@ -327,8 +393,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_dense_kernel(const FwdArgs a) 
 // causally visible to the block and not already inside a listed block (so a key is never
 // counted twice), 64 at a time, in ascending key order.
 // ------------------------------------------------------------------------------------------
-constexpr int kSeg = 1024;          // columns examined per compaction pass
-constexpr int kMaxBitmapWords = 1024;  // listed-block bitmap: up to 32768 key blocks (2M keys)
+constexpr int kSeg = 512;              // columns examined per compaction pass
+constexpr int kMaxBitmapWords = 512;   // listed-block bitmap: up to 16384 key blocks (1M keys)
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
@@ -393,8 +459,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
     if (base >= 0 && base + BN <= a.Lk) {
       issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl, off, w);
     } else {
-      issue_tile<D, NW>(a, st, kbp, vbp,
-                        [&](int r) { return base < 0 ? 0 : min(base + r, lkm1); }, w, l);
+      issue_tile_slow<D, NW>(a, st, kbp, vbp,
+                             [&](int r) { return base < 0 ? 0 : min(base + r, lkm1); }, w, l);
     }
   };
   auto step_blk = [&](auto S, int t) {
@@ -405,9 +471,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
     const int base = blk_base(t);
     if (base < 0) return;
     if (a.causal && base > qwlast + a.off) return;
-    bool need_mask = (base + BN > a.Lk);
-    if (a.causal && base + BN - 1 > qw0 + a.off) need_mask = true;
-    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, need_mask,
+    const bool masked = base + BN > a.Lk || (a.causal && base + BN - 1 > qw0 + a.off);
+    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, masked,
                  [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
   };
   if (nb > 0) issue_blk(ic<0>{}, 0);
@@ -455,7 +520,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
     auto issue_col = [&](auto S, int t) {
       char* st = decltype(S)::value == 0 ? st0 : st1;
       const int cb = t * BN;
-      issue_tile<D, NW>(a, st, kbp, vbp, [&](int r) { return kept[cb + r < cnt ? cb + r : 0]; }, w, l);
+      issue_tile_slow<D, NW>(a, st, kbp, vbp,
+                             [&](int r) { return kept[cb + r < cnt ? cb + r : 0]; }, w, l);
     };
     auto step_col = [&](auto S, int t) {
       constexpr int s = decltype(S)::value;

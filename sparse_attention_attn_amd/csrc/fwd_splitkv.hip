@@ -310,22 +310,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int64_t row = gid / TPR;
   const int c4 = (int)(gid % TPR);
   if (row >= rows) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.lse_part[(int64_t)s * rows + row]);
+  // Single pass with a running maximum (the combine's weights, rescaled when the maximum
+  // grows); four splits per iteration so their loads are in flight together.
+  float mx = -INFINITY, den = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  if (mx != -INFINITY) {
-#pragma unroll 8
-    for (int s = 0; s < a.S; ++s) {
-      const float ls = a.lse_part[(int64_t)s * rows + row];
-      const float ws = (ls == -INFINITY) ? 0.f : expf(ls - mx);
-      const float4 x = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
-      den += ws;
-      o.x += ws * x.x;
-      o.y += ws * x.y;
-      o.z += ws * x.z;
-      o.w += ws * x.w;
+  for (int s0 = 0; s0 < a.S; s0 += 4) {
+    float ls[4];
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u;
+      if (s < a.S) {
+        ls[u] = a.lse_part[(int64_t)s * rows + row];
+        x[u] = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
+      } else {
+        ls[u] = -INFINITY;
+        x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
+    float mnew = mx;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mnew = fmaxf(mnew, ls[u]);
+    if (mnew == -INFINITY) continue;
+    const float r = (mx == -INFINITY) ? 0.f : expf(mx - mnew);
+    den *= r;
+    o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float ws = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - mnew);
+      den += ws;
+      o.x += ws * x[u].x;
+      o.y += ws * x[u].y;
+      o.z += ws * x[u].z;
+      o.w += ws * x[u].w;
+    }
+    mx = mnew;
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const int pos = (int)(row % a.Lq);

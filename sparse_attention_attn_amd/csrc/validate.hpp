@@ -45,7 +45,7 @@ int check_blocksparse_lists(const char* fn, const int32_t* blk_ptr, const int32_
                             int Lk, int block_m, int block_n);
 
 // Largest key length the block-sparse kernel's listed-block bitmap covers.
-constexpr int kSparseMaxLk = 1 << 21;
+constexpr int kSparseMaxLk = 1 << 20;
 
 const char* status_string(int status);
 

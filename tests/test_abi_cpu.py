@@ -116,7 +116,7 @@ def test_blocksparse_entry_validation():
     assert f(bm=128) == S.ATTN_ERR_UNSUPPORTED
     assert f(ptr=None) == S.ATTN_ERR_INVALID_ARG
     assert "blk_ptr / col_ptr" in S.attn_last_error()
-    assert f(Lk=(1 << 21) + 64) == S.ATTN_ERR_UNSUPPORTED
+    assert f(Lk=(1 << 20) + 64) == S.ATTN_ERR_UNSUPPORTED
 
 
 def test_num_splits_heuristic_is_pure_and_in_range():
