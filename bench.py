@@ -193,7 +193,7 @@ def cpu_baseline(w, budget_s):
     kf = k.float().numpy().astype(np.float64)
     vf = v.float().numpy().astype(np.float64)
     sc = A.effective_scale(w.scale)
-    rows = sampled_rows(w.Lq, 512, 1000 * w.index + 4, edge=64)
+    rows = sampled_rows(w.Lq, 4096, 1000 * w.index + 4, edge=64)
     per_row_pairs = np.clip(rows + (w.Lk - w.Lq) + 1, 0, w.Lk).sum()
     t0 = time.perf_counter()
     heads = 0

@@ -23,11 +23,13 @@
 // register layout; the M-padding reason the FlashMLA-ETAP page gives for its transposed flow
 // does not arise with 32- or 16-row MFMA tiles.)
 //
-// LDS layout: K rows padded to 2D+16 bytes and V rows to 2D+64 bytes. With these strides the
-// K-operand read (16 consecutive rows, one 16-byte chunk each) and the transposed V read
-// (8 rows x 64 bytes) hit distinct banks, and every read address is a per-lane base plus a
-// compile-time offset. The copy engine writes 1 KiB per instruction, so the padding slots
-// are simply filled with a duplicate chunk that is never read.
+// LDS layout: the K tile is stored in MFMA-operand order (1 KiB slab per k-step and key block,
+// lane l's 16 bytes at offset 16*l), so every K-operand read is a linear ds_read_b128, the
+// pattern that reaches the full LDS read bandwidth (a row-major tile read by 32 rows per
+// instruction reaches half of it). V rows are padded to 2D+64 bytes, which keeps the
+// transposed V read (8 rows x 64 bytes per instruction) at full bandwidth. Every read address
+// is a per-lane base plus a compile-time offset. The copy engine writes 1 KiB per instruction;
+// V padding slots receive a duplicate chunk that is never read.
 //
 // Softmax: scores live in the exp2 domain (t = s·scale·log2 e). Each row keeps a reference
 // maximum m, moved when a tile's maximum exceeds it by more than kRescaleSlack; weights are
@@ -54,19 +56,26 @@ using ic = std::integral_constant<int, N>;
 template <int D>
 struct TileCfg {
   static constexpr int CPR = D / 8;                   // 16-byte chunks of data per row
-  static constexpr int KROW = 2 * D + 16;             // padded K row (bytes)
+  static constexpr int KSTEPS = D / 16;               // 32x32x16 MFMA steps over the head dim
+  static constexpr int KSLABS = 2 * KSTEPS;           // K tile: 1 KiB operand slabs
   static constexpr int VROW = 2 * D + 64;             // padded V row (bytes)
-  static constexpr int KSPR = KROW / 16;              // 16-byte slots per K row
-  static constexpr int VSPR = VROW / 16;
-  static constexpr int KT_BYTES = BN * KROW;
+  static constexpr int VSPR = VROW / 16;              // 16-byte slots per V row
+  static constexpr int KT_BYTES = KSLABS * 1024;
   static constexpr int VT_BYTES = BN * VROW;
   static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
-  static constexpr int KINSTR = KT_BYTES / 1024;      // 1 KiB copy instructions per K tile
+  static constexpr int KINSTR = KSLABS;               // 1 KiB copy instructions per K tile
   static constexpr int VINSTR = VT_BYTES / 1024;
-  static constexpr int KSTEPS = D / 16;               // 32x32x16 MFMA steps over the head dim
   static constexpr int DVB = D / 32;                  // 32-wide output column blocks
-  static_assert(KT_BYTES % 1024 == 0 && VT_BYTES % 1024 == 0, "whole KiB tiles");
+  static_assert(VT_BYTES % 1024 == 0, "whole KiB tiles");
 };
+
+// K slab (kb, s) holds, for lane l, the 16 bytes of key row 32*kb + l%32 at head-dim chunk
+// 2s + l/32: exactly the A operand of k-step s for key block kb, read linearly.
+template <int D>
+__device__ __forceinline__ void kslab_rc(int i, int l, uint32_t& r, uint32_t& c) {
+  r = 32u * (uint32_t)(i / TileCfg<D>::KSTEPS) + (uint32_t)(l & 31);
+  c = 2u * (uint32_t)(i % TileCfg<D>::KSTEPS) + (uint32_t)(l >> 5);
+}
 
 // Row r and chunk c that copy slot `slot` of a padded tile holds (padding slots duplicate
 // chunk 0 of their row).
@@ -85,7 +94,7 @@ __device__ __forceinline__ void copy_instr_slow(const FwdArgs& a, char* st, cons
   using C = TileCfg<D>;
   uint32_t r, c;
   if (i < C::KINSTR) {
-    slot_rc<C::KSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+    kslab_rc<D>(i, l, r, c);
     dma16(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + i * 1024);
   } else {
     const int iv = i - C::KINSTR;
@@ -93,6 +102,20 @@ __device__ __forceinline__ void copy_instr_slow(const FwdArgs& a, char* st, cons
     dma16(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
   }
 }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    // gfx9 encoding: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt at
+    // their maxima (no wait on them)
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+}
+// Workgroup barrier without a memory fence (the copies it orders are waited for explicitly).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
 // Per-lane element offsets (relative to a tile's first key row) of this wave's copy
 // instructions, for tiles whose 64 rows are consecutive keys all inside the sequence.
@@ -107,7 +130,7 @@ struct TileOffsets {
       const int i = w + NW * ii;
       uint32_t r, c;
       if (i < C::KINSTR) {
-        slot_rc<C::KSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+        kslab_rc<D>(i, l, r, c);
         off[ii] = r * (uint32_t)a.k_sl + c * 8u;
       } else {
         slot_rc<C::VSPR, C::CPR>((uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l, r, c);
@@ -169,13 +192,13 @@ __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, co
   const char* vt = st + C::KT_BYTES + ws.vofs;
   const int h = l >> 5;
 
-  // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks); k-step s reads chunk 2s + h
+  // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks), one K slab per operand
   f32x16 s0 = {}, s1 = {};
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int s = 0; s < C::KSTEPS; ++s) {
-    const bf16x8 k0 = lds_read_bf16x8(kt, 32u * s);
-    const bf16x8 k1 = lds_read_bf16x8(kt, 32u * C::KROW + 32u * s);
+    const bf16x8 k0 = lds_read_bf16x8(kt, 1024u * s);
+    const bf16x8 k1 = lds_read_bf16x8(kt, 1024u * (C::KSTEPS + s));
     s0 = mfma32(k0, ws.qop[s], s0);
     s1 = mfma32(k1, ws.qop[s], s1);
   }
@@ -261,8 +284,8 @@ __device__ __forceinline__ void load_q(const FwdArgs& a, WaveState<D>& ws, int b
   for (int bb = 0; bb < C::DVB; ++bb) ws.acc[bb] = f32x16{};
   ws.m = -INFINITY;
   ws.lsum = 0.f;
-  // K operand: row l%32 (+32 for the second key block), chunk 2s + l/32
-  ws.kofs = (uint32_t)(l & 31) * C::KROW + (uint32_t)h * 16u;
+  // K operand: lane l's 16 bytes of every slab
+  ws.kofs = (uint32_t)l * 16u;
   // V operand: group G = l/16, row 4*(G/2) + (l%16)/4, column 16*(G%2) + 4*(l%4)
   const int G = l >> 4;
   ws.vofs = (uint32_t)(4 * (G >> 1) + ((l & 15) >> 2)) * C::VROW +
