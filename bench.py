@@ -15,7 +15,6 @@ Inputs are resident in HBM before the timed region starts.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -93,11 +92,8 @@ def time_steps(step, steps, warmup):
 
 
 def kernel_source_hash(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "sparse_attention_attn_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from sparse_attention_attn_amd.profiling import kernel_source_hash as h
+    return h(files)
 
 
 def load_traffic(workload, src_hash):

@@ -1,0 +1,178 @@
+"""Summaries of rocprofv3 output for the kernels of libattn.so.
+
+Turns the CSV files that `rocprofv3 --kernel-trace --stats` and `rocprofv3 --pmc FETCH_SIZE`
+/ `--pmc WRITE_SIZE` write into the short text summaries kept with the sources, and into the
+per-launch HBM traffic record that bench.py attaches to its roofline figure.
+
+HBM traffic calibration. FETCH_SIZE and WRITE_SIZE count memory requests leaving the L2 in
+KiB; how a request is sized depends on the chip, so the raw counts are scaled by what the same
+counter reads for a plain device-to-device copy of known size (bench.py --copy-calib-mib N
+runs one such copy, which the runtime executes as `__amd_rocclr_copyBuffer` dispatches):
+factor = bytes the copy must move / bytes the counter reports for it.
+
+Usage (after the three rocprofv3 runs, see the header of each summary for the commands):
+
+    python -m sparse_attention_attn_amd.profiling summary --stats DIR --fetch DIR --write DIR \
+        --calib-mib 1024 --kernel "fwd_dense_kernel<128, 4>" --workload gqa_prefill_8k \
+        --command "..." --out profiles/fwd_dense_kernel_gqa_prefill_8k.md [--traffic-json F]
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_source_hash(files):
+    """First 16 hex digits of the SHA-256 of the named csrc files, concatenated in order."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def read_kernel_stats(stats_dir):
+    """Rows of *_kernel_stats.csv as dicts with numeric fields."""
+    path = _one(os.path.join(stats_dir, "**", "*kernel_stats.csv"))
+    out = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            out.append({"name": r["Name"], "calls": int(r["Calls"]),
+                        "total_ns": float(r["TotalDurationNs"]), "avg_ns": float(r["AverageNs"]),
+                        "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+                        "pct": float(r["Percentage"])})
+    return out
+
+
+def read_counter(counter_dir, counter):
+    """(kernel name, value) per dispatch, in dispatch order, for one counter."""
+    path = _one(os.path.join(counter_dir, "**", "*counter_collection.csv"))
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(n, v) for _, n, v in rows]
+
+
+def copy_factor(dispatches, calib_mib, moved_per_mib=1.0):
+    """Scale factor from the first run of copy dispatches (the calibration copy)."""
+    total = 0.0
+    seen = False
+    for name, v in dispatches:
+        if COPY_KERNEL in name:
+            total += v
+            seen = True
+        elif seen:
+            break
+    if not seen or total <= 0:
+        raise ValueError("no calibration copy dispatch found")
+    return calib_mib * 1024.0 * moved_per_mib / total
+
+
+def per_dispatch(dispatches, kernel):
+    vals = [v for n, v in dispatches if kernel in n]
+    if not vals:
+        raise ValueError(f"kernel {kernel!r} not found")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summary(stats_dir, fetch_dir, write_dir, calib_mib, kernel, workload, command,
+            algorithmic_bytes=None):
+    stats = read_kernel_stats(stats_dir)
+    rec = {"workload": workload, "kernel": kernel, "command": command}
+    mine = [s for s in stats if kernel in s["name"]]
+    if mine:
+        rec["avg_ns"] = mine[0]["avg_ns"]
+        rec["calls"] = mine[0]["calls"]
+    if fetch_dir and write_dir:
+        fd = read_counter(fetch_dir, "FETCH_SIZE")
+        wd = read_counter(write_dir, "WRITE_SIZE")
+        ff = copy_factor(fd, calib_mib)
+        wf = copy_factor(wd, calib_mib)
+        fk, nf = per_dispatch(fd, kernel)
+        wk, nw = per_dispatch(wd, kernel)
+        rec.update({"fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_factor": ff,
+                    "write_factor": wf, "dispatches_counted": min(nf, nw),
+                    "hbm_bytes_per_launch": int(round((fk * ff + wk * wf) * 1024.0))})
+        if algorithmic_bytes:
+            rec["algorithmic_bytes"] = int(algorithmic_bytes)
+            rec["traffic_over_algorithmic"] = rec["hbm_bytes_per_launch"] / algorithmic_bytes
+    return rec, stats
+
+
+def render_md(rec, stats, stats_cmd, fetch_cmd, write_cmd):
+    lines = [f"# {rec['kernel']} — {rec['workload']}", ""]
+    lines += ["Kernel-trace statistics command (run from the repository root):", "",
+              "```", stats_cmd, "```", ""]
+    lines += ["| kernel | calls | avg µs | min µs | max µs | % of GPU time |",
+              "|---|---|---|---|---|---|"]
+    for s in stats:
+        lines.append(f"| `{s['name']}` | {s['calls']} | {s['avg_ns'] / 1e3:.1f} | "
+                     f"{s['min_ns'] / 1e3:.1f} | {s['max_ns'] / 1e3:.1f} | {s['pct']:.2f} |")
+    lines.append("")
+    if "hbm_bytes_per_launch" in rec:
+        lines += ["Counter runs (one counter per run):", "", "```", fetch_cmd, write_cmd, "```", "",
+                  f"- FETCH_SIZE per dispatch (raw): {rec['fetch_kib_raw']:.1f} KiB, copy "
+                  f"calibration factor {rec['fetch_factor']:.4f}",
+                  f"- WRITE_SIZE per dispatch (raw): {rec['write_kib_raw']:.1f} KiB, copy "
+                  f"calibration factor {rec['write_factor']:.4f}",
+                  f"- HBM-side traffic per launch: {rec['hbm_bytes_per_launch']:,} B"]
+        if "algorithmic_bytes" in rec:
+            lines.append(f"- algorithmic bytes per launch: {rec['algorithmic_bytes']:,} B "
+                         f"(traffic / algorithmic = {rec['traffic_over_algorithmic']:.3f})")
+        lines.append("")
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m sparse_attention_attn_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summary")
+    s.add_argument("--stats", required=True)
+    s.add_argument("--fetch")
+    s.add_argument("--write")
+    s.add_argument("--calib-mib", type=int, default=1024)
+    s.add_argument("--kernel", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--algorithmic-bytes", type=float, default=None)
+    s.add_argument("--stats-command", required=True)
+    s.add_argument("--fetch-command", default="")
+    s.add_argument("--write-command", default="")
+    s.add_argument("--source-files", default="",
+                   help="comma list of csrc files whose hash tags the traffic record")
+    s.add_argument("--out", required=True)
+    s.add_argument("--traffic-json")
+    a = ap.parse_args(argv)
+    rec, stats = summary(a.stats, a.fetch, a.write, a.calib_mib, a.kernel, a.workload,
+                         a.stats_command, a.algorithmic_bytes)
+    with open(a.out, "w") as fh:
+        fh.write(render_md(rec, stats, a.stats_command, a.fetch_command, a.write_command))
+    if a.traffic_json:
+        if a.source_files:
+            rec["kernel_source_sha256_16"] = kernel_source_hash(a.source_files.split(","))
+        rec["counter_commands"] = [a.fetch_command, a.write_command]
+        with open(a.traffic_json, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+    print(json.dumps({k: v for k, v in rec.items() if k != "command"}))
+
+
+if __name__ == "__main__":
+    main()
