@@ -23,7 +23,8 @@
  * Tensors. Q is [B, Lq, Hq, Dqk], K is [B, Lk, Hkv, Dqk], V is [B, Lk, Hkv, Dv], O is
  *   [B, Lq, Hq, Dv], all bfloat16, described by attn_tensor_t: a DEVICE pointer plus element
  *   strides for the batch, sequence and head dimensions; the head-dim stride is 1. The data
- *   pointer must be 16-byte aligned and every stride a multiple of 8 elements. Contiguous
+ *   pointer must be 16-byte aligned and every stride a multiple of 8 elements; the sequence
+ *   stride of Q, K and V may not exceed 2^24 elements (ATTN_ERR_UNSUPPORTED). Contiguous
  *   [B, L, H, D] has stride_h = D, stride_l = H·D, stride_b = L·H·D.
  * LSE. Optional fp32 log-sum-exp of each query row, natural log of Σ_j exp(scale·q·k_j) over
  *   the visible keys, DEVICE pointer, contiguous [B, Hq, Lq]. Pass NULL to skip it. A row with

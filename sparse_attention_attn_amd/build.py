@@ -18,8 +18,15 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
-SOURCES = ["fwd_prefill.hip", "fwd_splitkv.hip", "api.cpp", "validate.cpp"]
+SOURCES = ["fwd_dense.hip", "fwd_prefill.hip", "fwd_splitkv.hip", "api.cpp", "validate.cpp"]
 ARCH = "gfx950"
+# Per-source extra flags for the dense kernel:
+#  * no IEEE mode and no NaN semantics: its row maxima then lower to plain v_max3_f32 with no
+#    operand quieting (inputs are finite; masked scores are -inf, which both settings keep);
+#  * MFMA results in VGPRs: the scores feed VALU code directly, and the register allocator
+#    parks the rarely touched output accumulators in AGPRs instead.
+EXTRA = {"fwd_dense.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans",
+                           "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -41,7 +48,7 @@ def _common_flags():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + _common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _common_flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"] if src == "api.cpp" else []
     if verbose:

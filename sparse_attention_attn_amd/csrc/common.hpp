@@ -75,6 +75,47 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
 }
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ------------------------------------------------------------------------------------------
+// LDS addressed by 32-bit byte addresses. The compiler folds a compile-time offset of up to
+// 64 KiB into the instruction's offset field, so reads at (base register + constant) need no
+// address arithmetic even when the LDS footprint exceeds 64 KiB.
+// ------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint4 lds_uint4_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* shared_ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)shared_ptr;
+}
+__device__ __forceinline__ bf16x8 lds_read_b128_at(uint32_t addr) {
+  return __builtin_bit_cast(bf16x8, *(const lds_uint4_t*)(uintptr_t)addr);
+}
+__device__ __forceinline__ bf16x8 lds_read_tr_pair_at(uint32_t lo, uint32_t hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)lo);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(uintptr_t)hi);
+  const uint2 ua = __builtin_bit_cast(uint2, a);
+  const uint2 ub = __builtin_bit_cast(uint2, b);
+  return __builtin_bit_cast(bf16x8, make_uint4(ua.x, ua.y, ub.x, ub.y));
+}
+
+// Asynchronous 16-byte-per-lane global -> LDS copy written as one instruction with a scalar
+// base: lane l reads sbase + voff (bytes) and its 16 bytes land at LDS address lds + 16*l
+// (`lds` is wave-uniform and goes through M0). The compiler does not see this LDS write, so it
+// adds no waits of its own before later LDS reads: the caller orders them with an explicit
+// vmcnt wait and a workgroup barrier.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds) {
+  // The base and the LDS address are wave-uniform: pin them to scalar registers. readfirstlane
+  // returns a signed int, so each half is zero-extended explicitly.
+  const uint64_t p = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
+  // The compiler's hazard checks do not look inside inline assembly. s_nop 4 provides the wait
+  // states this load needs after the instructions that produce its operands: 5 after a VALU
+  // write of an SGPR it reads, 1 after an SALU write of M0.
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps),
+               "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 

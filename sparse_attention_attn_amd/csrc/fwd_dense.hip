@@ -1,0 +1,470 @@
+// fwd_dense.hip — fused dense attention forward (prefill; causal or not, GQA) on gfx950.
+//
+// What is computed: O = softmax(scale·Q·Kᵀ + mask)·V and the LSE of every query row ("Resumen
+// Técnico: FlashMLA-ETAP", section "Mecanismo Central"), tile by tile with running softmax
+// statistics kept on chip ("Activar Flash Attention con llama.cpp para optimizar la
+// inferencia", section "¿Qué es Flash Attention y por qué es crucial para llama.cpp?").
+//
+// Work decomposition. One workgroup (one per CU) owns 256 query rows of one (batch, query
+// head). Its waves own NR 32-row MFMA blocks each: NR = 1 gives 8 waves (two per SIMD, so each
+// SIMD also interleaves two instruction streams); NR = 2 gives 4 waves (one per SIMD) whose
+// K and V operand reads from LDS each feed two MFMAs.
+//
+// Per 64-key tile and wave, the products are formed transposed (the Sᵀ accumulator holds 16
+// keys of ONE query per lane, so the same registers, rounded to bf16, are the B operand Pᵀ of
+// Oᵀ += Vᵀ·Pᵀ):  Sᵀ = K·Qᵀ with 32x32x16 bf16 MFMA, K from LDS, Qᵀ in registers; Vᵀ from the
+// row-major V tile through the LDS transpose read.
+//
+// Software pipeline. Iteration t of a wave issues the MFMAs of Sᵀ(t+1) and of Oᵀ += Vᵀ(t-1)·
+// Pᵀ(t-1) and, independent of both, the softmax of tile t (max, exp2, bf16 packing, sums) on
+// the vector ALU, so a single wave keeps the matrix core and the VALU busy at the same time.
+// K/V tiles stream through a 4-stage LDS ring filled by asynchronous global->LDS copies:
+// iteration t copies tile t+2 while tiles t+1 (K read) and t-1 (V read) are in use. One
+// workgroup barrier per iteration frees the stage of tile t-2.
+//
+// Softmax. Scores live in the exp2 domain (x = s·scale·log2 e). Each row keeps a reference
+// maximum m that moves only when a tile's maximum exceeds it by more than kSlack, so the
+// output rescale (a multiply of all accumulators) almost never runs; weights are
+// exp2(x - m) <= 2^kSlack. Two row sums are kept: the sum of the bf16-rounded weights, which
+// normalises O (numerator and denominator then use the same weights, so a row dominated by one
+// key returns that key's value exactly), and the fp32 sum of the unrounded weights, which
+// gives the LSE.
+
+#include "tile_io.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kStages = 4;
+constexpr float kSlack = 8.0f;  // log2 headroom of the lazily moved reference maximum
+// Row blocks (32 query rows each) per wave of the dense kernel.
+constexpr int kDenseNR = 1;
+
+template <int N>
+using icn = std::integral_constant<int, N>;
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(icn<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(fmaxf(a, b), c);
+}
+
+// Value of v held by lane l^32 (one v_permlane32_swap).
+__device__ __forceinline__ float other_half(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  // lanes 0..31: r[1] holds lane l+32's value; lanes 32..63: r[0] holds lane l-32's value
+  return __builtin_bit_cast(float, ((threadIdx.x & 63) < 32) ? hi : lo);
+}
+__device__ __forceinline__ float max_halves(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
+// Sum of the two bf16 values of a packed pair, added to c (one v_dot2c_f32_bf16).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p = __builtin_bit_cast(bf16x2_t, pair);
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  return __builtin_amdgcn_fdot2_f32_bf16(p, one, c, false);
+}
+
+template <int D, int NR>
+struct WaveRows {
+  bf16x8 qop[NR][TileCfg<D>::KSTEPS];  // Qᵀ operands of the 32-row blocks
+  f32x16 acc[NR][TileCfg<D>::DVB];     // Oᵀ accumulators
+  float m[NR];                         // reference maxima (exp2 domain)
+  float lb[NR];                        // lane-partial sums of the bf16-rounded weights
+  float lf[NR];                        // lane-partial sums of the fp32 weights
+};
+
+// Sᵀ of one 32-key unit (key block kb of the tile whose K part starts at LDS address kt, plus
+// this lane's 16-byte offset): s[r] = K(kb) · Qᵀ(r).
+template <int D, int NR>
+__device__ __forceinline__ void qk_unit(const WaveRows<D, NR>& ws, uint32_t kt, int kb,
+                                        f32x16 (&s)[NR]) {
+  using C = TileCfg<D>;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) s[r] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < C::KSTEPS; ++st) {
+    const bf16x8 k = lds_read_b128_at(kt + 1024u * (kb * C::KSTEPS + st));
+#pragma unroll
+    for (int r = 0; r < NR; ++r) s[r] = mfma32(k, ws.qop[r][st], s[r]);
+  }
+}
+
+// Masks unit u: slot (r, j) holds key 32*u + 8*(j/4) + 4*(l/32) + j%4 of query row
+// qw0 + 32*r + l%32; keys past Lk or past the row's causal horizon get -inf.
+template <int NR>
+__device__ __forceinline__ void mask_unit(f32x16 (&s)[NR], int u, int qw0, int Lk, int causal,
+                                          int off, int l) {
+  const int kbase = 32 * u + 4 * (l >> 5);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int lim = causal ? min(Lk - 1, qw0 + 32 * r + (l & 31) + off) : Lk - 1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = kbase + 8 * (j >> 2) + (j & 3);
+      if (key > lim) s[r][j] = -INFINITY;
+    }
+  }
+}
+
+// One pipeline step of a wave, with an explicit issue schedule. It is written as NQ + NV MFMA
+// slots (NR MFMAs each, one per row block): the NQ slots of Sᵀ(next) = K·Qᵀ, then the NV slots
+// of Oᵀ += Vᵀ·Pᵀ(previous). Each slot is followed by a slice of the softmax of the current unit
+// (row maxima, reference moves, then groups of two weights) and by the LDS reads that feed the
+// MFMAs two slots later. Scheduling fences keep this order, so the VALU instructions issue
+// while the matrix core is busy.
+//
+//   sc: Sᵀ of the current unit (consumed);   sn: Sᵀ of the next unit (produced)
+//   pp: Pᵀ of the previous unit (consumed);  pc: Pᵀ of the current unit (produced)
+//   kt/kb: K tile address (lane offset included) and key block of the next unit
+//   vt/vkb: V tile address (lane offset included) and key block of the previous unit
+//
+// Operand slot i of lane l in P·V k-step ks covers unit key 16*ks + 8*(i/4) + 4*(l/32) + i%4,
+// which is where the Sᵀ accumulator keeps that key (slot 8*ks + i); the two transposed V
+// reads of an operand address rows 16*ks + 4*(l/32) + j and +8 (j = the lane's row inside its
+// 16-lane group).
+template <int D, int NR>
+__device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&sc)[NR],
+                                           f32x16 (&sn)[NR], const bf16x8 (&pp)[NR][2],
+                                           bf16x8 (&pc)[NR][2], uint32_t kt, int kb, uint32_t vt,
+                                           int vkb, float sl2, float (&alpha)[NR]) {
+  using C = TileCfg<D>;
+  constexpr int NQ = C::KSTEPS;
+  constexpr int NV = 2 * C::DVB;
+  constexpr int NP = NQ + NV;
+  constexpr int NITEMS = 2 + 8 * NR;  // row maxima, reference moves, weight groups
+  static_assert(NQ >= 2, "K read pipeline depth");
+
+  float mxl[NR], muse[NR], sb[NR], sf[NR];
+  uint32_t pk[NR][2][4];
+  bf16x8 kop[2], vop[3];
+
+  auto kread = [&](int st) { return lds_read_b128_at(kt + 1024u * (kb * C::KSTEPS + st)); };
+  // P·V slot v covers output column block b = v % DVB and k-step ks = v / DVB, so consecutive
+  // slots accumulate into different blocks (no back-to-back dependent MFMAs).
+  auto vread = [&](int v) {
+    const uint32_t o = vt + (32u * vkb + 16u * (v / C::DVB)) * C::VROW + 64u * (v % C::DVB);
+    return lds_read_tr_pair_at(o, o + 8u * C::VROW);
+  };
+  auto item = [&](auto IT) {
+    constexpr int it = decltype(IT)::value;
+    if constexpr (it == 0) {
+      // in-lane maxima of the 16 scores of each row block
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float mx = max3f(sc[r][0], sc[r][1], sc[r][2]);
+#pragma unroll
+        for (int j = 3; j + 1 < 16; j += 2) mx = max3f(mx, sc[r][j], sc[r][j + 1]);
+        mxl[r] = fmaxf(mx, sc[r][15]);
+      }
+    } else if constexpr (it == 1) {
+      // row maxima across the two lanes of a row; lazy move of the reference maxima
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float tmax = max_halves(mxl[r]) * sl2;
+        const bool move = tmax > ws.m[r] + kSlack;
+        const float mnew = move ? tmax : ws.m[r];
+        alpha[r] = move ? fast_exp2(ws.m[r] - mnew) : 1.0f;
+        ws.m[r] = mnew;
+        muse[r] = (mnew == -INFINITY) ? 0.f : mnew;
+        sb[r] = ws.lb[r] * alpha[r];
+        sf[r] = ws.lf[r] * alpha[r];
+      }
+    } else {
+      // weight group g: scores 8*ks + 2*i and +1 of row block r
+      constexpr int g = it - 2;
+      constexpr int r = g >> 3, ks = (g >> 2) & 1, i = g & 3;
+      const float e0 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i], sl2, -muse[r]));
+      const float e1 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i + 1], sl2, -muse[r]));
+      sf[r] += e0;
+      sf[r] += e1;
+      pk[r][ks][i] = pack_bf16x2(e0, e1);
+      sb[r] = add_bf16_pair(pk[r][ks][i], sb[r]);
+    }
+  };
+
+  kop[0] = kread(0);
+  kop[1] = kread(1);
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<0, NP>([&](auto PI) {
+    constexpr int i = decltype(PI)::value;
+    if constexpr (i < NQ) {
+      const bf16x8 k = kop[i & 1];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) sn[r] = mfma32(k, ws.qop[r][i], i == 0 ? f32x16{} : sn[r]);
+      if constexpr (i + 2 < NQ) kop[i & 1] = kread(i + 2);
+      if constexpr (i >= NQ - 2) vop[i - (NQ - 2)] = vread(i - (NQ - 2));
+    } else {
+      constexpr int v = i - NQ;
+      const bf16x8 vv = vop[v % 3];
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        ws.acc[r][v % C::DVB] = mfma32(vv, pp[r][v / C::DVB], ws.acc[r][v % C::DVB]);
+      if constexpr (v + 2 < NV) vop[(v + 2) % 3] = vread(v + 2);
+    }
+    static_for<NITEMS * i / NP, NITEMS * (i + 1) / NP>(item);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pc[r][ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[r][ks][0], pk[r][ks][1], pk[r][ks][2],
+                                                        pk[r][ks][3]));
+    ws.lb[r] = sb[r];
+    ws.lf[r] = sf[r];
+  }
+}
+
+// Pins the weights and row sums of a unit to this point of the instruction stream: without it
+// the compiler sinks their computation past the rescale branch, away from the MFMAs it is meant
+// to overlap with. Emits no instruction.
+template <int D, int NR>
+__device__ __forceinline__ void anchor_weights(const WaveRows<D, NR>& ws,
+                                               const bf16x8 (&p)[NR][2]) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(p[r][ks]));
+    asm volatile("" ::"v"(ws.lb[r]), "v"(ws.lf[r]));
+  }
+}
+
+template <int D, int NR>
+__device__ __forceinline__ void rescale(WaveRows<D, NR>& ws, const float (&alpha)[NR]) {
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) any = any || (alpha[r] != 1.0f);
+  if (__any(any)) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int b = 0; b < TileCfg<D>::DVB; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ws.acc[r][b][j] *= alpha[r];
+  }
+}
+
+template <int D, int NR>
+__device__ __forceinline__ void load_q_rows(const FwdArgs& a, WaveRows<D, NR>& ws, int b, int hq,
+                                            int qw0, int l) {
+  using C = TileCfg<D>;
+  const int h = l >> 5;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int row = qw0 + 32 * r + (l & 31);
+    if (row < a.Lq) {
+      const uint16_t* qr =
+          a.q + (int64_t)b * a.q_sb + (int64_t)row * a.q_sl + (int64_t)hq * a.q_sh;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) ws.qop[r][s] = load_bf16x8(qr + 16 * s + 8 * h);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) ws.qop[r][s] = zero_bf16x8();
+    }
+#pragma unroll
+    for (int bb = 0; bb < C::DVB; ++bb) ws.acc[r][bb] = f32x16{};
+    ws.m[r] = -INFINITY;
+    ws.lb[r] = 0.f;
+    ws.lf[r] = 0.f;
+  }
+}
+
+template <int D, int NR>
+__device__ __forceinline__ void store_rows(const FwdArgs& a, const WaveRows<D, NR>& ws, int b,
+                                           int hq, int qw0, int l) {
+  using C = TileCfg<D>;
+  const int h = l >> 5;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float tb = ws.lb[r] + other_half(ws.lb[r]);
+    const float tf = ws.lf[r] + other_half(ws.lf[r]);
+    const int row = qw0 + 32 * r + (l & 31);
+    if (row >= a.Lq) continue;
+    const float inv = tb > 0.f ? 1.0f / tb : 0.f;
+    uint16_t* orow = a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_sl + (int64_t)hq * a.o_sh;
+#pragma unroll
+    for (int bb = 0; bb < C::DVB; ++bb) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dv = 32 * bb + 8 * u + 4 * h;
+        uint2 pk;
+        pk.x = pack_bf16x2(ws.acc[r][bb][4 * u + 0] * inv, ws.acc[r][bb][4 * u + 1] * inv);
+        pk.y = pack_bf16x2(ws.acc[r][bb][4 * u + 2] * inv, ws.acc[r][bb][4 * u + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dv) = pk;
+      }
+    }
+    if (a.lse != nullptr && h == 0) {
+      a.lse[((int64_t)b * a.Hq + hq) * a.Lq + row] =
+          tf > 0.f ? ws.m[r] * kLn2 + logf(tf) : -INFINITY;
+    }
+  }
+}
+
+// Maps blockIdx.x to a logical tile id so that consecutive logical ids run on one XCD (the
+// hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+__device__ __forceinline__ int logical_block_xcd(int xcd_remap) {
+  const int bid = (int)blockIdx.x;
+  const int n = (int)gridDim.x;
+  return xcd_remap ? ((bid & 7) * (n >> 3) + (bid >> 3)) : bid;
+}
+
+// Logical order: (b, kv head) major so one XCD keeps one KV head's K/V in its L2, then query
+// tiles longest-first (causal work grows with the tile index), then the query heads of the
+// group.
+//
+// Pipeline. Keys are processed in 32-key units u (unit u = half u%2 of tile u/2). Step j issues
+// the MFMAs of Sᵀ(u = j+1) and of Oᵀ += Vᵀ(j-1)·Pᵀ(j-1), and the softmax of unit j. Score and
+// weight registers alternate between two sets by unit parity. Step 2t+1 (second half of tile
+// t) opens with the wait for tile t+1, the workgroup barrier, and the copy of tile t+2 into
+// the stage of tile t-2, whose last reader was step 2t-2.
+template <int D, int NR>
+__global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdArgs a) {
+  using C = TileCfg<D>;
+  constexpr int NW = 8 / NR;
+  constexpr int BM = 32 * NR * NW;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * C::STAGE_BYTES];
+  const uint32_t lds0 = lds_addr(smem);
+
+  const int tid = (int)threadIdx.x;
+  // wave index and everything derived from it are wave-uniform: keep them in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wu = w;
+  const int l = tid & 63;
+  int lid = logical_block_xcd(a.xcd_remap);
+  const int hg = lid % a.g;
+  lid /= a.g;
+  const int qt = a.n_qtiles - 1 - (lid % a.n_qtiles);
+  lid /= a.n_qtiles;
+  const int hkv = lid % a.Hkv;
+  const int b = lid / a.Hkv;
+  const int hq = hkv * a.g + hg;
+
+  const int q0 = qt * BM;
+  const int qw0 = q0 + 32 * NR * w;           // first row of this wave
+  const int qlast = min(q0 + BM, a.Lq) - 1;   // last row of the workgroup
+  int klimit = a.Lk;                          // keys [0, klimit) can be visible
+  if (a.causal) klimit = max(0, min(a.Lk, qlast + a.off + 1));
+  const int ntiles = __builtin_amdgcn_readfirstlane((klimit + BN - 1) / BN);
+
+  WaveRows<D, NR> ws;
+  load_q_rows<D, NR>(a, ws, b, hq, qw0, l);
+
+  if (ntiles == 0) {  // no row of the workgroup sees any key (causal with Lq > Lk)
+    store_rows<D, NR>(a, ws, b, hq, qw0, l);
+    return;
+  }
+
+  TileByteOffsets<D, NW> off;
+  off.init(a, w, l);
+  const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+  // Units [0, nfull) are complete and visible to every row of this wave; later units are
+  // masked (the causal diagonal, the ragged end, and the units past this wave's horizon that
+  // the workgroup still streams for its other waves).
+  int nfull = a.Lk / 32;
+  if (a.causal) nfull = min(nfull, max(0, qw0 + a.off + 1) / 32);
+  nfull = __builtin_amdgcn_readfirstlane(nfull);
+
+  auto stage_addr = [&](int t) -> uint32_t { return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES; };
+  // Copies tile t (t < ntiles, issued in increasing order) into its stage. A ragged last tile
+  // re-reads its last key row in the missing rows, so every copy stays inside the sequence; as
+  // it is the last tile copied, its clamped offsets replace the full-tile ones in place.
+  auto issue = [&](int t) {
+    const int base = t * BN;
+    const uint16_t* kt = kb + (int64_t)base * a.k_sl;
+    const uint16_t* vt = vb + (int64_t)base * a.v_sl;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(stage_addr(t));
+    if (base + BN > a.Lk) off.init(a, w, l, a.Lk - 1 - base);
+    issue_tile_sbase<D, NW>(st, kt, vt, off, wu);
+  };
+
+  f32x16 sc[2][NR];     // Sᵀ register sets (unit parity, row block)
+  bf16x8 pw[2][NR][2];  // Pᵀ operand sets (unit parity, row block, k-step)
+  const uint32_t kofs = (uint32_t)l * 16u;
+  // V operand: group G = l/16, row 4*(G/2) + (l%16)/4, column 16*(G%2) + 4*(l%4)
+  const int G = l >> 4;
+  const uint32_t vofs = C::KT_BYTES + (uint32_t)(4 * (G >> 1) + ((l & 15) >> 2)) * C::VROW +
+                        (uint32_t)(16 * (G & 1) + 4 * (l & 3)) * 2u;
+
+  // Prologue: tile 0 copied and waited for, tile 1 in flight; the V part of stage 3 (read by
+  // the P·V of "unit -1", whose weights are zero) is cleared so that it holds finite values.
+  issue(0);
+  {
+    char* v3 = smem + 3 * C::STAGE_BYTES + C::KT_BYTES;
+    for (int i = tid; i < C::VT_BYTES / 16; i += NW * 64)
+      *reinterpret_cast<uint4*>(v3 + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pw[1][r][ks] = zero_bf16x8();
+  wait_dma_all();
+  __syncthreads();
+  if (ntiles > 1) issue(1);
+  qk_unit<D, NR>(ws, stage_addr(0) + kofs, 0, sc[0]);
+
+  // Step j = 2t + H.
+  auto step = [&](auto HI, int t) {
+    constexpr int H = decltype(HI)::value;
+    const int j = 2 * t + H;
+    if constexpr (H == 1) {
+      wait_dma_all();  // tile t+1 landed (this wave's copies) ...
+      barrier_lds();   // ... for every wave, and every wave is done with step 2t
+      if (t + 2 < ntiles) issue(t + 2);
+    }
+    float alpha[NR];
+    if (j >= nfull) mask_unit<NR>(sc[H], j, qw0, a.Lk, a.causal, a.off, l);
+    // Sᵀ(j+1): H = 0 -> second half of tile t; H = 1 -> first half of tile t+1.
+    // P·V of unit j-1: H = 0 -> second half of tile t-1; H = 1 -> first half of tile t.
+    fused_step<D, NR>(ws, sc[H], sc[1 - H], pw[1 - H], pw[H], stage_addr(t + H) + kofs, 1 - H,
+                      stage_addr(t + 3 + H) + vofs, 1 - H, a.sl2, alpha);
+    anchor_weights<D, NR>(ws, pw[H]);
+    rescale<D, NR>(ws, alpha);
+  };
+
+  // 2*ntiles + 1 steps; the last one only finishes the P·V of the last unit.
+  const int J = 2 * ntiles + 1;
+  for (int t = 0;; ++t) {
+    step(icn<0>{}, t);
+    if (2 * t + 1 >= J) break;
+    step(icn<1>{}, t);
+    if (2 * t + 2 >= J) break;
+  }
+  wait_dma_all();
+  store_rows<D, NR>(a, ws, b, hq, qw0, l);
+}
+
+template <int D>
+hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NW = 8 / kDenseNR;
+  const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
+  FwdArgs aa = a;
+  aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+                     stream, aa);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_dense_t<128>(a, stream);
+  return launch_dense_t<64>(a, stream);
+}
+
+}  // namespace attn

@@ -40,135 +40,15 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile_io.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int BN = 64;                 // keys per tile
 // Log2 headroom before the reference maximum moves. Zero keeps the eager running maximum: the
 // largest weight of every row is then exactly 1.0, which bf16 represents exactly; a stale
 // reference would let that weight pick up a bf16 rounding error of up to 2^-9 relative.
 constexpr float kRescaleSlack = 0.0f;
-
-template <int N>
-using ic = std::integral_constant<int, N>;
-
-template <int D>
-struct TileCfg {
-  static constexpr int CPR = D / 8;                   // 16-byte chunks of data per row
-  static constexpr int KSTEPS = D / 16;               // 32x32x16 MFMA steps over the head dim
-  static constexpr int KSLABS = 2 * KSTEPS;           // K tile: 1 KiB operand slabs
-  static constexpr int VROW = 2 * D + 64;             // padded V row (bytes)
-  static constexpr int VSPR = VROW / 16;              // 16-byte slots per V row
-  static constexpr int KT_BYTES = KSLABS * 1024;
-  static constexpr int VT_BYTES = BN * VROW;
-  static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
-  static constexpr int KINSTR = KSLABS;               // 1 KiB copy instructions per K tile
-  static constexpr int VINSTR = VT_BYTES / 1024;
-  static constexpr int DVB = D / 32;                  // 32-wide output column blocks
-  static_assert(VT_BYTES % 1024 == 0, "whole KiB tiles");
-};
-
-// K slab (kb, s) holds, for lane l, the 16 bytes of key row 32*kb + l%32 at head-dim chunk
-// 2s + l/32: exactly the A operand of k-step s for key block kb, read linearly.
-template <int D>
-__device__ __forceinline__ void kslab_rc(int i, int l, uint32_t& r, uint32_t& c) {
-  r = 32u * (uint32_t)(i / TileCfg<D>::KSTEPS) + (uint32_t)(l & 31);
-  c = 2u * (uint32_t)(i % TileCfg<D>::KSTEPS) + (uint32_t)(l >> 5);
-}
-
-// Row r and chunk c that copy slot `slot` of a padded tile holds (padding slots duplicate
-// chunk 0 of their row).
-template <int SPR, int CPR>
-__device__ __forceinline__ void slot_rc(uint32_t slot, uint32_t& r, uint32_t& c) {
-  r = slot / SPR;
-  const uint32_t cs = slot % SPR;
-  c = cs < (uint32_t)CPR ? cs : 0u;
-}
-
-// Copy instruction i (K instructions first, then V) of one tile. key_of(r) must return a valid
-// key row, so every load is in bounds.
-template <int D, class KeyOf>
-__device__ __forceinline__ void copy_instr_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
-                                                const uint16_t* vbase, KeyOf key_of, int i, int l) {
-  using C = TileCfg<D>;
-  uint32_t r, c;
-  if (i < C::KINSTR) {
-    kslab_rc<D>(i, l, r, c);
-    dma16(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + i * 1024);
-  } else {
-    const int iv = i - C::KINSTR;
-    slot_rc<C::VSPR, C::CPR>((uint32_t)iv * 64u + (uint32_t)l, r, c);
-    dma16(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  if constexpr (N == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    // gfx9 encoding: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt at
-    // their maxima (no wait on them)
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  }
-}
-// Workgroup barrier without a memory fence (the copies it orders are waited for explicitly).
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
-
-// Per-lane element offsets (relative to a tile's first key row) of this wave's copy
-// instructions, for tiles whose 64 rows are consecutive keys all inside the sequence.
-template <int D, int NW>
-struct TileOffsets {
-  static constexpr int NI = (TileCfg<D>::KINSTR + TileCfg<D>::VINSTR + NW - 1) / NW;
-  uint32_t off[NI];
-  __device__ __forceinline__ void init(const FwdArgs& a, int w, int l) {
-    using C = TileCfg<D>;
-#pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      const int i = w + NW * ii;
-      uint32_t r, c;
-      if (i < C::KINSTR) {
-        kslab_rc<D>(i, l, r, c);
-        off[ii] = r * (uint32_t)a.k_sl + c * 8u;
-      } else {
-        slot_rc<C::VSPR, C::CPR>((uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l, r, c);
-        off[ii] = r * (uint32_t)a.v_sl + c * 8u;
-      }
-    }
-  }
-};
-
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile_fast(char* st, const uint16_t* ktile,
-                                                const uint16_t* vtile, const TileOffsets<D, NW>& o,
-                                                int w) {
-  using C = TileCfg<D>;
-  // the copy instruction index, the source tile and the LDS destination are wave-uniform
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-#pragma unroll
-  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
-    const int i = wu + NW * ii;
-    if (i < C::KINSTR + C::VINSTR) {
-      const bool is_k = i < C::KINSTR;
-      const uint16_t* src = is_k ? ktile : vtile;
-      const int dst = is_k ? i * 1024 : C::KT_BYTES + (i - C::KINSTR) * 1024;
-      dma16(src + o.off[ii], st + dst);
-    }
-  }
-}
-
-template <int D, int NW, class KeyOf>
-__device__ __forceinline__ void issue_tile_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
-                                                const uint16_t* vbase, KeyOf key_of, int w, int l) {
-  using C = TileCfg<D>;
-#pragma unroll
-  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
-    const int i = w + NW * ii;
-    if (i < C::KINSTR + C::VINSTR) copy_instr_slow<D>(a, st, kbase, vbase, key_of, i, l);
-  }
-}
 
 template <int D>
 struct WaveState {
@@ -324,90 +204,6 @@ __device__ __forceinline__ int logical_block(int xcd_remap) {
   const int bid = (int)blockIdx.x;
   const int n = (int)gridDim.x;
   return xcd_remap ? ((bid & 7) * (n >> 3) + (bid >> 3)) : bid;
-}
-
-// ------------------------------------------------------------------------------------------
-// Dense forward. Logical order: (b, kv head) major so one XCD keeps one KV head's K/V in its
-// L2, then query tiles longest-first (causal work grows with the tile index), then the g
-// query heads of the group.
-// ------------------------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_dense_kernel(const FwdArgs a) {
-  using C = TileCfg<D>;
-  constexpr int BM = 32 * NW;
-  // One array per ring stage: with compile-time stage indices the compiler can tell the stage
-  // being read from the stage still being filled and does not wait for that copy.
-  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
-
-  const int tid = (int)threadIdx.x;
-  const int w = tid >> 6;
-  const int l = tid & 63;
-  int lid = logical_block(a.xcd_remap);
-  const int hg = lid % a.g;
-  lid /= a.g;
-  const int qt = a.n_qtiles - 1 - (lid % a.n_qtiles);
-  lid /= a.n_qtiles;
-  const int hkv = lid % a.Hkv;
-  const int b = lid / a.Hkv;
-  const int hq = hkv * a.g + hg;
-
-  const int q0 = qt * BM;
-  const int qw0 = q0 + 32 * w;                // first row of this wave
-  const int row = qw0 + (l & 31);             // this lane's query row
-  const int qlast = min(q0 + BM, a.Lq) - 1;   // last row of the workgroup
-  const int qwlast = min(qw0 + 31, a.Lq - 1); // last row of the wave
-  int klimit = a.Lk;                          // keys [0, klimit) can be visible
-  if (a.causal) klimit = min(a.Lk, qlast + a.off + 1);
-  const int ntiles = klimit > 0 ? (klimit + BN - 1) / BN : 0;
-
-  WaveState<D> ws;
-  load_q<D>(a, ws, b, hq, row, l);
-  TileOffsets<D, NW> off;
-  off.init(a, w, l);
-
-  const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-  const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
-  const int lkm1 = a.Lk - 1;
-
-  // Tiles [0, nfull) are complete and fully visible to every row of the workgroup; the rest
-  // (causal diagonal, ragged end) take the masked path.
-  int nfull = a.Lk / BN;
-  if (a.causal) nfull = min(nfull, max(0, (q0 + a.off + 1) / BN));
-  nfull = min(nfull, ntiles);
-  const int64_t kstep = (int64_t)BN * a.k_sl, vstep = (int64_t)BN * a.v_sl;
-  const uint16_t* knext = kb;  // first key row of the next tile to copy
-  const uint16_t* vnext = vb;
-
-  auto issue = [&](auto S, int t) {
-    char* st = decltype(S)::value == 0 ? st0 : st1;
-    const int base = t * BN;
-    if (base + BN <= a.Lk) {
-      issue_tile_fast<D, NW>(st, knext, vnext, off, w);
-    } else {
-      issue_tile_slow<D, NW>(a, st, kb, vb, [&](int r) { return min(base + r, lkm1); }, w, l);
-    }
-    knext += kstep;
-    vnext += vstep;
-  };
-  auto step = [&](auto S, int t) {
-    constexpr int s = decltype(S)::value;
-    wait_dma_all();
-    __syncthreads();
-    if (t + 1 < ntiles) issue(ic<1 - s>{}, t + 1);
-    const int base = t * BN;
-    // wave-uniform: skip tiles entirely beyond this wave's causal horizon
-    if (a.causal && base > qwlast + a.off) return;
-    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, t >= nfull,
-                 [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
-  };
-
-  if (ntiles > 0) issue(ic<0>{}, 0);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(ic<0>{}, t);
-    if (t + 1 < ntiles) step(ic<1>{}, t + 1);
-  }
-  store_out<D>(a, ws, b, hq, row, l);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -568,15 +364,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
 }
 
 template <int D, int NW>
-hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
-  const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
-  FwdArgs aa = a;
-  aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_dense_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, stream, aa);
-  return hipGetLastError();
-}
-
-template <int D, int NW>
 hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
   FwdArgs aa = a;
@@ -586,11 +373,6 @@ hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_dense_t<128, 4>(a, stream);
-  return launch_dense_t<64, 4>(a, stream);
-}
 
 hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream) {
   if (d == 128) return launch_sparse_t<128, 2>(a, stream);

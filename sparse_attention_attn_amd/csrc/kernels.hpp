@@ -65,7 +65,7 @@ hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t strea
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);
 
 // Query rows per workgroup of the dense forward kernel.
-constexpr int kDenseBlockM = 128;
+constexpr int kDenseBlockM = 256;
 // Query rows per workgroup of the block-sparse kernel (one 64-row query block).
 constexpr int kSparseBlockM = 64;
 // Query columns ((head, position) pairs of one KV head) per split-KV workgroup.

@@ -1,0 +1,204 @@
+// tile_io.hpp — K/V tile staging for the prefill kernels: LDS tile geometry and the
+// asynchronous global->LDS copy of one 64-key tile, shared by the dense and block-sparse
+// forward kernels.
+//
+// LDS layout of one tile (keys 0..63 of the tile):
+//  * K: MFMA-operand order. Slab (kb, s) (1 KiB) holds, for lane l, the 16 bytes of key row
+//    32*kb + l%32 at head-dim chunk 2s + l/32, which is exactly the A operand of 32x32x16 k-step
+//    s for key block kb. Every K-operand read is then a linear ds_read_b128, the LDS read
+//    pattern that reaches full bandwidth.
+//  * V: row-major, rows padded to 2D+64 bytes, which keeps the transposed V read (8 rows x 64
+//    bytes per instruction) conflict-free. Padding slots receive a duplicate of the row's
+//    first chunk and are never read.
+// Every copy instruction moves 1 KiB (64 lanes x 16 bytes) and lands contiguously in LDS.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int BN = 64;                 // keys per tile
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+template <int D>
+struct TileCfg {
+  static constexpr int CPR = D / 8;                   // 16-byte chunks of data per row
+  static constexpr int KSTEPS = D / 16;               // 32x32x16 MFMA steps over the head dim
+  static constexpr int KSLABS = 2 * KSTEPS;           // K tile: 1 KiB operand slabs
+  static constexpr int VROW = 2 * D + 64;             // padded V row (bytes)
+  static constexpr int VSPR = VROW / 16;              // 16-byte slots per V row
+  static constexpr int KT_BYTES = KSLABS * 1024;
+  static constexpr int VT_BYTES = BN * VROW;
+  static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+  static constexpr int KINSTR = KSLABS;               // 1 KiB copy instructions per K tile
+  static constexpr int VINSTR = VT_BYTES / 1024;
+  static constexpr int DVB = D / 32;                  // 32-wide output column blocks
+  static_assert(VT_BYTES % 1024 == 0, "whole KiB tiles");
+};
+
+// K slab (kb, s) holds, for lane l, the 16 bytes of key row 32*kb + l%32 at head-dim chunk
+// 2s + l/32: exactly the A operand of k-step s for key block kb, read linearly.
+template <int D>
+__device__ __forceinline__ void kslab_rc(int i, int l, uint32_t& r, uint32_t& c) {
+  r = 32u * (uint32_t)(i / TileCfg<D>::KSTEPS) + (uint32_t)(l & 31);
+  c = 2u * (uint32_t)(i % TileCfg<D>::KSTEPS) + (uint32_t)(l >> 5);
+}
+
+// Row r and chunk c that copy slot `slot` of a padded tile holds (padding slots duplicate
+// chunk 0 of their row).
+template <int SPR, int CPR>
+__device__ __forceinline__ void slot_rc(uint32_t slot, uint32_t& r, uint32_t& c) {
+  r = slot / SPR;
+  const uint32_t cs = slot % SPR;
+  c = cs < (uint32_t)CPR ? cs : 0u;
+}
+
+// Copy instruction i (K instructions first, then V) of one tile. key_of(r) must return a valid
+// key row, so every load is in bounds.
+template <int D, class KeyOf>
+__device__ __forceinline__ void copy_instr_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
+                                                const uint16_t* vbase, KeyOf key_of, int i, int l) {
+  using C = TileCfg<D>;
+  uint32_t r, c;
+  if (i < C::KINSTR) {
+    kslab_rc<D>(i, l, r, c);
+    dma16(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + i * 1024);
+  } else {
+    const int iv = i - C::KINSTR;
+    slot_rc<C::VSPR, C::CPR>((uint32_t)iv * 64u + (uint32_t)l, r, c);
+    dma16(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    // gfx9 encoding: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt at
+    // their maxima (no wait on them)
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+}
+// Workgroup barrier without a memory fence (the copies it orders are waited for explicitly).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+// Per-lane element offsets (relative to a tile's first key row) of this wave's copy
+// instructions, for tiles whose 64 rows are consecutive keys all inside the sequence.
+template <int D, int NW>
+struct TileOffsets {
+  static constexpr int NI = (TileCfg<D>::KINSTR + TileCfg<D>::VINSTR + NW - 1) / NW;
+  uint32_t off[NI];
+  // maxrow < 63 describes a ragged last tile: rows past maxrow re-read row maxrow, so every
+  // copy stays inside the sequence.
+  __device__ __forceinline__ void init(const FwdArgs& a, int w, int l, int maxrow = BN - 1) {
+    using C = TileCfg<D>;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int i = w + NW * ii;
+      uint32_t r, c;
+      if (i < C::KINSTR) {
+        kslab_rc<D>(i, l, r, c);
+        r = min(r, (uint32_t)maxrow);
+        off[ii] = r * (uint32_t)a.k_sl + c * 8u;
+      } else {
+        slot_rc<C::VSPR, C::CPR>((uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l, r, c);
+        r = min(r, (uint32_t)maxrow);
+        off[ii] = r * (uint32_t)a.v_sl + c * 8u;
+      }
+    }
+  }
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_fast(char* st, const uint16_t* ktile,
+                                                const uint16_t* vtile, const TileOffsets<D, NW>& o,
+                                                int w) {
+  using C = TileCfg<D>;
+  // the copy instruction index, the source tile and the LDS destination are wave-uniform
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
+    const int i = wu + NW * ii;
+    if (i < C::KINSTR + C::VINSTR) {
+      const bool is_k = i < C::KINSTR;
+      const uint16_t* src = is_k ? ktile : vtile;
+      const int dst = is_k ? i * 1024 : C::KT_BYTES + (i - C::KINSTR) * 1024;
+      dma16(src + o.off[ii], st + dst);
+    }
+  }
+}
+
+// Scalar-base tile copy. Wave w of NW issues the K copy instructions w, w+NW, ... and the V
+// copy instructions w, w+NW, ... (KINSTR and VINSTR are multiples of NW), so which tensor an
+// instruction reads is fixed at compile time. `ko` / `vo` hold the lane's byte offsets
+// relative to the tile's first key row; maxrow < 63 describes a ragged last tile (rows past
+// maxrow re-read row maxrow, so every copy stays inside the sequence).
+template <int D, int NW>
+struct TileByteOffsets {
+  static constexpr int KI = (TileCfg<D>::KINSTR + NW - 1) / NW;
+  static constexpr int VI = (TileCfg<D>::VINSTR + NW - 1) / NW;
+  uint32_t ko[KI];
+  uint32_t vo[VI];
+  __device__ __forceinline__ void init(const FwdArgs& a, int w, int l, int maxrow = BN - 1) {
+    using C = TileCfg<D>;
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+      uint32_t r, c;
+      kslab_rc<D>(min(w + NW * k, C::KINSTR - 1), l, r, c);
+      r = min(r, (uint32_t)maxrow);
+      ko[k] = (r * (uint32_t)a.k_sl + c * 8u) * 2u;
+    }
+#pragma unroll
+    for (int v = 0; v < VI; ++v) {
+      uint32_t r, c;
+      slot_rc<C::VSPR, C::CPR>((uint32_t)min(w + NW * v, C::VINSTR - 1) * 64u + (uint32_t)l, r, c);
+      r = min(r, (uint32_t)maxrow);
+      vo[v] = (r * (uint32_t)a.v_sl + c * 8u) * 2u;
+    }
+  }
+};
+
+// Copies one tile (K rows from ktile, V rows from vtile, both wave-uniform) into the stage at
+// LDS address `stage` (wave-uniform) with the scalar-base copy instruction. Wave wu issues the
+// K instructions wu, wu+NW, ... and the V instructions wu, wu+NW, ... that exist.
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile_sbase(uint32_t stage, const uint16_t* ktile,
+                                                 const uint16_t* vtile,
+                                                 const TileByteOffsets<D, NW>& o, int wu) {
+  using C = TileCfg<D>;
+#pragma unroll
+  for (int k = 0; k < TileByteOffsets<D, NW>::KI; ++k) {
+    const int i = wu + NW * k;
+    if ((C::KINSTR % NW) == 0 || i < C::KINSTR)
+      dma16_sbase(ktile, o.ko[k], stage + (uint32_t)i * 1024u);
+  }
+#pragma unroll
+  for (int v = 0; v < TileByteOffsets<D, NW>::VI; ++v) {
+    const int i = wu + NW * v;
+    if ((C::VINSTR % NW) == 0 || i < C::VINSTR)
+      dma16_sbase(vtile, o.vo[v], stage + C::KT_BYTES + (uint32_t)i * 1024u);
+  }
+}
+
+template <int D, int NW, class KeyOf>
+__device__ __forceinline__ void issue_tile_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
+                                                const uint16_t* vbase, KeyOf key_of, int w, int l) {
+  using C = TileCfg<D>;
+#pragma unroll
+  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
+    const int i = w + NW * ii;
+    if (i < C::KINSTR + C::VINSTR) copy_instr_slow<D>(a, st, kbase, vbase, key_of, i, l);
+  }
+}
+
+
+}  // namespace
+}  // namespace attn

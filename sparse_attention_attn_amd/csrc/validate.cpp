@@ -23,6 +23,10 @@ int check_tensor(const char* fn, const char* name, const attn_tensor_t& t) {
   if ((t.stride_b % 8) != 0 || (t.stride_l % 8) != 0 || (t.stride_h % 8) != 0)
     return fail(ATTN_ERR_INVALID_ARG, fn,
                 std::string(name) + " strides must be multiples of 8 elements (16 bytes)");
+  // In-tile offsets (row * stride_l + column, up to 64 rows) are kept in 32-bit registers.
+  if (t.stride_l > kMaxStrideL)
+    return fail(ATTN_ERR_UNSUPPORTED, fn,
+                std::string(name) + " sequence stride exceeds 2^24 elements");
   return ATTN_OK;
 }
 

@@ -44,6 +44,9 @@ int check_blocksparse_lists(const char* fn, const int32_t* blk_ptr, const int32_
                             const int32_t* col_ptr, const int32_t* col_idx, int B, int Hq, int Lq,
                             int Lk, int block_m, int block_n);
 
+// Largest sequence stride (elements) of Q/K/V: in-tile offsets are 32-bit.
+constexpr int64_t kMaxStrideL = int64_t(1) << 24;
+
 // Largest key length the block-sparse kernel's listed-block bitmap covers.
 constexpr int kSparseMaxLk = 1 << 20;
 

@@ -71,6 +71,7 @@ def _fwd(q=None, k=None, v=None, o=None, lse=None, B=1, Hq=4, Hkv=2, Lq=64, Lk=6
     (dict(k=_t(ptr=FAKE + 2)), S.ATTN_ERR_INVALID_ARG, "aligned"),
     (dict(v=_t(sl=4 * 128 + 4)), S.ATTN_ERR_INVALID_ARG, "multiples of 8"),
     (dict(o=_t(sh=-128)), S.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(k=_t(sl=(1 << 24) + 8)), S.ATTN_ERR_UNSUPPORTED, "sequence stride"),
     (dict(lse=ctypes.c_void_p(FAKE + 2)), S.ATTN_ERR_INVALID_ARG, "lse"),
 ])
 def test_attn_fwd_validation(kw, code, frag):
