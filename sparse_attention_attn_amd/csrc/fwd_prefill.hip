@@ -198,12 +198,17 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, const WaveState<D>& 
   }
 }
 
-// Maps blockIdx.x to a logical tile id so that consecutive logical ids run on one XCD (the
-// hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+// Maps blockIdx.x to a logical work id. The hardware deals workgroups round-robin over the 8
+// XCDs (each with its own L2) in blockIdx order. Logical ids are cut into chunks of 32 (8 query
+// blocks x 4 query heads of one KV head) and chunk c runs on XCD c % 8: the query blocks that
+// share most of their local band of key blocks meet in one L2, while all XCDs work on
+// neighbouring chunks, i.e. on the same KV head, whose K/V then fits the device-wide cache.
 __device__ __forceinline__ int logical_block(int xcd_remap) {
   const int bid = (int)blockIdx.x;
-  const int n = (int)gridDim.x;
-  return xcd_remap ? ((bid & 7) * (n >> 3) + (bid >> 3)) : bid;
+  if (!xcd_remap) return bid;
+  const int x = bid & 7;
+  const int j = bid >> 3;
+  return 32 * x + 256 * (j >> 5) + (j & 31);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -252,13 +257,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
   const int nb = a.blk_ptr[lrow + 1] - bstart;
   const int nwords = (a.nkb + 31) >> 5;
 
+  // The block list is also staged in LDS (as 16-bit ids, in the column buffer that phase 2
+  // reuses later) when it fits, so the tile loop reads no global memory: a global load there
+  // would be waited for with a vmcnt wait that also drains the tile copies in flight.
+  short* blist = reinterpret_cast<short*>(kept);
+  constexpr int kListCap = 2 * kSeg;
+  const bool list_in_lds = nb <= kListCap;
   for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
   __syncthreads();
   for (int i = tid; i < nb; i += NT) {
     const int kbk = a.blk_idx[bstart + i];
-    if (kbk >= 0 && kbk < a.nkb) atomicOr(&bitmap[kbk >> 5], 1u << (kbk & 31));
+    const bool valid = kbk >= 0 && kbk < a.nkb;
+    if (valid) atomicOr(&bitmap[kbk >> 5], 1u << (kbk & 31));
+    if (i < kListCap) blist[i] = (short)(valid ? kbk : -1);
   }
-  // (the barrier at the top of the tile loop orders these writes before any read)
+  __syncthreads();
 
   WaveState<D> ws;
   load_q<D>(a, ws, b, hq, row, l);
@@ -269,8 +282,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
 
   // ---- phase 1: listed key blocks
   auto blk_base = [&](int i) -> int {
+    if (list_in_lds) {
+      const int kbk = blist[i];
+      return kbk >= 0 ? kbk * BN : -1;  // -1: invalid id, fully masked
+    }
     const int kbk = a.blk_idx[bstart + i];
-    return (kbk >= 0 && kbk < a.nkb) ? kbk * BN : -1;  // -1: invalid id, fully masked
+    return (kbk >= 0 && kbk < a.nkb) ? kbk * BN : -1;
   };
   auto issue_blk = [&](auto S, int i) {
     char* st = decltype(S)::value == 0 ? st0 : st1;
@@ -367,7 +384,7 @@ template <int D, int NW>
 hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
   FwdArgs aa = a;
-  aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+  aa.xcd_remap = (nwg % 256 == 0) ? 1 : 0;
   hipLaunchKernelGGL((fwd_sparse_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, stream, aa);
   return hipGetLastError();
 }

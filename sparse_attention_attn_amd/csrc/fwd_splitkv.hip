@@ -66,31 +66,37 @@ using ic = std::integral_constant<int, N>;
 template <int DQK, int DV, int BNK, int NST>
 __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   using C = SplitCfg<DQK, DV, BNK, NST>;
-  static_assert(NST >= 2 && NST <= 4, "2..4 stages");
+  static_assert(NST >= 2 && NST <= 6, "2..6 stages");
   // One array per ring stage: with the stage fixed at compile time the compiler can tell the
   // stage being read from the stages still being filled, and does not wait for those copies.
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[NST > 2 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NST > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[NST > 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[NST > 5 ? C::STAGE : 16];
   auto stage = [&](auto S) -> char* {
     constexpr int s = decltype(S)::value;
     if constexpr (s == 0) return st0;
     else if constexpr (s == 1) return st1;
     else if constexpr (s == 2) return st2;
-    else return st3;
+    else if constexpr (s == 3) return st3;
+    else if constexpr (s == 4) return st4;
+    else return st5;
   };
 
   const int tid = (int)threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l = tid & 63;
+  // Block order: KV head fastest, so the workgroups running together read the same key rows
+  // of a [B, L, H, D] cache for all heads (one contiguous stretch of memory per key range).
   int lid = (int)blockIdx.x;
+  const int hkv = lid % a.Hkv;
+  lid /= a.Hkv;
   const int sp = lid % a.num_splits;
   lid /= a.num_splits;
   const int cb = lid % a.ncolblk;
-  lid /= a.ncolblk;
-  const int hkv = lid % a.Hkv;
-  const int b = lid / a.Hkv;
+  const int b = lid / a.ncolblk;
 
   const int ncols = a.g * a.Lq;
   const int col = cb * 16 + (l & 15);
@@ -105,7 +111,10 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   const int first_pos = (cb * 16) / a.g;
   const int last_pos = last_col / a.g;
   if (a.causal) kend = min(kend, last_pos + a.off + 1);
-  const int ntiles = kend > kstart ? (kend - kstart + BNK - 1) / BNK : 0;
+  // split bounds are uniform over the workgroup: keep them in scalar registers so the ring's
+  // branches stay scalar
+  kend = __builtin_amdgcn_readfirstlane(kend);
+  const int ntiles = __builtin_amdgcn_readfirstlane(kend > kstart ? (kend - kstart + BNK - 1) / BNK : 0);
 
   // Qᵀ operand: lane l holds column l%16, head-dim elements 32*s + 8*(l/16) .. +7
   bf16x8 qop[C::QSTEPS];
@@ -114,35 +123,39 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
 #pragma unroll
     for (int s = 0; s < C::QSTEPS; ++s)
       qop[s] = col_ok ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
+    // Use the loaded operands here, before the copy ring starts: the compiler then waits for
+    // these loads once, instead of at their first use inside the loop, where its wait would
+    // also drain the tile copies in flight.
+#pragma unroll
+    for (int s = 0; s < C::QSTEPS; ++s) asm volatile("" ::"v"(qop[s]));
   }
 
   const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
   const int kmax = kend - 1;
 
-  // Per-lane source offsets (elements, relative to the tile's first key row) of this wave's
-  // copy instructions; instruction ii of wave w is tile copy w + 4*ii.
+  // Per-lane source byte offsets (relative to the tile's first key row) of this wave's copy
+  // instructions; instruction ii of wave w is tile copy w + 4*ii. `maxrow` < BNK-1 clamps the
+  // rows of the last tile of a split to its last key (those rows are masked later).
+  auto lane_offset = [&](int i, int maxrow) -> uint32_t {
+    const bool is_k = C::MLA || i < C::KINSTR;
+    const int li = is_k ? i : i - C::KINSTR;
+    const uint32_t slot = (uint32_t)li * 64u + (uint32_t)l;
+    const uint32_t cpr = is_k ? DQK / 8 : DV / 8;
+    const uint32_t r = slot / cpr;
+    const uint32_t c = (slot % cpr) ^ (is_k ? Swz<DQK>::f(r) : Swz<(C::MLA ? DQK : DV)>::f(r));
+    const uint32_t rc = min(r, (uint32_t)maxrow);
+    return (rc * (uint32_t)(is_k ? a.k_sl : a.v_sl) + c * 8u) * 2u;
+  };
   uint32_t src_off[C::IPW];
 #pragma unroll
-  for (int ii = 0; ii < C::IPW; ++ii) {
-    const int i = w + 4 * ii;
-    if (C::MLA || i < C::KINSTR) {
-      const uint32_t slot = (uint32_t)i * 64u + (uint32_t)l;
-      const uint32_t r = slot / (DQK / 8);
-      const uint32_t c = (slot % (DQK / 8)) ^ Swz<DQK>::f(r);
-      src_off[ii] = r * (uint32_t)a.k_sl + c * 8u;
-    } else {
-      if constexpr (!C::MLA) {
-        const uint32_t slot = (uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l;
-        const uint32_t r = slot / (DV / 8);
-        const uint32_t c = (slot % (DV / 8)) ^ Swz<DV>::f(r);
-        src_off[ii] = r * (uint32_t)a.v_sl + c * 8u;
-      }
-    }
-  }
+  for (int ii = 0; ii < C::IPW; ++ii) src_off[ii] = lane_offset(w + 4 * ii, BNK - 1);
 
+  // The copies are issued with the scalar-base instruction, which the compiler does not track:
+  // it adds no waits of its own for them, and the ring below orders them with counted vmcnt
+  // waits and barriers.
   auto issue = [&](auto S, int t) {
-    char* st = stage(S);
+    const uint32_t st = lds_addr(stage(S));
     const int base = kstart + t * BNK;
     const bool tail = base + BNK - 1 > kmax;
     const uint16_t* kt = kb + (int64_t)base * a.k_sl;
@@ -152,18 +165,9 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
       const int i = w + 4 * ii;
       const bool is_k = C::MLA || i < C::KINSTR;
       const int li = is_k ? i : i - C::KINSTR;
-      char* dst = st + (is_k ? 0 : C::KT_BYTES) + li * 1024;
-      if (!tail) {
-        dma16((is_k ? kt : vt) + src_off[ii], dst);
-      } else {  // last tile of the split: clamp rows past the end (masked later)
-        const uint32_t slot = (uint32_t)li * 64u + (uint32_t)l;
-        const int cpr = is_k ? DQK / 8 : DV / 8;
-        const uint32_t r = slot / cpr;
-        const uint32_t c = (slot % cpr) ^ (is_k ? Swz<DQK>::f(r) : Swz<(C::MLA ? DQK : DV)>::f(r));
-        const int key = min(base + (int)r, kmax);
-        const uint16_t* src = is_k ? kb + (int64_t)key * a.k_sl : vb + (int64_t)key * a.v_sl;
-        dma16(src + c * 8, dst);
-      }
+      const uint32_t dst = st + (is_k ? 0u : (uint32_t)C::KT_BYTES) + (uint32_t)li * 1024u;
+      const uint32_t off = tail ? lane_offset(i, kmax - base) : src_off[ii];
+      dma16_sbase(is_k ? (const void*)kt : (const void*)vt, off, dst);
     }
   };
 
@@ -274,11 +278,15 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   if (0 < ntiles) issue(ic<0>{}, 0);
   if (NST > 2 && 1 < ntiles) issue(ic<1>{}, 1);
   if (NST > 3 && 2 < ntiles) issue(ic<2 % NST>{}, 2);
+  if (NST > 4 && 3 < ntiles) issue(ic<3 % NST>{}, 3);
+  if (NST > 5 && 4 < ntiles) issue(ic<4 % NST>{}, 4);
   for (int t = 0; t < ntiles; t += NST) {
     step(ic<0>{}, t);
     if (t + 1 < ntiles) step(ic<1>{}, t + 1);
     if constexpr (NST > 2) { if (t + 2 < ntiles) step(ic<2 % NST>{}, t + 2); }
     if constexpr (NST > 3) { if (t + 3 < ntiles) step(ic<3 % NST>{}, t + 3); }
+    if constexpr (NST > 4) { if (t + 4 < ntiles) step(ic<4 % NST>{}, t + 4); }
+    if constexpr (NST > 5) { if (t + 5 < ntiles) step(ic<5 % NST>{}, t + 5); }
   }
 
   // ---- partial outputs of this split
@@ -302,60 +310,84 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
 // One thread per (output row, 4 consecutive output columns); the loop over splits issues
 // independent 16-byte loads.
 // ------------------------------------------------------------------------------------------
+// One workgroup per output row (b, query head, position). Its 256 threads are CPB float4
+// columns x G split groups; group g handles splits g, g+G, ... so that many partial rows are
+// loaded at once, and the groups' sums meet in LDS. With M = max_s LSE_s and w_s =
+// exp(LSE_s - M): O = sum_s w_s O_s / sum_s w_s and LSE = M + ln(sum_s w_s); a split with no
+// visible key (LSE_s = -inf) has weight 0.
 template <int DV>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  constexpr int TPR = DV / 4;  // threads per row
+  constexpr int CPB = DV / 4;       // float4 columns per row
+  constexpr int G = 256 / CPB;      // split groups
+  static_assert(CPB <= 256 && 256 % CPB == 0, "row must fit one workgroup");
+  __shared__ float4 red[G][CPB];
+  __shared__ float gmax[G];
+  __shared__ float gden[G];
   const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / TPR;
-  const int c4 = (int)(gid % TPR);
-  if (row >= rows) return;
-  // Single pass with a running maximum (the combine's weights, rescaled when the maximum
-  // grows); four splits per iteration so their loads are in flight together.
-  float mx = -INFINITY, den = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < a.S; s0 += 4) {
-    float ls[4];
-    float4 x[4];
+  const int64_t row = blockIdx.x;
+  const int c4 = threadIdx.x % CPB;
+  const int grp = threadIdx.x / CPB;
+
+  // maximum LSE over the splits
+  float mx = -INFINITY;
+  for (int s = grp; s < a.S; s += G) mx = fmaxf(mx, a.lse_part[(int64_t)s * rows + row]);
+  if (c4 == 0) gmax[grp] = mx;
+  __syncthreads();
+  float M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u;
-      if (s < a.S) {
-        ls[u] = a.lse_part[(int64_t)s * rows + row];
-        x[u] = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
-      } else {
-        ls[u] = -INFINITY;
-        x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = 0; g < G; ++g) M = fmaxf(M, gmax[g]);
+
+  // weighted sum of this group's splits, four partial rows in flight per step
+  float den = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+    for (int s0 = grp; s0 < a.S; s0 += 4 * G) {
+      float ls[4];
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u * G;
+        if (s < a.S) {
+          ls[u] = a.lse_part[(int64_t)s * rows + row];
+          x[u] = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
+        } else {
+          ls[u] = -INFINITY;
+          x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - M);
+        den += w;
+        o.x += w * x[u].x;
+        o.y += w * x[u].y;
+        o.z += w * x[u].z;
+        o.w += w * x[u].w;
       }
     }
-    float mnew = mx;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mnew = fmaxf(mnew, ls[u]);
-    if (mnew == -INFINITY) continue;
-    const float r = (mx == -INFINITY) ? 0.f : expf(mx - mnew);
-    den *= r;
-    o.x *= r; o.y *= r; o.z *= r; o.w *= r;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float ws = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - mnew);
-      den += ws;
-      o.x += ws * x[u].x;
-      o.y += ws * x[u].y;
-      o.z += ws * x[u].z;
-      o.w += ws * x[u].w;
-    }
-    mx = mnew;
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  red[grp][c4] = o;
+  if (c4 == 0) gden[grp] = den;
+  __syncthreads();
+  if (grp != 0) return;
+  float dt = 0.f;
+  float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float4 r = red[g][c4];
+    ot.x += r.x; ot.y += r.y; ot.z += r.z; ot.w += r.w;
+    dt += gden[g];
+  }
+  const float inv = dt > 0.f ? 1.0f / dt : 0.f;
   const int pos = (int)(row % a.Lq);
   const int hq = (int)((row / a.Lq) % a.Hq);
   const int b = (int)(row / ((int64_t)a.Lq * a.Hq));
   uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)pos * a.o_sl + (int64_t)hq * a.o_sh + 4 * c4;
   uint2 pk;
-  pk.x = pack_bf16x2(o.x * inv, o.y * inv);
-  pk.y = pack_bf16x2(o.z * inv, o.w * inv);
+  pk.x = pack_bf16x2(ot.x * inv, ot.y * inv);
+  pk.y = pack_bf16x2(ot.z * inv, ot.w * inv);
   *reinterpret_cast<uint2*>(dst) = pk;
-  if (a.lse != nullptr && c4 == 0) a.lse[row] = den > 0.f ? mx + logf(den) : -INFINITY;
+  if (a.lse != nullptr && c4 == 0) a.lse[row] = dt > 0.f ? M + logf(dt) : -INFINITY;
 }
 
 template <int DQK, int DV, int BNK, int NST>
@@ -367,17 +399,16 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
 
 template <int DV>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.B * a.Hq * a.Lq * (DV / 4);
-  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, a);
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream) {
-  if (dqk == 576) return launch_split_t<576, 512, 32, 3>(a, stream);
-  if (dqk == 128) return launch_split_t<128, 128, 64, 3>(a, stream);
+  if (dqk == 576) return launch_split_t<576, 512, 32, 4>(a, stream);
+  if (dqk == 128) return launch_split_t<128, 128, 64, 4>(a, stream);
   return launch_split_t<64, 64, 64, 4>(a, stream);
 }
 

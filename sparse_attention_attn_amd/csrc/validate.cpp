@@ -107,7 +107,7 @@ int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   const int g = Hq / Hkv;
   const int64_t colblk = ((int64_t)g * Lq + 15) / 16;
   const int64_t units = (int64_t)B * Hkv * colblk;
-  const int wg_per_cu = (Dqk == 64) ? 2 : 1;  // LDS ring: 64 KiB (D=64), 96-108 KiB otherwise
+  const int wg_per_cu = (Dqk == 64) ? 2 : 1;  // LDS ring: 64 KiB (D=64), 128-144 KiB otherwise
   int64_t s = (kCUs * wg_per_cu + units - 1) / units;
   const int64_t max_by_len = std::max<int64_t>(1, Lk / 256);  // at least 256 keys per split
   const int64_t max_s = (Lk + 63) / 64;
