@@ -1,13 +1,14 @@
-// fwd_prefill.hip — fused attention forward for prefill (dense, causal or not, GQA) and for
-// block-sparse index lists, on gfx950.
+// fwd_blocksparse.hip — fused block-sparse attention forward (causal, GQA) on gfx950.
 //
 // What is computed: O = softmax(scale·Q·Kᵀ + mask)·V and LSE per query row ("Resumen Técnico:
-// FlashMLA-ETAP", section "Mecanismo Central"), tile by tile with running softmax statistics
-// kept on chip ("Activar Flash Attention con llama.cpp para optimizar la inferencia", section
-// "¿Qué es Flash Attention y por qué es crucial para llama.cpp?"). The block-sparse variant
-// visits only the listed key blocks plus the listed vertical key columns of each query head
-// (MInference article, paragraphs on the A-shape / vertical-slash / block-sparse patterns and
-// the dynamically built sparse indices).
+// FlashMLA-ETAP", section "Mecanismo Central"), where a key is visible to a query only if its
+// 64-key block is listed for the query's 64-row block or its column is listed for the query's
+// head, and it is not in the query's causal future. The kernel visits only the listed key
+// blocks, then the listed vertical key columns outside them (MInference article, paragraphs on
+// the A-shape / vertical-slash / block-sparse patterns and the dynamically built sparse
+// indices), with running softmax statistics kept on chip ("Activar Flash Attention con
+// llama.cpp para optimizar la inferencia", section "¿Qué es Flash Attention y por qué es
+// crucial para llama.cpp?").
 //
 // Work decomposition: one workgroup owns 32*NW query rows of one (batch, query head); each
 // wave owns 32 rows. Keys stream through LDS in 64-key tiles (K tile + V tile), copied by
