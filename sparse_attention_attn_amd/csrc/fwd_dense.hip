@@ -22,13 +22,20 @@
 // iteration t copies tile t+2 while tiles t+1 (K read) and t-1 (V read) are in use. One
 // workgroup barrier per iteration frees the stage of tile t-2.
 //
-// Softmax. Scores live in the exp2 domain (x = s·scale·log2 e). Each row keeps a reference
-// maximum m that moves only when a tile's maximum exceeds it by more than kSlack, so the
-// output rescale (a multiply of all accumulators) almost never runs; weights are
-// exp2(x - m) <= 2^kSlack. Two row sums are kept: the sum of the bf16-rounded weights, which
-// normalises O (numerator and denominator then use the same weights, so a row dominated by one
-// key returns that key's value exactly), and the fp32 sum of the unrounded weights, which
-// gives the LSE.
+// Softmax. Scores live in the exp2 domain (x = s·scale·log2 e). Each row keeps a reference m,
+// the largest score seen when it was last set, and weights are exp2(x - m). The reference is
+// not moved by every larger score: the weights of a unit are computed against the current m
+// with no maximum taken, and only afterwards one compare of the row's updated fp32 sum decides
+// whether the unit was safe: the sum must be positive (the row has a reference) and at most
+// kSumLimit (no weight can overflow the accumulators; inf and NaN fail too). If any row of the
+// wave fails, the wave takes a slow path for that unit: it takes the unit's row maxima, moves
+// m, rescales the accumulators and sums, and recomputes the unit's weights. The P·V of a unit
+// runs one step after its weights, so the recomputed weights are the ones used. With a
+// reference that can lag the true maximum the weights exceed 1, which fp32 and bf16 hold
+// exactly as well in relative terms; two row sums are kept: the sum of the bf16-rounded
+// weights, which normalises O (numerator and denominator then use the same weights, so a row
+// dominated by one key returns that key's value exactly), and the fp32 sum of the unrounded
+// weights, which gives the LSE.
 
 #include "tile_io.hpp"
 
@@ -36,7 +43,9 @@ namespace attn {
 namespace {
 
 constexpr int kStages = 4;
-constexpr float kSlack = 8.0f;  // log2 headroom of the lazily moved reference maximum
+// Largest fp32 row sum a unit may leave (2^64). Every weight and the accumulated |O| (at most
+// the weight sum times max|V|) then stay far from fp32 overflow for any V below 2^60.
+constexpr uint32_t kSumLimitBits = 0x5f800000u;
 // Row blocks (32 query rows each) per wave of the dense kernel.
 constexpr int kDenseNR = 1;
 
@@ -82,7 +91,8 @@ template <int D, int NR>
 struct WaveRows {
   bf16x8 qop[NR][TileCfg<D>::KSTEPS];  // Qᵀ operands of the 32-row blocks
   f32x16 acc[NR][TileCfg<D>::DVB];     // Oᵀ accumulators
-  float m[NR];                         // reference maxima (exp2 domain)
+  float m[NR];                         // reference maxima (exp2 domain), -inf before any key
+  float mu[NR];                        // m where finite, +inf otherwise (all weights then 0)
   float lb[NR];                        // lane-partial sums of the bf16-rounded weights
   float lf[NR];                        // lane-partial sums of the fp32 weights
 };
@@ -140,15 +150,15 @@ template <int D, int NR>
 __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&sc)[NR],
                                            f32x16 (&sn)[NR], const bf16x8 (&pp)[NR][2],
                                            bf16x8 (&pc)[NR][2], uint32_t kt, int kb, uint32_t vt,
-                                           int vkb, float sl2, float (&alpha)[NR]) {
+                                           int vkb, float sl2, float (&sb)[NR], float (&sf)[NR],
+                                           bool& ok) {
   using C = TileCfg<D>;
   constexpr int NQ = C::KSTEPS;
   constexpr int NV = 2 * C::DVB;
   constexpr int NP = NQ + NV;
-  constexpr int NITEMS = 2 + 8 * NR;  // row maxima, reference moves, weight groups
+  constexpr int NITEMS = 8 * NR + 1;  // weight groups, then the check of the sums
   static_assert(NQ >= 2, "K read pipeline depth");
 
-  float mxl[NR], muse[NR], sb[NR], sf[NR];
   uint32_t pk[NR][2][4];
   bf16x8 kop[2], vop[3];
 
@@ -161,41 +171,29 @@ __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&s
   };
   auto item = [&](auto IT) {
     constexpr int it = decltype(IT)::value;
-    if constexpr (it == 0) {
-      // in-lane maxima of the 16 scores of each row block
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float mx = max3f(sc[r][0], sc[r][1], sc[r][2]);
-#pragma unroll
-        for (int j = 3; j + 1 < 16; j += 2) mx = max3f(mx, sc[r][j], sc[r][j + 1]);
-        mxl[r] = fmaxf(mx, sc[r][15]);
-      }
-    } else if constexpr (it == 1) {
-      // row maxima across the two lanes of a row; lazy move of the reference maxima
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const float tmax = max_halves(mxl[r]) * sl2;
-        const bool move = tmax > ws.m[r] + kSlack;
-        const float mnew = move ? tmax : ws.m[r];
-        alpha[r] = move ? fast_exp2(ws.m[r] - mnew) : 1.0f;
-        ws.m[r] = mnew;
-        muse[r] = (mnew == -INFINITY) ? 0.f : mnew;
-        sb[r] = ws.lb[r] * alpha[r];
-        sf[r] = ws.lf[r] * alpha[r];
-      }
-    } else {
-      // weight group g: scores 8*ks + 2*i and +1 of row block r
-      constexpr int g = it - 2;
-      constexpr int r = g >> 3, ks = (g >> 2) & 1, i = g & 3;
-      const float e0 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i], sl2, -muse[r]));
-      const float e1 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i + 1], sl2, -muse[r]));
+    if constexpr (it < 8 * NR) {
+      // weight group it: scores 8*ks + 2*i and +1 of row block r
+      constexpr int r = it >> 3, ks = (it >> 2) & 1, i = it & 3;
+      const float e0 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i], sl2, -ws.mu[r]));
+      const float e1 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i + 1], sl2, -ws.mu[r]));
       sf[r] += e0;
       sf[r] += e1;
       pk[r][ks][i] = pack_bf16x2(e0, e1);
       sb[r] = add_bf16_pair(pk[r][ks][i], sb[r]);
+    } else {
+      // 0 < sf <= 2^64 for every row of the lane (bit compare: 0, inf and NaN fail)
+      ok = true;
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        ok = ok && (__builtin_bit_cast(uint32_t, sf[r]) - 1u < kSumLimitBits);
     }
   };
 
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    sb[r] = ws.lb[r];
+    sf[r] = ws.lf[r];
+  }
   kop[0] = kread(0);
   kop[1] = kread(1);
   __builtin_amdgcn_sched_barrier(0);
@@ -224,37 +222,63 @@ __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&s
     for (int ks = 0; ks < 2; ++ks)
       pc[r][ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[r][ks][0], pk[r][ks][1], pk[r][ks][2],
                                                         pk[r][ks][3]));
-    ws.lb[r] = sb[r];
-    ws.lf[r] = sf[r];
   }
 }
 
 // Pins the weights and row sums of a unit to this point of the instruction stream: without it
-// the compiler sinks their computation past the rescale branch, away from the MFMAs it is meant
-// to overlap with. Emits no instruction.
-template <int D, int NR>
-__device__ __forceinline__ void anchor_weights(const WaveRows<D, NR>& ws,
-                                               const bf16x8 (&p)[NR][2]) {
+// the compiler sinks their computation past the slow-path branch, away from the MFMAs it is
+// meant to overlap with. Emits no instruction.
+template <int NR>
+__device__ __forceinline__ void anchor_weights(const bf16x8 (&p)[NR][2], const float (&sb)[NR],
+                                               const float (&sf)[NR]) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(p[r][ks]));
-    asm volatile("" ::"v"(ws.lb[r]), "v"(ws.lf[r]));
+    asm volatile("" ::"v"(sb[r]), "v"(sf[r]));
   }
 }
 
+// Slow path of a unit (taken when some row's sum check failed): moves every row's reference to
+// the larger of m and the unit's row maximum, rescales the accumulators and the sums of the
+// earlier units by exp2(m_old - m_new), and recomputes the unit's weights, packed Pᵀ and sums.
 template <int D, int NR>
-__device__ __forceinline__ void rescale(WaveRows<D, NR>& ws, const float (&alpha)[NR]) {
-  bool any = false;
+__device__ __forceinline__ void slow_unit(WaveRows<D, NR>& ws, const f32x16 (&sc)[NR],
+                                       bf16x8 (&pc)[NR][2], float sl2) {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) any = any || (alpha[r] != 1.0f);
-  if (__any(any)) {
+  for (int r = 0; r < NR; ++r) {
+    float mx = max3f(sc[r][0], sc[r][1], sc[r][2]);
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+    for (int j = 3; j + 1 < 16; j += 2) mx = max3f(mx, sc[r][j], sc[r][j + 1]);
+    mx = fmaxf(mx, sc[r][15]);
+    const float mnew = fmaxf(ws.m[r], max_halves(mx) * sl2);
+    const float munew = (mnew == -INFINITY) ? INFINITY : mnew;
+    // m_old = -inf gives 0 (nothing accumulated yet); an unchanged finite m gives 1
+    const float alpha = fast_exp2(ws.m[r] - munew);
 #pragma unroll
-      for (int b = 0; b < TileCfg<D>::DVB; ++b)
+    for (int b = 0; b < TileCfg<D>::DVB; ++b)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) ws.acc[r][b][j] *= alpha[r];
+      for (int j = 0; j < 16; ++j) ws.acc[r][b][j] *= alpha;
+    float sb = ws.lb[r] * alpha, sf = ws.lf[r] * alpha;
+    uint32_t pk[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e0 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i], sl2, -munew));
+        const float e1 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i + 1], sl2, -munew));
+        sf += e0;
+        sf += e1;
+        pk[ks][i] = pack_bf16x2(e0, e1);
+        sb = add_bf16_pair(pk[ks][i], sb);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pc[r][ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]));
+    ws.m[r] = mnew;
+    ws.mu[r] = munew;
+    ws.lb[r] = sb;
+    ws.lf[r] = sf;
   }
 }
 
@@ -278,6 +302,7 @@ __device__ __forceinline__ void load_q_rows(const FwdArgs& a, WaveRows<D, NR>& w
 #pragma unroll
     for (int bb = 0; bb < C::DVB; ++bb) ws.acc[r][bb] = f32x16{};
     ws.m[r] = -INFINITY;
+    ws.mu[r] = INFINITY;
     ws.lb[r] = 0.f;
     ws.lf[r] = 0.f;
   }
@@ -427,24 +452,32 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
       barrier_lds();   // ... for every wave, and every wave is done with step 2t
       if (t + 2 < ntiles) issue(t + 2);
     }
-    float alpha[NR];
+    float sb[NR], sf[NR];
+    bool ok;
     if (j >= nfull) mask_unit<NR>(sc[H], j, qw0, a.Lk, a.causal, a.off, l);
     // Sᵀ(j+1): H = 0 -> second half of tile t; H = 1 -> first half of tile t+1.
     // P·V of unit j-1: H = 0 -> second half of tile t-1; H = 1 -> first half of tile t.
     fused_step<D, NR>(ws, sc[H], sc[1 - H], pw[1 - H], pw[H], stage_addr(t + H) + kofs, 1 - H,
-                      stage_addr(t + 3 + H) + vofs, 1 - H, a.sl2, alpha);
-    anchor_weights<D, NR>(ws, pw[H]);
-    rescale<D, NR>(ws, alpha);
+                      stage_addr(t + 3 + H) + vofs, 1 - H, a.sl2, sb, sf, ok);
+    anchor_weights<NR>(pw[H], sb, sf);
+    if (__builtin_expect(__any(!ok), 0)) {
+      slow_unit<D, NR>(ws, sc[H], pw[H], a.sl2);
+    } else {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        ws.lb[r] = sb[r];
+        ws.lf[r] = sf[r];
+      }
+    }
   };
 
-  // 2*ntiles + 1 steps; the last one only finishes the P·V of the last unit.
-  const int J = 2 * ntiles + 1;
-  for (int t = 0;; ++t) {
+  // 2*ntiles + 1 steps; the last one only finishes the P·V of the last unit. The loop body is
+  // a whole tile with a single exit, so the accumulators keep their registers across it.
+  for (int t = 0; t < ntiles; ++t) {
     step(icn<0>{}, t);
-    if (2 * t + 1 >= J) break;
     step(icn<1>{}, t);
-    if (2 * t + 2 >= J) break;
   }
+  step(icn<0>{}, ntiles);
   wait_dma_all();
   store_rows<D, NR>(a, ws, b, hq, qw0, l);
 }

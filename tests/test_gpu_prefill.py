@@ -159,6 +159,31 @@ def test_planted_keys_causal_boundary():
     check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "planted")
 
 
+def test_reference_jumps():
+    """Scores that rise by about 29 (exp2 domain) per 32 keys in some heads and fall in others:
+    weights against a reference set on early keys overflow fp32 within a few units, so the
+    kernel has to move its reference mid-row; falling scores underflow instead."""
+    import torch
+    B, H, L, D = 1, 4, 256, 64
+    say("reference jumps")
+    u = torch.full((D,), 1.0)
+    t = 20.0 * (torch.arange(L) // 32).float()               # 0, 20, ..., 140
+    q = u.expand(B, L, H, D) + 0.1 * randn_bf16((B, L, H, D), 7600).float()
+    k = 0.1 * randn_bf16((B, L, H, D), 7601).float()
+    k[0, :, 0] += t[:, None] / 8.0                           # rising: s grows by 160 per unit
+    k[0, :, 1] += t.flip(0)[:, None] / 8.0                   # falling
+    k[0, :, 2] += (t[:, None] / 8.0) * ((torch.arange(L) % 64) < 32).float()[:, None]
+    v = randn_bf16((B, L, H, D), 7602).float()
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    scale = D ** -0.5
+    for causal in (True, False):
+        o, lse = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal, scale)
+        o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(scale),
+                                     causal)
+        assert np.isfinite(to_f64(o)).all()
+        check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"reference jumps causal={causal}")
+
+
 def test_prefill_deterministic():
     say("determinism prefill")
     q, k, v = _qkv(1, 8, 2, 700, 700, 128, 7500)
