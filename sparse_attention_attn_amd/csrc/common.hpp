@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -133,6 +135,44 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float xor_shuffle(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+template <int N>
+using icn = std::integral_constant<int, N>;
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(icn<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return fmaxf(fmaxf(a, b), c);
+}
+
+// Value of v held by lane l^32 (one v_permlane32_swap).
+__device__ __forceinline__ float other_half(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  // lanes 0..31: r[1] holds lane l+32's value; lanes 32..63: r[0] holds lane l-32's value
+  return __builtin_bit_cast(float, ((threadIdx.x & 63) < 32) ? hi : lo);
+}
+__device__ __forceinline__ float max_halves(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
+// Sum of the two bf16 values of a packed pair, added to c (one v_dot2c_f32_bf16).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p = __builtin_bit_cast(bf16x2_t, pair);
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  return __builtin_amdgcn_fdot2_f32_bf16(p, one, c, false);
+}
 
 // ------------------------------------------------------------------------------------------
 // Swizzled LDS tile layout. A tile holds ROWS rows of D bf16 (CPR = D/8 chunks of 16 bytes

@@ -43,49 +43,16 @@ namespace attn {
 namespace {
 
 constexpr int kStages = 4;
+// MFMA slots between an operand's LDS read and its use.
+#ifndef ATTN_DENSE_READ_AHEAD
+#define ATTN_DENSE_READ_AHEAD 2
+#endif
+constexpr int kReadAhead = ATTN_DENSE_READ_AHEAD;
 // Largest fp32 row sum a unit may leave (2^64). Every weight and the accumulated |O| (at most
 // the weight sum times max|V|) then stay far from fp32 overflow for any V below 2^60.
 constexpr uint32_t kSumLimitBits = 0x5f800000u;
 // Row blocks (32 query rows each) per wave of the dense kernel.
 constexpr int kDenseNR = 1;
-
-template <int N>
-using icn = std::integral_constant<int, N>;
-
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(icn<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  return fmaxf(fmaxf(a, b), c);
-}
-
-// Value of v held by lane l^32 (one v_permlane32_swap).
-__device__ __forceinline__ float other_half(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const uint32_t lo = r[0], hi = r[1];
-  // lanes 0..31: r[1] holds lane l+32's value; lanes 32..63: r[0] holds lane l-32's value
-  return __builtin_bit_cast(float, ((threadIdx.x & 63) < 32) ? hi : lo);
-}
-__device__ __forceinline__ float max_halves(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const uint32_t lo = r[0], hi = r[1];
-  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
-}
-
-// Sum of the two bf16 values of a packed pair, added to c (one v_dot2c_f32_bf16).
-__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float c) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t p = __builtin_bit_cast(bf16x2_t, pair);
-  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-  return __builtin_amdgcn_fdot2_f32_bf16(p, one, c, false);
-}
 
 template <int D, int NR>
 struct WaveRows {
@@ -156,11 +123,18 @@ __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&s
   constexpr int NQ = C::KSTEPS;
   constexpr int NV = 2 * C::DVB;
   constexpr int NP = NQ + NV;
-  constexpr int NITEMS = 8 * NR + 1;  // weight groups, then the check of the sums
+  // Softmax items, skewed so that no instruction waits on an exp of its own slot: item k
+  // computes the two weights of group k (fma, exp2) and folds in group k-1 (sums, bf16 pack);
+  // the last item checks the sums.
+  constexpr int NG = 8 * NR;
+  constexpr int NITEMS = NG + 2;
   static_assert(NQ >= 2, "K read pipeline depth");
 
   uint32_t pk[NR][2][4];
-  bf16x8 kop[2], vop[3];
+  float ew[2][2];  // weights of the last two groups, by group parity
+  constexpr int RA = kReadAhead;
+  static_assert(NQ >= RA && NV >= RA, "read-ahead deeper than a phase");
+  bf16x8 kop[RA], vop[RA + 1];
 
   auto kread = [&](int st) { return lds_read_b128_at(kt + 1024u * (kb * C::KSTEPS + st)); };
   // P·V slot v covers output column block b = v % DVB and k-step ks = v / DVB, so consecutive
@@ -171,16 +145,21 @@ __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&s
   };
   auto item = [&](auto IT) {
     constexpr int it = decltype(IT)::value;
-    if constexpr (it < 8 * NR) {
-      // weight group it: scores 8*ks + 2*i and +1 of row block r
+    if constexpr (it < NG) {
+      // group it: scores 8*ks + 2*i and +1 of row block r
       constexpr int r = it >> 3, ks = (it >> 2) & 1, i = it & 3;
-      const float e0 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i], sl2, -ws.mu[r]));
-      const float e1 = fast_exp2(fmaf(sc[r][8 * ks + 2 * i + 1], sl2, -ws.mu[r]));
-      sf[r] += e0;
-      sf[r] += e1;
-      pk[r][ks][i] = pack_bf16x2(e0, e1);
+      ew[it & 1][0] = fast_exp2(fmaf(sc[r][8 * ks + 2 * i], sl2, -ws.mu[r]));
+      ew[it & 1][1] = fast_exp2(fmaf(sc[r][8 * ks + 2 * i + 1], sl2, -ws.mu[r]));
+    }
+    if constexpr (it >= 1 && it <= NG) {
+      constexpr int g = it - 1;
+      constexpr int r = g >> 3, ks = (g >> 2) & 1, i = g & 3;
+      sf[r] += ew[g & 1][0];
+      sf[r] += ew[g & 1][1];
+      pk[r][ks][i] = pack_bf16x2(ew[g & 1][0], ew[g & 1][1]);
       sb[r] = add_bf16_pair(pk[r][ks][i], sb[r]);
-    } else {
+    }
+    if constexpr (it == NG + 1) {
       // 0 < sf <= 2^64 for every row of the lane (bit compare: 0, inf and NaN fail)
       ok = true;
 #pragma unroll
@@ -194,24 +173,24 @@ __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&s
     sb[r] = ws.lb[r];
     sf[r] = ws.lf[r];
   }
-  kop[0] = kread(0);
-  kop[1] = kread(1);
+#pragma unroll
+  for (int i = 0; i < RA; ++i) kop[i] = kread(i);
   __builtin_amdgcn_sched_barrier(0);
   static_for<0, NP>([&](auto PI) {
     constexpr int i = decltype(PI)::value;
     if constexpr (i < NQ) {
-      const bf16x8 k = kop[i & 1];
+      const bf16x8 k = kop[i % RA];
 #pragma unroll
       for (int r = 0; r < NR; ++r) sn[r] = mfma32(k, ws.qop[r][i], i == 0 ? f32x16{} : sn[r]);
-      if constexpr (i + 2 < NQ) kop[i & 1] = kread(i + 2);
-      if constexpr (i >= NQ - 2) vop[i - (NQ - 2)] = vread(i - (NQ - 2));
+      if constexpr (i + RA < NQ) kop[i % RA] = kread(i + RA);
+      if constexpr (i >= NQ - RA) vop[i - (NQ - RA)] = vread(i - (NQ - RA));
     } else {
       constexpr int v = i - NQ;
-      const bf16x8 vv = vop[v % 3];
+      const bf16x8 vv = vop[v % (RA + 1)];
 #pragma unroll
       for (int r = 0; r < NR; ++r)
         ws.acc[r][v % C::DVB] = mfma32(vv, pp[r][v / C::DVB], ws.acc[r][v % C::DVB]);
-      if constexpr (v + 2 < NV) vop[(v + 2) % 3] = vread(v + 2);
+      if constexpr (v + RA < NV) vop[(v + RA) % (RA + 1)] = vread(v + RA);
     }
     static_for<NITEMS * i / NP, NITEMS * (i + 1) / NP>(item);
     __builtin_amdgcn_sched_barrier(0);
