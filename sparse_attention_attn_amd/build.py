@@ -25,8 +25,12 @@ ARCH = "gfx950"
 #    operand quieting (inputs are finite; masked scores are -inf, which both settings keep);
 #  * MFMA results in VGPRs: the scores feed VALU code directly, and the register allocator
 #    parks the rarely touched output accumulators in AGPRs instead.
+#  * fwd_splitkv.hip: MFMA results in VGPRs too. Its output accumulators are only rescaled on
+#    the rare slow path, but with AGPR accumulators the compiler still moves all of them
+#    through VGPRs around that branch on every tile.
 EXTRA = {"fwd_dense.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans",
-                           "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                           "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "fwd_splitkv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -166,6 +166,16 @@ __device__ __forceinline__ float max_halves(float v) {
   return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
 }
 
+// Maximum-free softmax check. A unit's weights are computed as exp2(x - mu) against a row's
+// reference mu, with no maximum taken; the unit is accepted when the row's running fp32 weight
+// sum afterwards lies in (0, 2^64]: positive (the row has a reference) and small enough that no
+// weight, nor |O| <= (weight sum) * max|V| for any V below 2^60, comes near fp32 overflow. The
+// compare is on the bits, so 0, inf and NaN all fail.
+constexpr uint32_t kSumLimitBits = 0x5f800000u;  // 2^64
+__device__ __forceinline__ bool sum_ok(float s) {
+  return __builtin_bit_cast(uint32_t, s) - 1u < kSumLimitBits;
+}
+
 // Sum of the two bf16 values of a packed pair, added to c (one v_dot2c_f32_bf16).
 __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float c) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

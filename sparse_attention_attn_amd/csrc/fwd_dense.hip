@@ -48,9 +48,6 @@ constexpr int kStages = 4;
 #define ATTN_DENSE_READ_AHEAD 2
 #endif
 constexpr int kReadAhead = ATTN_DENSE_READ_AHEAD;
-// Largest fp32 row sum a unit may leave (2^64). Every weight and the accumulated |O| (at most
-// the weight sum times max|V|) then stay far from fp32 overflow for any V below 2^60.
-constexpr uint32_t kSumLimitBits = 0x5f800000u;
 // Row blocks (32 query rows each) per wave of the dense kernel.
 constexpr int kDenseNR = 1;
 
@@ -164,7 +161,7 @@ __device__ __forceinline__ void fused_step(WaveRows<D, NR>& ws, const f32x16 (&s
       ok = true;
 #pragma unroll
       for (int r = 0; r < NR; ++r)
-        ok = ok && (__builtin_bit_cast(uint32_t, sf[r]) - 1u < kSumLimitBits);
+        ok = ok && sum_ok(sf[r]);
     }
   };
 

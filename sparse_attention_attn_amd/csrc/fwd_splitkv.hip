@@ -75,6 +75,10 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char st3[NST > 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char st4[NST > 4 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char st5[NST > 5 ? C::STAGE : 16];
+  // MLA: the 4 waves split the Dqk reduction of Sᵀ and add their partial score tiles here.
+  constexpr bool KSPLIT = C::MLA;
+  constexpr int QW = KSPLIT ? (C::QSTEPS + 3) / 4 : C::QSTEPS;  // Qᵀ steps held per wave
+  __shared__ f32x4 xbuf[KSPLIT ? 4 * C::KBLK * 64 : 1];
   auto stage = [&](auto S) -> char* {
     constexpr int s = decltype(S)::value;
     if constexpr (s == 0) return st0;
@@ -117,17 +121,22 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   const int ntiles = __builtin_amdgcn_readfirstlane(kend > kstart ? (kend - kstart + BNK - 1) / BNK : 0);
 
   // Qᵀ operand: lane l holds column l%16, head-dim elements 32*s + 8*(l/16) .. +7
-  bf16x8 qop[C::QSTEPS];
+  // With KSPLIT, wave w holds the reduction steps [qs0, qs1) only (4 or 5 of 18 for MLA).
+  const int qs0 = KSPLIT ? (C::QSTEPS * w) / 4 : 0;
+  const int qs1 = KSPLIT ? (C::QSTEPS * (w + 1)) / 4 : C::QSTEPS;
+  bf16x8 qop[QW];
   {
     const uint16_t* qr = a.q + (int64_t)b * a.q_sb + (int64_t)pos * a.q_sl + (int64_t)hq * a.q_sh;
 #pragma unroll
-    for (int s = 0; s < C::QSTEPS; ++s)
-      qop[s] = col_ok ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
+    for (int i = 0; i < QW; ++i) {
+      const int s = qs0 + i;
+      qop[i] = (col_ok && s < qs1) ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
+    }
     // Use the loaded operands here, before the copy ring starts: the compiler then waits for
     // these loads once, instead of at their first use inside the loop, where its wait would
     // also drain the tile copies in flight.
 #pragma unroll
-    for (int s = 0; s < C::QSTEPS; ++s) asm volatile("" ::"v"(qop[s]));
+    for (int i = 0; i < QW; ++i) asm volatile("" ::"v"(qop[i]));
   }
 
   const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
@@ -174,7 +183,9 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   f32x4 acc[C::DVB];
 #pragma unroll
   for (int i = 0; i < C::DVB; ++i) acc[i] = f32x4{};
-  float m = -INFINITY, lsum = 0.f;
+  // m: reference maximum (exp2 domain), -inf before any visible key; mu: m where finite, +inf
+  // otherwise; sb / sf: lane-partial sums of the bf16-rounded and of the fp32 weights.
+  float m = -INFINITY, mu = INFINITY, sb = 0.f, sf = 0.f;
 
   const int G = l >> 4;
   const int jj = (l & 15) >> 2;
@@ -187,29 +198,56 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     const char* vt = C::MLA ? kt : kt + C::KT_BYTES;
     const int base = kstart + t * BNK;
 
-    // ---- Sᵀ: KBLK blocks of 16 keys x 16 columns; K operands read one step ahead
+    // ---- Sᵀ: KBLK blocks of 16 keys x 16 columns
     f32x4 st[C::KBLK];
-    bf16x8 kcur[C::KBLK], knxt[C::KBLK];
-#pragma unroll
-    for (int k = 0; k < C::KBLK; ++k) {
-      st[k] = f32x4{};
+    auto kread = [&](int s, int k) {
       const uint32_t r = 16u * k + krow;
-      kcur[k] = lds_read_bf16x8(kt, (r * (DQK / 8) + ((uint32_t)G ^ Swz<DQK>::f(r))) * 16u);
-    }
+      const uint32_t c = (uint32_t)(4 * s + G);
+      return lds_read_bf16x8(kt, (r * (DQK / 8) + (c ^ Swz<DQK>::f(r))) * 16u);
+    };
 #pragma unroll
-    for (int s = 0; s < C::QSTEPS; ++s) {
-      if (s + 1 < C::QSTEPS) {
+    for (int k = 0; k < C::KBLK; ++k) st[k] = f32x4{};
+    if constexpr (KSPLIT) {
+      // this wave's share of the reduction, then the sum of the four partial tiles (added in
+      // wave order, so every wave holds the same scores and the same softmax state)
 #pragma unroll
-        for (int k = 0; k < C::KBLK; ++k) {
-          const uint32_t r = 16u * k + krow;
-          const uint32_t c = (uint32_t)(4 * (s + 1) + G);
-          knxt[k] = lds_read_bf16x8(kt, (r * (DQK / 8) + (c ^ Swz<DQK>::f(r))) * 16u);
+      for (int i = 0; i < QW; ++i) {
+        if (i + 1 < QW || qs0 + i < qs1) {
+#pragma unroll
+          for (int k = 0; k < C::KBLK; ++k) st[k] = mfma16(kread(qs0 + i, k), qop[i], st[k]);
         }
       }
 #pragma unroll
-      for (int k = 0; k < C::KBLK; ++k) st[k] = mfma16(kcur[k], qop[s], st[k]);
+      for (int k = 0; k < C::KBLK; ++k) xbuf[(w * C::KBLK + k) * 64 + l] = st[k];
+      // LDS writes of all waves done; the copy ring's loads stay in flight
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-      for (int k = 0; k < C::KBLK; ++k) kcur[k] = knxt[k];
+      for (int k = 0; k < C::KBLK; ++k) {
+        f32x4 sum = xbuf[k * 64 + l];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) sum += xbuf[(ww * C::KBLK + k) * 64 + l];
+        st[k] = sum;
+      }
+    } else {
+      // K operands of step s read RA steps ahead (about 64 MFMA cycles of cover, more than
+      // the LDS latency): with one wave per SIMD nothing else hides that latency.
+      constexpr int RA = C::KBLK >= 4 ? 1 : 3;
+      static_assert(C::QSTEPS > RA, "read-ahead deeper than the reduction");
+      bf16x8 kr[RA + 1][C::KBLK];
+#pragma unroll
+      for (int s = 0; s < RA; ++s)
+#pragma unroll
+        for (int k = 0; k < C::KBLK; ++k) kr[s][k] = kread(s, k);
+      static_for<0, C::QSTEPS>([&](auto SI) {
+        constexpr int s = decltype(SI)::value;
+#pragma unroll
+        for (int k = 0; k < C::KBLK; ++k) st[k] = mfma16(kr[s % (RA + 1)][k], qop[s], st[k]);
+        // refill the slot consumed one step earlier
+        if constexpr (s + RA < C::QSTEPS) {
+#pragma unroll
+          for (int k = 0; k < C::KBLK; ++k) kr[(s + RA) % (RA + 1)][k] = kread(s + RA, k);
+        }
+      });
     }
     // ---- mask: slot (k, j) holds key base + 16*k + 4*(l/16) + j
     const bool need_mask = (base + BNK > kend) || (a.causal && base + BNK - 1 > first_pos + a.off);
@@ -222,37 +260,59 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
           if (key >= kend || key > lim) st[k][j] = -INFINITY;
         }
     }
-    // ---- online softmax over this tile's keys for each column
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < C::KBLK; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, st[k][j]);
-    mx = fmaxf(mx, xor_shuffle(mx, 16));
-    mx = fmaxf(mx, xor_shuffle(mx, 32));
-    const float mnew = fmaxf(m, mx * a.sl2);
-    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
-    m = mnew;
-    float psum = 0.f;
+    // ---- weights against the column's reference mu, with no maximum taken; the running
+    // fp32 sum then decides whether the tile was safe, else the slow path moves the reference
+    f32x4 pw[C::KBLK];
+    float sfn = sf;
 #pragma unroll
     for (int k = 0; k < C::KBLK; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        st[k][j] = fast_exp2(fmaf(st[k][j], a.sl2, -muse));
-        psum += st[k][j];
+        pw[k][j] = fast_exp2(fmaf(st[k][j], a.sl2, -mu));
+        sfn += pw[k][j];
       }
-    lsum = lsum * alpha + psum;
+    if (__builtin_expect(__any(!sum_ok(sfn)), 0)) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < C::DVB; ++i) acc[i] *= alpha;
+      for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, st[k][j]);
+      mx = fmaxf(mx, xor_shuffle(mx, 16));
+      mx = fmaxf(mx, xor_shuffle(mx, 32));
+      const float mnew = fmaxf(m, mx * a.sl2);
+      const float munew = (mnew == -INFINITY) ? INFINITY : mnew;
+      const float alpha = fast_exp2(m - munew);  // 0 while nothing was accumulated, 1 if unmoved
+#pragma unroll
+      for (int i = 0; i < C::DVB; ++i) acc[i] *= alpha;
+      sb *= alpha;
+      sf *= alpha;
+      sfn = sf;
+#pragma unroll
+      for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pw[k][j] = fast_exp2(fmaf(st[k][j], a.sl2, -munew));
+          sfn += pw[k][j];
+        }
+      m = mnew;
+      mu = munew;
+    }
+    sf = sfn;
 
     // ---- Oᵀ += Vᵀ·Pᵀ over 32-key steps. Operand slot i of lane l covers key
-    // 32*ps + 16*(i/4) + 4*(l/16) + i%4 (blocks 2ps and 2ps+1 of Sᵀ).
+    // 32*ps + 16*(i/4) + 4*(l/16) + i%4 (blocks 2ps and 2ps+1 of Sᵀ). The bf16 sum is taken
+    // over the packed weights the MFMAs multiply.
 #pragma unroll
     for (int ps = 0; ps < C::PVSTEPS; ++ps) {
-      const f32x4& x0 = st[2 * ps];
-      const f32x4& x1 = st[2 * ps + 1];
-      const bf16x8 pop = pack_bf16x8(x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]);
+      const f32x4& x0 = pw[2 * ps];
+      const f32x4& x1 = pw[2 * ps + 1];
+      const uint4 pq = make_uint4(pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                                  pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]));
+      sb = add_bf16_pair(pq.x, sb);
+      sb = add_bf16_pair(pq.y, sb);
+      sb = add_bf16_pair(pq.z, sb);
+      sb = add_bf16_pair(pq.w, sb);
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, pq);
       const uint32_t rlo = (uint32_t)(32 * ps + 4 * G + jj);
       bf16x8 vop[C::DVB];
 #pragma unroll
@@ -290,10 +350,14 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   }
 
   // ---- partial outputs of this split
-  float tot = lsum + xor_shuffle(lsum, 16);
-  tot = tot + xor_shuffle(tot, 32);
+  // O_s is normalised by the sum of the bf16 weights the MFMAs multiplied (a column dominated
+  // by one key returns its value exactly); LSE_s comes from the fp32 sum.
+  float tb = sb + xor_shuffle(sb, 16);
+  tb = tb + xor_shuffle(tb, 32);
+  float tf = sf + xor_shuffle(sf, 16);
+  tf = tf + xor_shuffle(tf, 32);
   if (!col_ok) return;
-  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  const float inv = tb > 0.f ? 1.0f / tb : 0.f;
   const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq) * a.Lq + pos;
   float* op = a.o_part + prow * DV;
 #pragma unroll
@@ -302,7 +366,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     *reinterpret_cast<float4*>(op + dv) =
         make_float4(acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv);
   }
-  if (w == 0 && G == 0) a.lse_part[prow] = tot > 0.f ? m * kLn2 + logf(tot) : -INFINITY;
+  if (w == 0 && G == 0) a.lse_part[prow] = tf > 0.f ? m * kLn2 + logf(tf) : -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------------
