@@ -175,6 +175,57 @@ def bench_blocksparse(w, steps, warmup):
             "density_vs_causal": pairs / dense}
 
 
+def mla_causal_pairs(lq, lk):
+    """Visible (query, key) pairs of one head with bottom-right causal masking."""
+    return sum(max(0, min(lk, p + lk - lq + 1)) for p in range(lq))
+
+
+def bench_etap_grid(steps, warmup):
+    """The FlashMLA-ETAP decode grid: MLA (16 heads, Dqk 576, V = first 512 columns of the
+    latent cache), batch 16 and 32, one or two query tokens, KV length 512..64K, split-KV +
+    LSE combine per step. Inputs are drawn on the device from seeded generators (the largest
+    points hold several GB); KV copies rotate over >= 1 GiB so the 256 MB Infinity Cache
+    cannot serve repeats."""
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import ETAP_GRID, randn_bf16_device
+    out = []
+    caches = {}
+    for name, w in ETAP_GRID.items():
+        key = (w.B, w.Lk)
+        kv_bytes = w.B * w.Lk * w.Dqk * 2
+        if key not in caches:
+            caches.clear()
+            torch.cuda.empty_cache()
+            ncopies = max(2, -(-(1 << 30) // kv_bytes))
+            caches[key] = [randn_bf16_device((w.B, w.Lk, 1, w.Dqk), 1000 * w.index + 1 + 7 * c)
+                           for c in range(ncopies)]
+        ks = caches[key]
+        q = randn_bf16_device((w.B, w.Lq, w.Hq, w.Dqk), 1000 * w.index)
+        o = torch.empty((w.B, w.Lq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+        nsp = S.attn_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.Dqk, w.Dv)
+        op = torch.empty((nsp, w.B, w.Hq, w.Lq, w.Dv), dtype=torch.float32, device="cuda:0")
+        lp = torch.empty((nsp, w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+        it = [0]
+
+        def step():
+            kk = ks[it[0] % len(ks)]
+            it[0] += 1
+            S.attn_fwd_splitkv(q, kk, kk[..., :w.Dv], op, lp, causal=True, scale=w.scale)
+            S.attn_combine_lse(op, lp, o, lse)
+
+        ms, _ = time_steps(step, steps, warmup)
+        flops = 2 * (w.Dqk + w.Dv) * w.B * w.Hq * mla_causal_pairs(w.Lq, w.Lk)
+        nbytes = kv_bytes + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4
+        out.append({"B": w.B, "Lq": w.Lq, "Lk": w.Lk, "num_splits": nsp, "us": round(ms * 1e3, 2),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        log(f"  {name}: {out[-1]}")
+    caches.clear()
+    return out
+
+
 # ------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, budget_s):
     """The fp64 oracle, as it stands, timed on a bounded sample of the headline workload:
@@ -217,6 +268,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None, help="comma list of workloads to run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-etap-grid", action="store_true",
+                    help="skip the FlashMLA-ETAP decode grid sweep")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -293,6 +346,11 @@ def main():
             if "density_vs_causal" in r:
                 wl[name]["density_vs_causal"] = round(r["density_vs_causal"], 4)
     out["workloads"] = wl
+    if not args.no_etap_grid and args.only is None:
+        log("FlashMLA-ETAP decode grid ...")
+        out["etap_grid"] = {"unit": "split-KV + combine per step; TFLOP/s = 2*(576+512) per "
+                                    "visible (query, key) pair; GB/s = latent cache + Q + O + LSE",
+                            "points": bench_etap_grid(max(5, args.steps // 2), 3)}
     if not args.no_cpu_baseline and HEADLINE in res:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)

@@ -101,7 +101,8 @@ int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o
     a.sl2 = scale * kLog2e;
     a.num_splits = num_splits;
     a.chunk = attn::split_chunk(Lk, num_splits);
-    a.ncolblk = (a.g * Lq + attn::kSplitCols - 1) / attn::kSplitCols;
+    const int cols = attn::split_cols(Dqk, a.g * Lq);
+    a.ncolblk = (a.g * Lq + cols - 1) / cols;
     return launch_status(fn, attn::launch_splitkv(a, Dqk, Dv, static_cast<hipStream_t>(stream)));
   } catch (const std::exception& e) {
     return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());

@@ -23,6 +23,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "validate.hpp"
 
 namespace attn {
 namespace {
@@ -63,9 +64,10 @@ struct SplitCfg {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-template <int DQK, int DV, int BNK, int NST>
+template <int DQK, int DV, int BNK, int NST, int NCB>
 __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   using C = SplitCfg<DQK, DV, BNK, NST>;
+  static_assert(NCB == 1 || C::MLA, "two column blocks per workgroup only for the MLA shape");
   static_assert(NST >= 2 && NST <= 6, "2..6 stages");
   // One array per ring stage: with the stage fixed at compile time the compiler can tell the
   // stage being read from the stages still being filled, and does not wait for those copies.
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   // MLA: the 4 waves split the Dqk reduction of Sᵀ and add their partial score tiles here.
   constexpr bool KSPLIT = C::MLA;
   constexpr int QW = KSPLIT ? (C::QSTEPS + 3) / 4 : C::QSTEPS;  // Qᵀ steps held per wave
-  __shared__ f32x4 xbuf[KSPLIT ? 4 * C::KBLK * 64 : 1];
+  __shared__ f32x4 xbuf[KSPLIT ? 4 * NCB * C::KBLK * 64 : 1];
   auto stage = [&](auto S) -> char* {
     constexpr int s = decltype(S)::value;
     if constexpr (s == 0) return st0;
@@ -102,17 +104,23 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   const int cb = lid % a.ncolblk;
   const int b = lid / a.ncolblk;
 
+  // The workgroup's query columns: NCB blocks of 16; lane l holds column l%16 of each block.
   const int ncols = a.g * a.Lq;
-  const int col = cb * 16 + (l & 15);
-  const bool col_ok = col < ncols;
-  const int pos = col_ok ? col / a.g : 0;
-  const int hq = hkv * a.g + (col_ok ? col % a.g : 0);
+  bool col_ok[NCB];
+  int pos[NCB], hq[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    const int col = (cb * NCB + c) * 16 + (l & 15);
+    col_ok[c] = col < ncols;
+    pos[c] = col_ok[c] ? col / a.g : 0;
+    hq[c] = hkv * a.g + (col_ok[c] ? col % a.g : 0);
+  }
 
-  // keys of this split, cut by the causal horizon of the block's last column
+  // keys of this split, cut by the causal horizon of the workgroup's last column
   const int kstart = sp * a.chunk;
   int kend = min(a.Lk, kstart + a.chunk);
-  const int last_col = min(ncols, cb * 16 + 16) - 1;
-  const int first_pos = (cb * 16) / a.g;
+  const int last_col = min(ncols, (cb + 1) * NCB * 16) - 1;
+  const int first_pos = (cb * NCB * 16) / a.g;
   const int last_pos = last_col / a.g;
   if (a.causal) kend = min(kend, last_pos + a.off + 1);
   // split bounds are uniform over the workgroup: keep them in scalar registers so the ring's
@@ -124,20 +132,24 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   // With KSPLIT, wave w holds the reduction steps [qs0, qs1) only (4 or 5 of 18 for MLA).
   const int qs0 = KSPLIT ? (C::QSTEPS * w) / 4 : 0;
   const int qs1 = KSPLIT ? (C::QSTEPS * (w + 1)) / 4 : C::QSTEPS;
-  bf16x8 qop[QW];
-  {
-    const uint16_t* qr = a.q + (int64_t)b * a.q_sb + (int64_t)pos * a.q_sl + (int64_t)hq * a.q_sh;
+  bf16x8 qop[NCB][QW];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    const uint16_t* qr =
+        a.q + (int64_t)b * a.q_sb + (int64_t)pos[c] * a.q_sl + (int64_t)hq[c] * a.q_sh;
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
       const int s = qs0 + i;
-      qop[i] = (col_ok && s < qs1) ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
+      qop[c][i] = (col_ok[c] && s < qs1) ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
     }
-    // Use the loaded operands here, before the copy ring starts: the compiler then waits for
-    // these loads once, instead of at their first use inside the loop, where its wait would
-    // also drain the tile copies in flight.
-#pragma unroll
-    for (int i = 0; i < QW; ++i) asm volatile("" ::"v"(qop[i]));
   }
+  // Use the loaded operands here, before the copy ring starts: the compiler then waits for
+  // these loads once, instead of at their first use inside the loop, where its wait would
+  // also drain the tile copies in flight.
+#pragma unroll
+  for (int c = 0; c < NCB; ++c)
+#pragma unroll
+    for (int i = 0; i < QW; ++i) asm volatile("" ::"v"(qop[c][i]));
 
   const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
@@ -180,17 +192,26 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     }
   };
 
-  f32x4 acc[C::DVB];
+  // Per column block: Oᵀ accumulators; m: reference maximum (exp2 domain), -inf before any
+  // visible key; mu: m where finite, +inf otherwise; sb / sf: lane-partial sums of the
+  // bf16-rounded and of the fp32 weights.
+  f32x4 acc[NCB][C::DVB];
+  float m[NCB], mu[NCB], sb[NCB], sf[NCB];
+  int lim[NCB];
 #pragma unroll
-  for (int i = 0; i < C::DVB; ++i) acc[i] = f32x4{};
-  // m: reference maximum (exp2 domain), -inf before any visible key; mu: m where finite, +inf
-  // otherwise; sb / sf: lane-partial sums of the bf16-rounded and of the fp32 weights.
-  float m = -INFINITY, mu = INFINITY, sb = 0.f, sf = 0.f;
+  for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+    for (int i = 0; i < C::DVB; ++i) acc[c][i] = f32x4{};
+    m[c] = -INFINITY;
+    mu[c] = INFINITY;
+    sb[c] = 0.f;
+    sf[c] = 0.f;
+    lim[c] = a.causal ? pos[c] + a.off : 0x7fffffff;
+  }
 
   const int G = l >> 4;
   const int jj = (l & 15) >> 2;
   const int cc = l & 3;
-  const int lim = a.causal ? pos + a.off : 0x7fffffff;
   const uint32_t krow = (uint32_t)(l & 15);
 
   auto compute = [&](auto S, int t) {
@@ -198,15 +219,17 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     const char* vt = C::MLA ? kt : kt + C::KT_BYTES;
     const int base = kstart + t * BNK;
 
-    // ---- Sᵀ: KBLK blocks of 16 keys x 16 columns
-    f32x4 st[C::KBLK];
+    // ---- Sᵀ: per column block, KBLK blocks of 16 keys x 16 columns
+    f32x4 st[NCB][C::KBLK];
     auto kread = [&](int s, int k) {
       const uint32_t r = 16u * k + krow;
       const uint32_t c = (uint32_t)(4 * s + G);
       return lds_read_bf16x8(kt, (r * (DQK / 8) + (c ^ Swz<DQK>::f(r))) * 16u);
     };
 #pragma unroll
-    for (int k = 0; k < C::KBLK; ++k) st[k] = f32x4{};
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int k = 0; k < C::KBLK; ++k) st[c][k] = f32x4{};
     if constexpr (KSPLIT) {
       // this wave's share of the reduction, then the sum of the four partial tiles (added in
       // wave order, so every wave holds the same scores and the same softmax state)
@@ -214,20 +237,28 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
       for (int i = 0; i < QW; ++i) {
         if (i + 1 < QW || qs0 + i < qs1) {
 #pragma unroll
-          for (int k = 0; k < C::KBLK; ++k) st[k] = mfma16(kread(qs0 + i, k), qop[i], st[k]);
+          for (int k = 0; k < C::KBLK; ++k) {
+            const bf16x8 kk = kread(qs0 + i, k);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) st[c][k] = mfma16(kk, qop[c][i], st[c][k]);
+          }
         }
       }
 #pragma unroll
-      for (int k = 0; k < C::KBLK; ++k) xbuf[(w * C::KBLK + k) * 64 + l] = st[k];
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int k = 0; k < C::KBLK; ++k) xbuf[((w * NCB + c) * C::KBLK + k) * 64 + l] = st[c][k];
       // LDS writes of all waves done; the copy ring's loads stay in flight
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-      for (int k = 0; k < C::KBLK; ++k) {
-        f32x4 sum = xbuf[k * 64 + l];
+      for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) sum += xbuf[(ww * C::KBLK + k) * 64 + l];
-        st[k] = sum;
-      }
+        for (int k = 0; k < C::KBLK; ++k) {
+          f32x4 sum = xbuf[(c * C::KBLK + k) * 64 + l];
+#pragma unroll
+          for (int ww = 1; ww < 4; ++ww) sum += xbuf[((ww * NCB + c) * C::KBLK + k) * 64 + l];
+          st[c][k] = sum;
+        }
     } else {
       // K operands of step s read RA steps ahead (about 64 MFMA cycles of cover, more than
       // the LDS latency): with one wave per SIMD nothing else hides that latency.
@@ -241,7 +272,8 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
       static_for<0, C::QSTEPS>([&](auto SI) {
         constexpr int s = decltype(SI)::value;
 #pragma unroll
-        for (int k = 0; k < C::KBLK; ++k) st[k] = mfma16(kr[s % (RA + 1)][k], qop[s], st[k]);
+        for (int k = 0; k < C::KBLK; ++k)
+          st[0][k] = mfma16(kr[s % (RA + 1)][k], qop[0][s], st[0][k]);
         // refill the slot consumed one step earlier
         if constexpr (s + RA < C::QSTEPS) {
 #pragma unroll
@@ -253,66 +285,77 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     const bool need_mask = (base + BNK > kend) || (a.causal && base + BNK - 1 > first_pos + a.off);
     if (need_mask) {
 #pragma unroll
-      for (int k = 0; k < C::KBLK; ++k)
+      for (int c = 0; c < NCB; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = base + 16 * k + 4 * G + j;
-          if (key >= kend || key > lim) st[k][j] = -INFINITY;
-        }
+        for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = base + 16 * k + 4 * G + j;
+            if (key >= kend || key > lim[c]) st[c][k][j] = -INFINITY;
+          }
     }
     // ---- weights against the column's reference mu, with no maximum taken; the running
     // fp32 sum then decides whether the tile was safe, else the slow path moves the reference
-    f32x4 pw[C::KBLK];
-    float sfn = sf;
+    f32x4 pw[NCB][C::KBLK];
 #pragma unroll
-    for (int k = 0; k < C::KBLK; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pw[k][j] = fast_exp2(fmaf(st[k][j], a.sl2, -mu));
-        sfn += pw[k][j];
-      }
-    if (__builtin_expect(__any(!sum_ok(sfn)), 0)) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < C::KBLK; ++k)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, st[k][j]);
-      mx = fmaxf(mx, xor_shuffle(mx, 16));
-      mx = fmaxf(mx, xor_shuffle(mx, 32));
-      const float mnew = fmaxf(m, mx * a.sl2);
-      const float munew = (mnew == -INFINITY) ? INFINITY : mnew;
-      const float alpha = fast_exp2(m - munew);  // 0 while nothing was accumulated, 1 if unmoved
-#pragma unroll
-      for (int i = 0; i < C::DVB; ++i) acc[i] *= alpha;
-      sb *= alpha;
-      sf *= alpha;
-      sfn = sf;
+    for (int c = 0; c < NCB; ++c) {
+      float sfn = sf[c];
 #pragma unroll
       for (int k = 0; k < C::KBLK; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pw[k][j] = fast_exp2(fmaf(st[k][j], a.sl2, -munew));
-          sfn += pw[k][j];
+          pw[c][k][j] = fast_exp2(fmaf(st[c][k][j], a.sl2, -mu[c]));
+          sfn += pw[c][k][j];
         }
-      m = mnew;
-      mu = munew;
+      if (__builtin_expect(__any(!sum_ok(sfn)), 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, st[c][k][j]);
+        mx = fmaxf(mx, xor_shuffle(mx, 16));
+        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        const float mnew = fmaxf(m[c], mx * a.sl2);
+        const float munew = (mnew == -INFINITY) ? INFINITY : mnew;
+        // 0 while nothing was accumulated, 1 if unmoved
+        const float alpha = fast_exp2(m[c] - munew);
+#pragma unroll
+        for (int i = 0; i < C::DVB; ++i) acc[c][i] *= alpha;
+        sb[c] *= alpha;
+        sf[c] *= alpha;
+        sfn = sf[c];
+#pragma unroll
+        for (int k = 0; k < C::KBLK; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pw[c][k][j] = fast_exp2(fmaf(st[c][k][j], a.sl2, -munew));
+            sfn += pw[c][k][j];
+          }
+        m[c] = mnew;
+        mu[c] = munew;
+      }
+      sf[c] = sfn;
     }
-    sf = sfn;
 
     // ---- Oᵀ += Vᵀ·Pᵀ over 32-key steps. Operand slot i of lane l covers key
-    // 32*ps + 16*(i/4) + 4*(l/16) + i%4 (blocks 2ps and 2ps+1 of Sᵀ). The bf16 sum is taken
-    // over the packed weights the MFMAs multiply.
+    // 32*ps + 16*(i/4) + 4*(l/16) + i%4 (blocks 2ps and 2ps+1 of Sᵀ). Every V operand feeds
+    // the MFMAs of all column blocks. The bf16 sum is taken over the packed weights the MFMAs
+    // multiply.
 #pragma unroll
     for (int ps = 0; ps < C::PVSTEPS; ++ps) {
-      const f32x4& x0 = pw[2 * ps];
-      const f32x4& x1 = pw[2 * ps + 1];
-      const uint4 pq = make_uint4(pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
-                                  pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]));
-      sb = add_bf16_pair(pq.x, sb);
-      sb = add_bf16_pair(pq.y, sb);
-      sb = add_bf16_pair(pq.z, sb);
-      sb = add_bf16_pair(pq.w, sb);
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pq);
+      bf16x8 pop[NCB];
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const f32x4& x0 = pw[c][2 * ps];
+        const f32x4& x1 = pw[c][2 * ps + 1];
+        const uint4 pq = make_uint4(pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]),
+                                    pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]));
+        sb[c] = add_bf16_pair(pq.x, sb[c]);
+        sb[c] = add_bf16_pair(pq.y, sb[c]);
+        sb[c] = add_bf16_pair(pq.z, sb[c]);
+        sb[c] = add_bf16_pair(pq.w, sb[c]);
+        pop[c] = __builtin_bit_cast(bf16x8, pq);
+      }
       const uint32_t rlo = (uint32_t)(32 * ps + 4 * G + jj);
       bf16x8 vop[C::DVB];
 #pragma unroll
@@ -321,7 +364,9 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
         vop[i] = lds_read_tr_pair(vt, elem_off<C::VW>(rlo, dv), elem_off<C::VW>(rlo + 16, dv));
       }
 #pragma unroll
-      for (int i = 0; i < C::DVB; ++i) acc[i] = mfma16(vop[i], pop, acc[i]);
+      for (int i = 0; i < C::DVB; ++i)
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) acc[c][i] = mfma16(vop[i], pop[c], acc[c][i]);
     }
   };
 
@@ -352,21 +397,24 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   // ---- partial outputs of this split
   // O_s is normalised by the sum of the bf16 weights the MFMAs multiplied (a column dominated
   // by one key returns its value exactly); LSE_s comes from the fp32 sum.
-  float tb = sb + xor_shuffle(sb, 16);
-  tb = tb + xor_shuffle(tb, 32);
-  float tf = sf + xor_shuffle(sf, 16);
-  tf = tf + xor_shuffle(tf, 32);
-  if (!col_ok) return;
-  const float inv = tb > 0.f ? 1.0f / tb : 0.f;
-  const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq) * a.Lq + pos;
-  float* op = a.o_part + prow * DV;
 #pragma unroll
-  for (int i = 0; i < C::DVB; ++i) {
-    const int dv = w * C::DVW + 16 * i + 4 * G;
-    *reinterpret_cast<float4*>(op + dv) =
-        make_float4(acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv);
+  for (int c = 0; c < NCB; ++c) {
+    float tb = sb[c] + xor_shuffle(sb[c], 16);
+    tb = tb + xor_shuffle(tb, 32);
+    float tf = sf[c] + xor_shuffle(sf[c], 16);
+    tf = tf + xor_shuffle(tf, 32);
+    if (!col_ok[c]) continue;
+    const float inv = tb > 0.f ? 1.0f / tb : 0.f;
+    const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq[c]) * a.Lq + pos[c];
+    float* op = a.o_part + prow * DV;
+#pragma unroll
+    for (int i = 0; i < C::DVB; ++i) {
+      const int dv = w * C::DVW + 16 * i + 4 * G;
+      *reinterpret_cast<float4*>(op + dv) = make_float4(acc[c][i][0] * inv, acc[c][i][1] * inv,
+                                                        acc[c][i][2] * inv, acc[c][i][3] * inv);
+    }
+    if (w == 0 && G == 0) a.lse_part[prow] = tf > 0.f ? m[c] * kLn2 + logf(tf) : -INFINITY;
   }
-  if (w == 0 && G == 0) a.lse_part[prow] = tf > 0.f ? m * kLn2 + logf(tf) : -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -454,10 +502,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   if (a.lse != nullptr && c4 == 0) a.lse[row] = dt > 0.f ? M + logf(dt) : -INFINITY;
 }
 
-template <int DQK, int DV, int BNK, int NST>
+template <int DQK, int DV, int BNK, int NST, int NCB>
 hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.B * a.Hkv * a.ncolblk * a.num_splits;
-  hipLaunchKernelGGL((splitkv_kernel<DQK, DV, BNK, NST>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((splitkv_kernel<DQK, DV, BNK, NST, NCB>), dim3((unsigned)nwg), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -471,9 +520,12 @@ hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream) {
-  if (dqk == 576) return launch_split_t<576, 512, 32, 4>(a, stream);
-  if (dqk == 128) return launch_split_t<128, 128, 64, 4>(a, stream);
-  return launch_split_t<64, 64, 64, 4>(a, stream);
+  if (dqk == 576) {
+    if (split_cols(dqk, a.g * a.Lq) == 32) return launch_split_t<576, 512, 32, 4, 2>(a, stream);
+    return launch_split_t<576, 512, 32, 4, 1>(a, stream);
+  }
+  if (dqk == 128) return launch_split_t<128, 128, 64, 4, 1>(a, stream);
+  return launch_split_t<64, 64, 64, 4, 1>(a, stream);
 }
 
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream) {

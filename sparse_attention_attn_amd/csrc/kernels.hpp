@@ -47,7 +47,7 @@ struct SplitArgs {
   float sl2;
   int num_splits;
   int chunk;        // keys per split (multiple of 64)
-  int ncolblk;      // ceil(g * Lq / 16)
+  int ncolblk;      // ceil(g * Lq / split_cols(Dqk, g * Lq))
 };
 
 struct CombineArgs {
@@ -68,7 +68,7 @@ hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);
 constexpr int kDenseBlockM = 256;
 // Query rows per workgroup of the block-sparse kernel (one 64-row query block).
 constexpr int kSparseBlockM = 64;
-// Query columns ((head, position) pairs of one KV head) per split-KV workgroup.
+// Query columns per 16-column block of a split-KV workgroup (see split_cols in validate.hpp).
 constexpr int kSplitCols = 16;
 
 }  // namespace attn

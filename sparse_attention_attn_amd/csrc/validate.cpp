@@ -105,7 +105,8 @@ int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   constexpr int kCUs = 256;  // MI355X
   const int g = Hq / Hkv;
-  const int64_t colblk = ((int64_t)g * Lq + 15) / 16;
+  const int cols = split_cols(Dqk, g * Lq);
+  const int64_t colblk = ((int64_t)g * Lq + cols - 1) / cols;
   const int64_t units = (int64_t)B * Hkv * colblk;
   const int wg_per_cu = (Dqk == 64) ? 2 : 1;  // LDS ring: 64 KiB (D=64), 128-144 KiB otherwise
   int64_t s = (kCUs * wg_per_cu + units - 1) / units;

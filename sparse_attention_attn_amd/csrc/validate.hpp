@@ -29,6 +29,11 @@ int check_attention_args(const char* fn, Op op, const attn_tensor_t& q, const at
 int check_num_splits(const char* fn, int num_splits, int Lk);
 
 // Split count heuristic for a 256-CU MI355X (pure function).
+// Query columns ((head, position) pairs of one KV head) per split-KV workgroup: 32 for the
+// MLA shape (Dqk = 576) with more than 16 columns, whose two 16-column blocks then share every
+// read of the latent cache; 16 otherwise.
+inline int split_cols(int dqk, int ncols) { return (dqk == 576 && ncols > 16) ? 32 : 16; }
+
 int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
 // Keys per split: 64 * ceil(ceil(Lk / S) / 64).

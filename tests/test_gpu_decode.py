@@ -6,7 +6,7 @@ import pytest
 
 from oracle import attention as A
 from tests.helpers import check_parity, say, to_f64
-from workloads import WORKLOADS, make_qkv, randn_bf16
+from workloads import ETAP_GRID, WORKLOADS, make_qkv, randn_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -152,3 +152,47 @@ def test_decode_deterministic():
     o1, l1 = _decode(q.to(DEV), k, k[..., :512], False, 192 ** -0.5)
     o2, l2 = _decode(q.to(DEV), k, k[..., :512], False, 192 ** -0.5)
     assert bool((o1 == o2).all()) and bool((l1 == l2).all())
+
+
+# ---- the FlashMLA-ETAP decode grid (MLA, 16 heads of dimension 576, one or two query tokens,
+# bottom-right causal): with two tokens the 32 query columns share one workgroup, so every
+# read of the latent cache feeds both 16-column MFMA blocks.
+
+def _etap(B, Lq, Lk, num_splits=None):
+    w = ETAP_GRID["etap_b16_q2_k512"]      # the grid's recipe at reduced sizes
+    q, k, _ = make_qkv(w, b=B, lq=Lq, lk=Lk)
+    kd = k.to(DEV)
+    o, lse = _decode(q.to(DEV), kd, kd[..., :512], True, w.scale, num_splits=num_splits)
+    kf = to_f64(k)
+    o_ref, lse_ref = A.attention(to_f64(q), kf, A.mla_value_view(kf, 512),
+                                 A.effective_scale(w.scale), True)
+    return o, lse, o_ref, lse_ref
+
+
+@pytest.mark.parametrize("shape", [(3, 2, 513), (3, 2, 2049), (3, 1, 2049), (2, 2, 40)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_etap_grid_reduced(shape):
+    B, Lq, Lk = shape
+    say(f"etap reduced B={B} Lq={Lq} Lk={Lk}")
+    o, lse, o_ref, lse_ref = _etap(B, Lq, Lk)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"etap{shape}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 47])
+def test_etap_split_invariance(splits):
+    say(f"etap split invariance S={splits}")
+    o, lse, o_ref, lse_ref = _etap(2, 2, 3000, num_splits=splits)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"etap splits={splits}")
+
+
+def test_etap_grid_point_full():
+    """A full grid point (batch 16, two query tokens, 16K keys), every output element."""
+    w = ETAP_GRID["etap_b16_q2_k16384"]
+    say(f"etap full {w}")
+    q, k, _ = make_qkv(w)
+    kd = k.to(DEV)
+    o, lse = _decode(q.to(DEV), kd, kd[..., :512], True, w.scale)
+    kf = to_f64(k)
+    o_ref, lse_ref = A.attention(to_f64(q), kf, A.mla_value_view(kf, 512),
+                                 A.effective_scale(w.scale), True)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "etap_b16_q2_k16384")

@@ -13,6 +13,12 @@ Recipe:
   blocks kb in [qb-63, qb] (diagonal included), each remaining causal block kb <= qb chosen
   independently with probability 0.03, and 1000 vertical key columns drawn uniformly without
   replacement over [0, L) per head. Lists are sorted and unique.
+* The MLA decode grid of the FlashMLA-ETAP page (section on experiments: DeepSeek-R1's 16
+  heads of dimension 576, batch sizes 16 and 32, KV lengths 512 to 64K; one or two query
+  tokens per the problem statement) uses the MLA recipe above with bottom-right causal
+  masking. Parity cases draw it on the host like every other workload. The timing sweep
+  draws it on the device (`randn_bf16_device`: a seeded device generator, same distribution
+  and rounding), because the largest points hold several GB.
 """
 
 from __future__ import annotations
@@ -29,6 +35,8 @@ __all__ = [
     "randn_bf16",
     "make_qkv",
     "make_blocksparse_lists",
+    "ETAP_GRID",
+    "randn_bf16_device",
     "sampled_rows",
     "dense_causal_lists",
 ]
@@ -65,6 +73,26 @@ WORKLOADS = {
                                  Dqk=128, Dv=128, causal=True, scale=1.0 / math.sqrt(128),
                                  kind="blocksparse"),
 }
+
+
+# FlashMLA-ETAP decode grid: (batch, query tokens, KV length) points of the MLA shape.
+ETAP_GRID = {}
+for _i, (_b, _lq, _lk) in enumerate((b, lq, lk) for b in (16, 32) for lq in (1, 2)
+                                    for lk in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536)):
+    _name = f"etap_b{_b}_q{_lq}_k{_lk}"
+    ETAP_GRID[_name] = Workload(_name, 100 + _i, B=_b, Hq=16, Hkv=1, Lq=_lq, Lk=_lk, Dqk=576,
+                                Dv=512, causal=True, scale=1.0 / math.sqrt(192),
+                                kind="mla_decode", mla=True)
+del _i, _b, _lq, _lk, _name
+
+
+def randn_bf16_device(shape, seed: int, device="cuda:0") -> torch.Tensor:
+    """float32 N(0,1) from a seeded generator on `device`, rounded to bf16 (RNE). For timing
+    inputs only: the values differ from randn_bf16's for the same seed."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device).to(
+        torch.bfloat16)
 
 
 def _gen(seed: int) -> torch.Generator:
