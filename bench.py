@@ -226,6 +226,59 @@ def bench_etap_grid(steps, warmup):
     return out
 
 
+def bench_memory(lengths, eager_max):
+    """Peak device memory of one causal prefill (B 1, Hq 32, Hkv 8, D 128) above its inputs and
+    outputs: attn_fwd's (it allocates nothing and keeps no S or P) against an eager attention
+    that materialises the scores (fp32 S = Q·Kᵀ, softmax, P·V in plain PyTorch). The eager one
+    is measured up to `eager_max` keys; its 2·Hq·L²·4 bytes of S and P are given beyond."""
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import randn_bf16_device
+    B, Hq, Hkv, D = 1, 32, 8, 128
+    scale = D ** -0.5
+    out = []
+    for L in lengths:
+        torch.cuda.empty_cache()
+        q = randn_bf16_device((B, L, Hq, D), 900 + L)
+        k = randn_bf16_device((B, L, Hkv, D), 901 + L)
+        v = randn_bf16_device((B, L, Hkv, D), 902 + L)
+        o = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda:0")
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        S.attn_fwd(q, k, v, o, lse, causal=True, scale=scale)
+        torch.cuda.synchronize()
+        ours = torch.cuda.max_memory_allocated() - base
+        io = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse))
+        rec = {"L": L, "inputs_outputs_bytes": int(io), "allocated_before_bytes": int(base),
+               "attn_fwd_extra_bytes": int(ours),
+               "eager_extra_bytes_formula": 2 * B * Hq * L * L * 4}
+        if L <= eager_max:
+            g = Hq // Hkv
+            qf = q.float().permute(0, 2, 1, 3).contiguous()
+            kf = k.float().repeat_interleave(g, dim=2).permute(0, 2, 3, 1).contiguous()
+            vf = v.float().repeat_interleave(g, dim=2).permute(0, 2, 1, 3).contiguous()
+            torch.cuda.synchronize()
+            base_e = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            s_ = torch.matmul(qf, kf)
+            s_.mul_(scale)
+            s_.masked_fill_(torch.ones(L, L, dtype=torch.bool, device="cuda:0").triu_(1),
+                            float("-inf"))
+            p_ = torch.softmax(s_, dim=-1)
+            del s_
+            oe = torch.matmul(p_, vf)
+            torch.cuda.synchronize()
+            rec["eager_extra_bytes_measured"] = int(torch.cuda.max_memory_allocated() - base_e)
+            del p_, oe, qf, kf, vf
+        out.append(rec)
+        log(f"  memory L={L}: {rec}")
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, budget_s):
     """The fp64 oracle, as it stands, timed on a bounded sample of the headline workload:
@@ -270,6 +323,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-etap-grid", action="store_true",
                     help="skip the FlashMLA-ETAP decode grid sweep")
+    ap.add_argument("--no-memory", action="store_true",
+                    help="skip the peak-memory comparison at long sequence lengths")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -351,6 +406,11 @@ def main():
         out["etap_grid"] = {"unit": "split-KV + combine per step; TFLOP/s = 2*(576+512) per "
                                     "visible (query, key) pair; GB/s = latent cache + Q + O + LSE",
                             "points": bench_etap_grid(max(5, args.steps // 2), 3)}
+    if not args.no_memory and args.only is None:
+        log("peak memory at long sequence lengths ...")
+        out["memory"] = {"op": "causal prefill B 1, Hq 32, Hkv 8, D 128",
+                         "points": bench_memory([4096, 8192, 16384, 32768, 65536, 131072],
+                                                eager_max=16384)}
     if not args.no_cpu_baseline and HEADLINE in res:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
