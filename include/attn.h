@@ -140,6 +140,46 @@ int attn_blocksparse_check(const int32_t* blk_ptr, const int32_t* blk_idx,
                            const int32_t* col_ptr, const int32_t* col_idx,
                            int B, int Hq, int Lq, int Lk, int block_m, int block_n);
 
+/*
+ * attn_build_sparse_index — builds, from Q and K, the block-sparse index lists that
+ * attn_fwd_blocksparse consumes (square causal sizes: Lq = Lk = L).
+ *
+ * The pages (MInference article, paragraphs on the three patterns and on dynamic sparse
+ * indices; "SparseAccelerate: Acelerando Modelos de Lenguaje", section "Patrones de Atención
+ * Dispersa Dinámicos") fix that the indices are built per head at run time by a fast
+ * approximation, and name no estimator. This library's estimator:
+ *   - blocks: each 64-row block of Q and of K is mean-pooled; causal key block kb <= qb scores
+ *     scale * <mean q_qb, mean k_kb>; query block qb lists its diagonal block and the top
+ *     (topk_blocks - 1) other causal blocks (ties to the lower id), i.e. min(topk_blocks, qb+1)
+ *     blocks, sorted ascending;
+ *   - columns: the last min(64, L) query rows each take a causal softmax over the keys; a
+ *     key's importance is the sum of its probabilities over those rows; the top
+ *     min(n_cols, L) keys (ties to the lower index) are listed, sorted ascending.
+ * The query head of KV head j are heads j*g .. j*g+g-1 (g = Hq / Hkv).
+ *
+ * Outputs (DEVICE int32 arrays owned by the caller; sizes from attn_sparse_index_sizes):
+ *   blk_ptr [B*Hq*ceil(L/64) + 1], blk_idx [n_blk_idx], col_ptr [B*Hq + 1], col_idx [n_col_idx]
+ *   (col_idx may be NULL when n_col_idx is 0).
+ * workspace: DEVICE buffer of at least attn_sparse_index_workspace_bytes bytes, 256-byte
+ * aligned, owned by the caller; its contents on entry do not matter.
+ * Limits: D in {64, 128}, L <= 131072, topk_blocks >= 1, n_cols >= 0, every list total below
+ * 2^31. Errors: INVALID_ARG for bad sizes, scale, pointers or alignment; UNSUPPORTED for D or
+ * L outside the limits; WORKSPACE for a missing or short workspace; LAUNCH for a launch
+ * failure. Nothing is launched on error.
+ */
+int attn_build_sparse_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int Hkv, int L, int D,
+                            float scale, int topk_blocks, int n_cols, int32_t* blk_ptr,
+                            int32_t* blk_idx, int32_t* col_ptr, int32_t* col_idx, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Entries of blk_idx and col_idx that attn_build_sparse_index writes for these sizes.
+ * Returns ATTN_OK, or INVALID_ARG for sizes < 1 (or n_cols < 0, topk_blocks < 1). */
+int attn_sparse_index_sizes(int B, int Hq, int L, int topk_blocks, int n_cols,
+                            int64_t* n_blk_idx, int64_t* n_col_idx);
+
+/* Workspace bytes attn_build_sparse_index needs (0 on invalid sizes). */
+size_t attn_sparse_index_workspace_bytes(int B, int Hq, int Hkv, int L, int D);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

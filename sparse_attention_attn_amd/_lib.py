@@ -24,6 +24,9 @@ EXPORTED_SYMBOLS = (
     "attn_combine_lse",
     "attn_fwd_blocksparse",
     "attn_blocksparse_check",
+    "attn_build_sparse_index",
+    "attn_sparse_index_sizes",
+    "attn_sparse_index_workspace_bytes",
     "attn_status_string",
     "attn_last_error",
 )
@@ -84,6 +87,14 @@ def load_library():
     lib.attn_fwd_blocksparse.restype = i32
     lib.attn_blocksparse_check.argtypes = [ip, ip, ip, ip, i32, i32, i32, i32, i32, i32]
     lib.attn_blocksparse_check.restype = i32
+    lib.attn_build_sparse_index.argtypes = [T, T, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp,
+                                            vp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_build_sparse_index.restype = i32
+    lib.attn_sparse_index_sizes.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i64),
+                                            ctypes.POINTER(i64)]
+    lib.attn_sparse_index_sizes.restype = i32
+    lib.attn_sparse_index_workspace_bytes.argtypes = [i32] * 5
+    lib.attn_sparse_index_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -251,3 +262,45 @@ def attn_blocksparse_check(blk_ptr, blk_idx, col_ptr, col_idx, B, Hq, Lq, Lk, bl
     st = load_library().attn_blocksparse_check(*ptrs, B, Hq, Lq, Lk, block_m, block_n)
     _check("attn_blocksparse_check", st)
     return st
+
+
+def attn_sparse_index_sizes(B, Hq, L, topk_blocks, n_cols):
+    """(entries of blk_idx, entries of col_idx) that attn_build_sparse_index writes."""
+    nb, nc = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = load_library().attn_sparse_index_sizes(B, Hq, L, topk_blocks, n_cols, ctypes.byref(nb),
+                                                ctypes.byref(nc))
+    _check("attn_sparse_index_sizes", st)
+    return nb.value, nc.value
+
+
+def attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D) -> int:
+    return int(load_library().attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D))
+
+
+def attn_build_sparse_index(q, k, topk_blocks, n_cols, scale=None, outputs=None, workspace=None,
+                            stream=None):
+    """Block and column lists (CSR, int32 GPU tensors: blk_ptr, blk_idx, col_ptr, col_idx) for
+    the block-sparse forward, built from Q [B, L, Hq, D] and K [B, L, Hkv, D] by the library's
+    estimator (see include/attn.h). Allocates the outputs and the workspace with torch unless
+    given."""
+    torch = _torch()
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = D ** -0.5
+    nb, nc = attn_sparse_index_sizes(B, Hq, L, topk_blocks, n_cols)
+    if outputs is None:
+        nqb = -(-L // 64)
+        mk = lambda n: torch.empty(max(int(n), 1), dtype=torch.int32, device=q.device)
+        outputs = (mk(B * Hq * nqb + 1), mk(nb), mk(B * Hq + 1), mk(nc))
+    blk_ptr, blk_idx, col_ptr, col_idx = outputs
+    wsb = attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    st = load_library().attn_build_sparse_index(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), B, Hq, Hkv, L, D, float(scale),
+        int(topk_blocks), int(n_cols), _int_ptr(blk_ptr, "blk_ptr"), _int_ptr(blk_idx, "blk_idx"),
+        _int_ptr(col_ptr, "col_ptr"), _int_ptr(col_idx, "col_idx"),
+        ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(stream, q.device))
+    _check("attn_build_sparse_index", st)
+    return blk_ptr, blk_idx[:nb], col_ptr, col_idx[:nc]

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
-SOURCES = ["fwd_dense.hip", "fwd_blocksparse.hip", "fwd_splitkv.hip", "api.cpp", "validate.cpp"]
+SOURCES = ["fwd_dense.hip", "fwd_blocksparse.hip", "fwd_splitkv.hip", "sparse_index.hip", "api.cpp",
+           "validate.cpp"]
 ARCH = "gfx950"
 # Per-source extra flags for the dense kernel:
 #  * no IEEE mode and no NaN semantics: its row maxima then lower to plain v_max3_f32 with no

@@ -172,6 +172,58 @@ int attn_blocksparse_check(const int32_t* blk_ptr, const int32_t* blk_idx, const
                                        col_idx, B, Hq, Lq, Lk, block_m, block_n);
 }
 
+int attn_build_sparse_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int Hkv, int L, int D,
+                            float scale, int topk_blocks, int n_cols, int32_t* blk_ptr,
+                            int32_t* blk_idx, int32_t* col_ptr, int32_t* col_idx, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_build_sparse_index";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_index_args(fn, q, k, B, Hq, Hkv, L, D, scale, topk_blocks, n_cols,
+                                    blk_ptr, blk_idx, col_ptr, col_idx, workspace,
+                                    workspace_bytes);
+    if (st != ATTN_OK) return st;
+    const attn::IndexWorkspace ws = attn::index_workspace(B, Hq, Hkv, L, D);
+    char* wb = static_cast<char*>(workspace);
+    attn::IndexArgs a;
+    a.q = static_cast<const uint16_t*>(q.data);
+    a.k = static_cast<const uint16_t*>(k.data);
+    a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
+    a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L;
+    a.scale = scale;
+    a.sl2 = scale * kLog2e;
+    a.topk = topk_blocks;
+    a.ncols = n_cols;
+    a.blk_ptr = blk_ptr; a.blk_idx = blk_idx; a.col_ptr = col_ptr; a.col_idx = col_idx;
+    a.blk_head_len = attn::index_blk_head_len(L, topk_blocks);
+    a.blk_total = (int64_t)B * Hq * a.blk_head_len;
+    a.qbar = reinterpret_cast<float*>(wb + ws.qbar);
+    a.kbar = reinterpret_cast<float*>(wb + ws.kbar);
+    a.stats = reinterpret_cast<float*>(wb + ws.stats);
+    a.imp = reinterpret_cast<float*>(wb + ws.imp);
+    return launch_status(fn, attn::launch_build_index(a, D, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_sparse_index_sizes(int B, int Hq, int L, int topk_blocks, int n_cols, int64_t* n_blk_idx,
+                            int64_t* n_col_idx) {
+  attn::clear_last_error();
+  if (B < 1 || Hq < 1 || L < 1 || topk_blocks < 1 || n_cols < 0)
+    return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sparse_index_sizes", "invalid sizes");
+  if (n_blk_idx != nullptr) *n_blk_idx = (int64_t)B * Hq * attn::index_blk_head_len(L, topk_blocks);
+  if (n_col_idx != nullptr) *n_col_idx = (int64_t)B * Hq * (n_cols < L ? n_cols : L);
+  return ATTN_OK;
+}
+
+size_t attn_sparse_index_workspace_bytes(int B, int Hq, int Hkv, int L, int D) {
+  return attn::index_workspace(B, Hq, Hkv, L, D).total;
+}
+
 const char* attn_status_string(int status) { return attn::status_string(status); }
 
 const char* attn_last_error(void) { return attn::last_error_cstr(); }

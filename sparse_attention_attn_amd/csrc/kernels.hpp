@@ -59,7 +59,38 @@ struct CombineArgs {
   int B, Hq, Lq, S;
 };
 
+// Dynamic sparse-index builder (square causal sizes, L = Lq = Lk).
+struct IndexArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t q_sb, q_sl, q_sh;
+  int64_t k_sb, k_sl, k_sh;
+  int B, Hq, Hkv, L;
+  float scale;         // score scale of the pooled block scores
+  float sl2;           // scale * log2(e): probe scores in the exp2 domain
+  int topk;            // blocks listed per query block (at most; the diagonal included)
+  int ncols;           // vertical columns listed per head (at most L)
+  int32_t* blk_ptr;    // [B*Hq*nqb + 1]
+  int32_t* blk_idx;    // [blk_total]
+  int32_t* col_ptr;    // [B*Hq + 1]
+  int32_t* col_idx;    // [B*Hq*min(ncols, L)]
+  int64_t blk_head_len;  // block-list entries per head
+  int64_t blk_total;     // B*Hq*blk_head_len
+  float* qbar;         // workspace: pooled Q [B, Hq, nqb, D]
+  float* kbar;         // workspace: pooled K [B, Hkv, nqb, D]
+  float* stats;        // workspace: probe softmax statistics [B, Hq, nchunks, 64, 2]
+  float* imp;          // workspace: column importance [B, Hq, L]
+};
+
+// Rows per pooled block, the largest block count one list builder workgroup sorts, probe rows,
+// keys per probe workgroup.
+constexpr int kIndexBlock = 64;
+constexpr int kIndexMaxBlocks = 2048;
+constexpr int kProbeRows = 64;
+constexpr int kProbeChunk = 1024;
+
 hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_build_index(const IndexArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);

@@ -212,6 +212,76 @@ int check_blocksparse_lists(const char* fn, const int32_t* blk_ptr, const int32_
   return ATTN_OK;
 }
 
+int64_t index_blk_head_len(int L, int topk) {
+  if (L < 1 || topk < 1) return 0;
+  const int64_t nqb = (L + 63) / 64;
+  if (nqb <= topk) return nqb * (nqb + 1) / 2;
+  return (int64_t)topk * (topk + 1) / 2 + (nqb - topk) * (int64_t)topk;
+}
+
+IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D) {
+  IndexWorkspace w{0, 0, 0, 0, 0};
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return w;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t nqb = (size_t)(L + 63) / 64;
+  const size_t nch = (size_t)(L + 1023) / 1024;
+  size_t off = 0;
+  w.qbar = off; off = up(off + (size_t)B * Hq * nqb * D * 4);
+  w.kbar = off; off = up(off + (size_t)B * Hkv * nqb * D * 4);
+  w.stats = off; off = up(off + (size_t)B * Hq * nch * 64 * 2 * 4);
+  w.imp = off; off = up(off + (size_t)B * Hq * L * 4);
+  w.total = off;
+  return w;
+}
+
+int check_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k, int B, int Hq,
+                     int Hkv, int L, int D, float scale, int topk, int ncols,
+                     const int32_t* blk_ptr, const int32_t* blk_idx, const int32_t* col_ptr,
+                     const int32_t* col_idx, const void* workspace, size_t workspace_bytes) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1) {
+    std::ostringstream s;
+    s << "sizes must be >= 1 (B=" << B << " Hq=" << Hq << " Hkv=" << Hkv << " L=" << L << ")";
+    return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+  }
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, fn, "Hq must be a multiple of Hkv");
+  if (topk < 1) return fail(ATTN_ERR_INVALID_ARG, fn, "topk_blocks must be >= 1");
+  if (ncols < 0) return fail(ATTN_ERR_INVALID_ARG, fn, "n_cols must be >= 0");
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, fn, "scale is not finite");
+  if (D != 64 && D != 128) {
+    std::ostringstream s;
+    s << "D=" << D << " not supported (64, 128)";
+    return fail(ATTN_ERR_UNSUPPORTED, fn, s.str());
+  }
+  if (L > kIndexMaxL) {
+    std::ostringstream s;
+    s << "L=" << L << " exceeds the index builder's limit of " << kIndexMaxL;
+    return fail(ATTN_ERR_UNSUPPORTED, fn, s.str());
+  }
+  int st;
+  if ((st = check_tensor(fn, "q", q)) != ATTN_OK) return st;
+  if ((st = check_tensor(fn, "k", k)) != ATTN_OK) return st;
+  const int64_t nblk = (int64_t)B * Hq * index_blk_head_len(L, topk);
+  const int64_t ncol = (int64_t)B * Hq * std::min(ncols, L);
+  const int64_t nptr = (int64_t)B * Hq * ((L + 63) / 64) + 1;
+  const int64_t imax = std::numeric_limits<int32_t>::max();
+  if (nblk > imax || ncol > imax || nptr > imax)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "an index list would exceed 2^31 entries");
+  if (blk_ptr == nullptr || blk_idx == nullptr || col_ptr == nullptr ||
+      (ncol > 0 && col_idx == nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "an output list pointer is NULL");
+  if (!aligned4(blk_ptr) || !aligned4(blk_idx) || !aligned4(col_ptr) ||
+      (col_idx != nullptr && !aligned4(col_idx)))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "output lists must be 4-byte aligned");
+  const size_t need = index_workspace(B, Hq, Hkv, L, D).total;
+  if (workspace == nullptr || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) {
+    std::ostringstream s;
+    s << "workspace must be non-NULL, 256-byte aligned and at least " << need << " bytes";
+    return fail(ATTN_ERR_WORKSPACE, fn, s.str());
+  }
+  return ATTN_OK;
+}
+
 const char* status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";

@@ -55,6 +55,20 @@ constexpr int64_t kMaxStrideL = int64_t(1) << 24;
 // Largest key length the block-sparse kernel's listed-block bitmap covers.
 constexpr int kSparseMaxLk = 1 << 20;
 
+// Dynamic sparse-index builder (square causal sizes L = Lq = Lk).
+constexpr int kIndexMaxL = 131072;  // 2048 key blocks: one builder workgroup sorts them in LDS
+// Block-list entries per head: sum over query blocks qb of min(topk, qb + 1).
+int64_t index_blk_head_len(int L, int topk);
+// Workspace layout (byte offsets, 256-byte aligned) and total size.
+struct IndexWorkspace {
+  size_t qbar, kbar, stats, imp, total;
+};
+IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D);
+int check_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k, int B, int Hq,
+                     int Hkv, int L, int D, float scale, int topk, int ncols,
+                     const int32_t* blk_ptr, const int32_t* blk_idx, const int32_t* col_ptr,
+                     const int32_t* col_idx, const void* workspace, size_t workspace_bytes);
+
 const char* status_string(int status);
 
 }  // namespace attn

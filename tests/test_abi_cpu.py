@@ -162,6 +162,44 @@ def test_blocksparse_check_rejects(mutate, frag):
     assert frag in str(e.value)
 
 
+def _build_index(B=1, Hq=4, Hkv=2, L=1000, D=128, scale=0.1, topk=8, ncols=16, ws=FAKE,
+                 ws_bytes=None, ptrs=(FAKE, FAKE, FAKE, FAKE), q=None):
+    if ws_bytes is None:
+        ws_bytes = S.attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D)
+    return _lib().attn_build_sparse_index(q or _t(), _t(), B, Hq, Hkv, L, D, ctypes.c_float(scale),
+                                          topk, ncols, *ptrs, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, code, frag", [
+    (dict(B=0), S.ATTN_ERR_INVALID_ARG, "sizes must be"),
+    (dict(Hq=3), S.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(topk=0), S.ATTN_ERR_INVALID_ARG, "topk_blocks"),
+    (dict(ncols=-1), S.ATTN_ERR_INVALID_ARG, "n_cols"),
+    (dict(scale=float("inf")), S.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(D=96), S.ATTN_ERR_UNSUPPORTED, "D=96"),
+    (dict(L=131073), S.ATTN_ERR_UNSUPPORTED, "limit"),
+    (dict(ptrs=(FAKE, None, FAKE, FAKE)), S.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(ptrs=(FAKE, FAKE + 2, FAKE, FAKE)), S.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(ws=None), S.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=1024), S.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(ws=FAKE + 16), S.ATTN_ERR_WORKSPACE, "256-byte"),
+    (dict(q=_t(sl=4 * 128 + 3)), S.ATTN_ERR_INVALID_ARG, "multiples of 8"),
+])
+def test_build_sparse_index_validation(kw, code, frag):
+    assert _build_index(**kw) == code
+    assert frag in S.attn_last_error()
+
+
+def test_sparse_index_sizes_closed_form():
+    # L = 1000: 16 query blocks; topk 8 -> 1+2+...+8 + 8*8 = 100 entries per head
+    nb, nc = S.attn_sparse_index_sizes(2, 4, 1000, 8, 16)
+    assert (nb, nc) == (2 * 4 * 100, 2 * 4 * 16)
+    nb, nc = S.attn_sparse_index_sizes(1, 1, 100, 50, 500)   # 2 blocks; columns capped at L
+    assert (nb, nc) == (3, 100)
+    assert S.attn_sparse_index_workspace_bytes(1, 4, 2, 1000, 128) > 0
+    assert S.attn_sparse_index_workspace_bytes(0, 4, 2, 1000, 128) == 0
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     import sparse_attention_attn_amd._lib as L
     monkeypatch.setattr(L, "_LIB", None)

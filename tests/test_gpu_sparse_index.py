@@ -1,0 +1,159 @@
+"""GPU parity of attn_build_sparse_index (the dynamic block / column list builder) against the
+fp64 oracle in oracle/sparse_index.py, through the C ABI.
+
+The lists are index work decided by floating point (a top-k of scores), and the kernel ranks in
+fp32 what the oracle ranks in fp64. So each list is compared as a set: equal to the oracle's,
+or, where the two differ, every swapped element must sit at a near-tie of the oracle's ranking
+(within TOL of the k-th score), which is the only place rounding can move a top-k. The block
+offsets (blk_ptr, col_ptr) are closed-form and compared exactly, and the list order (ascending)
+is checked as is.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import sparse_index as X
+from tests.helpers import check_parity, say, to_f64
+from workloads import WORKLOADS, make_qkv, randn_bf16
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-4          # relative to (1 + |k-th score|): fp32 pooling and dot products vs fp64
+
+
+def _build(q, k, topk, ncols, scale):
+    import torch
+    import sparse_attention_attn_amd as S
+    out = S.attn_build_sparse_index(q.to(DEV), k.to(DEV), topk, ncols, scale=scale)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def _check_topk_set(got, ref, scores, k_sel, forced, label):
+    """got / ref: ascending id arrays; scores: oracle scores over the candidate ids."""
+    assert np.all(np.diff(got) > 0), f"{label}: list not strictly ascending: {got}"
+    if np.array_equal(got, ref):
+        return
+    assert got.size == ref.size, f"{label}: {got.size} ids, oracle {ref.size}"
+    cand = [i for i in ref if i not in forced]
+    kth = min(scores[i] for i in cand) if cand else np.inf
+    tol = TOL * (1.0 + abs(kth))
+    for i in set(got) ^ set(ref):
+        assert abs(scores[i] - kth) <= tol, (
+            f"{label}: id {i} (score {scores[i]:.6g}) differs from the oracle's choice away from "
+            f"a near-tie (k-th score {kth:.6g})")
+
+
+def _compare(q, k, topk, ncols, scale, label):
+    B, L, Hq, D = q.shape
+    nqb = -(-L // 64)
+    bp, bi, cp, ci = _build(q, k, topk, ncols, scale)
+    rbp, rbi, rcp, rci, scores, imp = X.build_index(to_f64(q), to_f64(k), float(np.float32(scale)),
+                                                     topk, ncols)
+    assert np.array_equal(bp, rbp), f"{label}: blk_ptr"
+    assert np.array_equal(cp, rcp), f"{label}: col_ptr"
+    for b in range(B):
+        for h in range(Hq):
+            for qb in range(nqb):
+                r = (b * Hq + h) * nqb + qb
+                _check_topk_set(bi[bp[r]:bp[r + 1]], rbi[rbp[r]:rbp[r + 1]], scores[b, h, qb],
+                                topk - 1, {qb}, f"{label} b={b} h={h} qb={qb}")
+            r = b * Hq + h
+            _check_topk_set(ci[cp[r]:cp[r + 1]], rci[rcp[r]:rcp[r + 1]], imp[b, h], ncols, set(),
+                            f"{label} columns b={b} h={h}")
+    return bp, bi, cp, ci
+
+
+SHAPES = [
+    # B, Hq, Hkv, L, D, topk, ncols
+    (1, 4, 2, 64, 128, 4, 10),        # one query block
+    (2, 4, 2, 200, 128, 2, 30),       # ragged last block, GQA
+    (1, 2, 1, 1000, 64, 5, 100),      # D = 64
+    (1, 4, 4, 2049, 128, 40, 5000),   # more columns than keys: all keys listed
+    (1, 8, 2, 3000, 128, 1, 0),       # diagonal only, no columns
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_build_index_matches_oracle(shape):
+    B, Hq, Hkv, L, D, topk, ncols = shape
+    say(f"sparse index {shape}")
+    q = randn_bf16((B, L, Hq, D), 9100 + L)
+    k = randn_bf16((B, L, Hkv, D), 9101 + L)
+    _compare(q, k, topk, ncols, D ** -0.5, f"index{shape}")
+
+
+def test_build_index_planted_structure():
+    """Planted key blocks and columns that the estimator must find (far from any tie)."""
+    B, Hq, Hkv, L, D = 1, 2, 1, 1024, 128
+    say("sparse index planted")
+    q = randn_bf16((B, L, Hq, D), 9200).float()
+    k = randn_bf16((B, L, Hkv, D), 9201).float() * 0.2
+    qm = q[0, 15 * 64:16 * 64, 0].mean(0)
+    k[0, 3 * 64:4 * 64, 0] = 8.0 * qm / qm.norm()          # block 3 for query block 15 of head 0
+    pm = q[0, L - 64:, 1].mean(0)
+    k[0, 500, 0] = 40.0 * pm / pm.dot(pm)                  # column 500 for head 1's probe
+    q, k = q.bfloat16(), k.bfloat16()
+    bp, bi, cp, ci = _compare(q, k, 2, 5, D ** -0.5, "planted")
+    assert list(bi[bp[15]:bp[16]]) == [3, 15]
+    assert 500 in list(ci[cp[1]:cp[2]])
+
+
+def test_build_index_deterministic():
+    say("sparse index determinism")
+    q = randn_bf16((1, 3000, 8, 128), 9300)
+    k = randn_bf16((1, 3000, 2, 128), 9301)
+    a = _build(q, k, 16, 200, 0.09)
+    b = _build(q, k, 16, 200, 0.09)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_built_lists_drive_blocksparse_forward():
+    """The builder's lists, fed to attn_fwd_blocksparse, give the oracle's attention over the
+    same lists."""
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Hq, Hkv, L, D = 1, 4, 2, 1500, 128
+    say("sparse index -> blocksparse forward")
+    q = randn_bf16((B, L, Hq, D), 9400)
+    k = randn_bf16((B, L, Hkv, D), 9401)
+    v = randn_bf16((B, L, Hkv, D), 9402)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lists = S.attn_build_sparse_index(qd, kd, 6, 50, scale=D ** -0.5)
+    o = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
+    S.attn_fwd_blocksparse(qd, kd, vd, o, *lists, lse=lse, causal=True, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    bp, bi, cp, ci = [t.cpu().numpy() for t in lists]
+    S.attn_blocksparse_check(bp, bi, cp, ci, B, Hq, L, L)
+    allowed = A.csr_allowed_fn(bp, bi, cp, ci, Hq, -(-L // 64), L)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
+                                 True, allowed_fn=allowed)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "index->blocksparse")
+
+
+def test_build_index_full_size_sampled():
+    """The 128K block-sparse workload's shape (B 1, Hq 32, Hkv 8, L 131072, D 128), 96 blocks
+    per query block and 1000 columns per head: two heads checked against the oracle, every
+    query block of them plus their column lists."""
+    w = WORKLOADS["blocksparse_128k"]
+    say(f"sparse index full size {w.name}")
+    q, k, _ = make_qkv(w)
+    topk, ncols = 96, 1000
+    bp, bi, cp, ci = _build(q, k, topk, ncols, w.scale)
+    nqb = -(-w.Lq // 64)
+    sc = float(np.float32(w.scale))
+    for h in (0, 29):
+        qh = q[0, :, h].double().numpy()
+        kh = k[0, :, h // (w.Hq // w.Hkv)].double().numpy()
+        scores = X.block_scores(qh, kh, sc, 64)
+        for qb in range(nqb):
+            r = h * nqb + qb
+            ref = X.select_blocks(scores[qb], qb, topk)
+            _check_topk_set(bi[bp[r]:bp[r + 1]], ref, scores[qb], topk - 1, {qb},
+                            f"full h={h} qb={qb}")
+        imp = X.probe_importance(qh, kh, sc, 64)
+        _check_topk_set(ci[cp[h]:cp[h + 1]], X.select_columns(imp, ncols), imp, ncols, set(),
+                        f"full columns h={h}")
