@@ -171,8 +171,35 @@ def bench_blocksparse(w, steps, warmup):
     pairs = blocksparse_pairs(lists, w.B, w.Hq, w.Lq)
     flops = 2 * (w.Dqk + w.Dv) * pairs
     dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
-    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
-            "density_vs_causal": pairs / dense}
+    res = {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+           "density_vs_causal": pairs / dense}
+    # The same attention with lists built from Q and K at run time (attn_build_sparse_index:
+    # 96 blocks per query block, 1000 columns per head, about the synthetic lists' density).
+    topk, ncols = 96, 1000
+    nb, nc = S.attn_sparse_index_sizes(w.B, w.Hq, w.Lq, topk, ncols)
+    nqb = -(-w.Lq // 64)
+    outs = (torch.empty(w.B * w.Hq * nqb + 1, dtype=torch.int32, device="cuda:0"),
+            torch.empty(nb, dtype=torch.int32, device="cuda:0"),
+            torch.empty(w.B * w.Hq + 1, dtype=torch.int32, device="cuda:0"),
+            torch.empty(nc, dtype=torch.int32, device="cuda:0"))
+    ws = torch.empty(S.attn_sparse_index_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Dqk),
+                     dtype=torch.uint8, device="cuda:0")
+    build = lambda: S.attn_build_sparse_index(q, k, topk, ncols, scale=w.scale, outputs=outs,
+                                              workspace=ws)
+    ms_b, _ = time_steps(build, steps, warmup)
+    built = build()
+    torch.cuda.synchronize()
+    step_d = lambda: (build(), S.attn_fwd_blocksparse(q, k, v, o, *built, lse=lse, causal=True,
+                                                      scale=w.scale))
+    ms_d, _ = time_steps(step_d, steps, warmup)
+    hl = [t.cpu().numpy() for t in built]
+    pairs_d = blocksparse_pairs(hl, w.B, w.Hq, w.Lq)
+    flops_d = 2 * (w.Dqk + w.Dv) * pairs_d
+    res["dynamic"] = {"index_build_ms": round(ms_b, 4), "build_plus_attention_ms": round(ms_d, 4),
+                      "topk_blocks": topk, "n_cols": ncols,
+                      "density_vs_causal": round(pairs_d / dense, 4),
+                      "tflops_incl_build": round(flops_d / (ms_d * 1e-3) / 1e12, 3)}
+    return res
 
 
 def mla_causal_pairs(lq, lk):
@@ -400,6 +427,8 @@ def main():
                         "flops": r["flops"]}
             if "density_vs_causal" in r:
                 wl[name]["density_vs_causal"] = round(r["density_vs_causal"], 4)
+            if "dynamic" in r:
+                wl[name]["dynamic_index"] = r["dynamic"]
     out["workloads"] = wl
     if not args.no_etap_grid and args.only is None:
         log("FlashMLA-ETAP decode grid ...")

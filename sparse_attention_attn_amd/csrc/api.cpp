@@ -201,6 +201,7 @@ int attn_build_sparse_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int
     a.qbar = reinterpret_cast<float*>(wb + ws.qbar);
     a.kbar = reinterpret_cast<float*>(wb + ws.kbar);
     a.stats = reinterpret_cast<float*>(wb + ws.stats);
+    a.fin = reinterpret_cast<float*>(wb + ws.fin);
     a.imp = reinterpret_cast<float*>(wb + ws.imp);
     return launch_status(fn, attn::launch_build_index(a, D, static_cast<hipStream_t>(stream)));
   } catch (const std::exception& e) {

@@ -77,8 +77,9 @@ struct IndexArgs {
   int64_t blk_head_len;  // block-list entries per head
   int64_t blk_total;     // B*Hq*blk_head_len
   float* qbar;         // workspace: pooled Q [B, Hq, nqb, D]
-  float* kbar;         // workspace: pooled K [B, Hkv, nqb, D]
+  float* kbar;         // workspace: pooled K, transposed [B, Hkv, D, nqb]
   float* stats;        // workspace: probe softmax statistics [B, Hq, nchunks, 64, 2]
+  float* fin;          // workspace: per probe row, max + log2(sum) over all keys [B, Hq, 64]
   float* imp;          // workspace: column importance [B, Hq, L]
 };
 

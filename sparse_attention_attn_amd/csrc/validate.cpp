@@ -220,7 +220,7 @@ int64_t index_blk_head_len(int L, int topk) {
 }
 
 IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D) {
-  IndexWorkspace w{0, 0, 0, 0, 0};
+  IndexWorkspace w{0, 0, 0, 0, 0, 0};
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return w;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t nqb = (size_t)(L + 63) / 64;
@@ -229,6 +229,7 @@ IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D) {
   w.qbar = off; off = up(off + (size_t)B * Hq * nqb * D * 4);
   w.kbar = off; off = up(off + (size_t)B * Hkv * nqb * D * 4);
   w.stats = off; off = up(off + (size_t)B * Hq * nch * 64 * 2 * 4);
+  w.fin = off; off = up(off + (size_t)B * Hq * 64 * 4);
   w.imp = off; off = up(off + (size_t)B * Hq * L * 4);
   w.total = off;
   return w;

@@ -61,7 +61,7 @@ constexpr int kIndexMaxL = 131072;  // 2048 key blocks: one builder workgroup so
 int64_t index_blk_head_len(int L, int topk);
 // Workspace layout (byte offsets, 256-byte aligned) and total size.
 struct IndexWorkspace {
-  size_t qbar, kbar, stats, imp, total;
+  size_t qbar, kbar, stats, fin, imp, total;
 };
 IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D);
 int check_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k, int B, int Hq,

@@ -157,3 +157,34 @@ def test_build_index_full_size_sampled():
         imp = X.probe_importance(qh, kh, sc, 64)
         _check_topk_set(ci[cp[h]:cp[h + 1]], X.select_columns(imp, ncols), imp, ncols, set(),
                         f"full columns h={h}")
+
+
+def test_build_index_exact_ties_take_lowest_ids():
+    """Every key row equal: the pooled block scores are bitwise equal (the sums of equal bf16
+    values are exact in fp32), so the lists are exact ties, broken toward the lowest ids. The
+    probe importance is flat over the keys every probe row sees, so the column list is the
+    lowest indices."""
+    import torch
+    B, Hq, Hkv, L, D, topk, ncols = 1, 4, 2, 1000, 128, 5, 40
+    say("sparse index exact ties")
+    q = randn_bf16((B, L, Hq, D), 9500)
+    k = randn_bf16((1, 1, Hkv, D), 9501).expand(B, L, Hkv, D).contiguous()
+    bp, bi, cp, ci = _build(q, k, topk, ncols, D ** -0.5)
+    rbp, rbi, rcp, rci, _, _ = X.build_index(to_f64(q), to_f64(k), float(np.float32(D ** -0.5)),
+                                             topk, ncols)
+    assert np.array_equal(bp, rbp) and np.array_equal(bi, rbi)
+    assert np.array_equal(cp, rcp) and np.array_equal(ci, rci)
+    nqb = -(-L // 64)
+    for h in range(Hq):
+        for qb in range(nqb):
+            r = h * nqb + qb
+            assert list(bi[bp[r]:bp[r + 1]]) == sorted(set(range(min(topk - 1, qb))) | {qb})
+        assert list(ci[cp[h]:cp[h + 1]]) == list(range(ncols))
+
+
+def test_build_index_negative_scale():
+    """A negative scale reverses the ranking of the block scores and of the probe scores."""
+    say("sparse index negative scale")
+    q = randn_bf16((1, 1500, 4, 128), 9600)
+    k = randn_bf16((1, 1500, 2, 128), 9601)
+    _compare(q, k, 6, 80, -0.08, "negative scale")
