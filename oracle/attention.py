@@ -28,7 +28,9 @@ What it computes is the plain definition that every page reaches exactly, only f
   "SparseAccelerate: Acelerando Modelos de Lenguaje", section "Patrones de Atención Dispersa
   Dinámicos": per-head sparse patterns. Reading taken: per query head, a list of 64x64 key
   blocks per 64-row query block plus a list of vertical key columns; the visible set is the
-  union of both, intersected with the causal mask, each key counted once.
+  union of both, intersected with the causal mask, each key counted once. The vertical-slash
+  pattern adds per-head slash lines: diagonals at listed offsets below the causal diagonal,
+  joined to the same union (`slash_row_mask`).
 
 Readings where the pages are silent (each listed again with its reason in the design notes):
 causal alignment is bottom-right (query i sees key j iff j <= i + Lk - Lq); the log-sum-exp is
@@ -273,6 +275,41 @@ def csr_allowed_fn(blk_ptr, blk_idx, col_ptr, col_idx, hq, nqb, lk, block_m=64, 
         c = (b * hq + h)
         return blocksparse_row_mask(rows, lk, blocks_of_qb, col_idx[col_ptr[c]:col_ptr[c + 1]],
                                     block_m, block_n)
+
+    return fn
+
+
+def slash_row_mask(rows, lq, lk, offsets):
+    """Visible-key mask [len(rows), Lk] of the slash lines of one (batch, query head).
+
+    A slash line at offset o >= 0 is the diagonal o keys below the causal one: query row i sees
+    key i + (Lk - Lq) - o when that key exists (MInference article, paragraph on the
+    vertical-slash pattern; reading: the diagonal is bottom-right aligned like the causal mask,
+    offsets are counted downward from it). Built by scattering each listed diagonal into the
+    mask, one offset at a time.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, lk), dtype=bool)
+    for o in np.asarray(offsets, dtype=np.int64):
+        keys = rows + (lk - lq) - o
+        ok = (o >= 0) & (keys >= 0) & (keys < lk)
+        out[np.nonzero(ok)[0], keys[ok]] = True
+    return out
+
+
+def vslash_allowed_fn(blk_ptr, blk_idx, col_ptr, col_idx, sl_ptr, sl_idx, hq, nqb, lq, lk,
+                      block_m=64, block_n=64):
+    """Adapter like `csr_allowed_fn`, with per-head slash offsets added to the union:
+    sl_ptr has B*Hq + 1 entries over (b, h); sl_idx holds the offsets."""
+    blocks_cols = csr_allowed_fn(blk_ptr, blk_idx, col_ptr, col_idx, hq, nqb, lk, block_m,
+                                 block_n)
+    sl_ptr = np.asarray(sl_ptr, np.int64)
+    sl_idx = np.asarray(sl_idx, np.int64)
+
+    def fn(b, h, rows):
+        c = b * hq + h
+        return blocks_cols(b, h, rows) | slash_row_mask(rows, lq, lk,
+                                                        sl_idx[sl_ptr[c]:sl_ptr[c + 1]])
 
     return fn
 
