@@ -133,6 +133,41 @@ int attn_fwd_blocksparse(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn
                          const int32_t* blk_ptr, const int32_t* blk_idx,
                          const int32_t* col_ptr, const int32_t* col_idx, void* stream);
 
+/*
+ * attn_fwd_vertical_slash — attn_fwd_blocksparse with per-head slash lines added to the union
+ * (the vertical-slash pattern of the MInference article, paragraph on the three patterns).
+ * A slash line at offset o >= 0 is the diagonal o keys below the causal one: query row i
+ * sees key i + (Lk - Lq) - o when that key exists. A key visible through a listed block, a
+ * listed column and a slash line at once is counted once.
+ *
+ *   blk_ptr, blk_idx, col_ptr, col_idx — as attn_fwd_blocksparse (pass all-zero pointer
+ *       arrays for no blocks or no columns).
+ *   slash_ptr [B·Hq + 1], slash_idx — CSR over (b, h): sorted unique offsets in [0, Lk).
+ *       DEVICE int32; slash_idx may be NULL only when every list is empty. Offsets outside
+ *       [0, Lk) are ignored on the device; attn_vertical_slash_check validates host copies.
+ *   workspace — DEVICE buffer of at least attn_vertical_slash_workspace_bytes(B, Hq, Lk)
+ *       bytes, 256-byte aligned, owned by the caller; it receives two per-head bitmaps (the
+ *       offsets and the columns) and holds nothing between calls.
+ * Errors: as attn_fwd_blocksparse, plus INVALID_ARG when slash_ptr is NULL and WORKSPACE for
+ * a missing, short or misaligned workspace.
+ */
+int attn_fwd_vertical_slash(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                            float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                            int causal, float scale, const int32_t* blk_ptr,
+                            const int32_t* blk_idx, const int32_t* col_ptr,
+                            const int32_t* col_idx, const int32_t* slash_ptr,
+                            const int32_t* slash_idx, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes of attn_fwd_vertical_slash (0 for sizes < 1). */
+size_t attn_vertical_slash_workspace_bytes(int B, int Hq, int Lk);
+
+/* Validates slash lists given as HOST pointers: slash_ptr[0] = 0 and monotone, offsets sorted
+ * strictly ascending inside each head, in [0, Lk). Returns ATTN_OK or ATTN_ERR_INVALID_ARG
+ * with a message naming the first bad entry. Touches no GPU. */
+int attn_vertical_slash_check(const int32_t* slash_ptr, const int32_t* slash_idx, int B, int Hq,
+                              int Lk);
+
 /* Validates block-sparse index lists given as HOST pointers (same layout as above):
  * monotone pointers starting at 0, sorted unique ids, ids in range. Returns ATTN_OK or
  * ATTN_ERR_INVALID_ARG with a message naming the first bad entry. Touches no GPU. */

@@ -26,6 +26,9 @@ from ._lib import (  # noqa: F401
     attn_splitkv_num_splits,
     attn_splitkv_workspace_bytes,
     attn_blocksparse_check,
+    attn_fwd_vertical_slash,
+    attn_vertical_slash_workspace_bytes,
+    attn_vertical_slash_check,
     attn_build_sparse_index,
     attn_sparse_index_sizes,
     attn_sparse_index_workspace_bytes,

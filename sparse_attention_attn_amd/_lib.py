@@ -24,6 +24,9 @@ EXPORTED_SYMBOLS = (
     "attn_combine_lse",
     "attn_fwd_blocksparse",
     "attn_blocksparse_check",
+    "attn_fwd_vertical_slash",
+    "attn_vertical_slash_workspace_bytes",
+    "attn_vertical_slash_check",
     "attn_build_sparse_index",
     "attn_sparse_index_sizes",
     "attn_sparse_index_workspace_bytes",
@@ -87,6 +90,14 @@ def load_library():
     lib.attn_fwd_blocksparse.restype = i32
     lib.attn_blocksparse_check.argtypes = [ip, ip, ip, ip, i32, i32, i32, i32, i32, i32]
     lib.attn_blocksparse_check.restype = i32
+    lib.attn_fwd_vertical_slash.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, f32, ip, ip, ip, ip, ip, ip, vp,
+                                            ctypes.c_size_t, vp]
+    lib.attn_fwd_vertical_slash.restype = i32
+    lib.attn_vertical_slash_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.attn_vertical_slash_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_vertical_slash_check.argtypes = [ip, ip, i32, i32, i32]
+    lib.attn_vertical_slash_check.restype = i32
     lib.attn_build_sparse_index.argtypes = [T, T, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp,
                                             vp, vp, vp, ctypes.c_size_t, vp]
     lib.attn_build_sparse_index.restype = i32
@@ -261,6 +272,44 @@ def attn_blocksparse_check(blk_ptr, blk_idx, col_ptr, col_idx, B, Hq, Lq, Lk, bl
     ptrs = [ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(None) for a in arrs]
     st = load_library().attn_blocksparse_check(*ptrs, B, Hq, Lq, Lk, block_m, block_n)
     _check("attn_blocksparse_check", st)
+    return st
+
+
+def attn_vertical_slash_workspace_bytes(B, Hq, Lk) -> int:
+    return int(load_library().attn_vertical_slash_workspace_bytes(B, Hq, Lk))
+
+
+def attn_fwd_vertical_slash(q, k, v, o, blk_ptr, blk_idx, col_ptr, col_idx, slash_ptr,
+                            slash_idx, lse=None, causal=True, scale=None, workspace=None,
+                            stream=None):
+    """Block-sparse forward with per-head slash lines added to the union (int32 GPU tensors,
+    layout in include/attn.h). Allocates the bitmap workspace with torch unless given."""
+    torch = _torch()
+    B, Lq, Hq, Dqk = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    if scale is None:
+        scale = Dqk ** -0.5
+    wsb = attn_vertical_slash_workspace_bytes(B, Hq, Lk)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    st = load_library().attn_fwd_vertical_slash(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
+        _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
+        _int_ptr(blk_ptr, "blk_ptr"), _int_ptr(blk_idx, "blk_idx"), _int_ptr(col_ptr, "col_ptr"),
+        _int_ptr(col_idx, "col_idx"), _int_ptr(slash_ptr, "slash_ptr"),
+        _int_ptr(slash_idx, "slash_idx"), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check("attn_fwd_vertical_slash", st)
+    return o
+
+
+def attn_vertical_slash_check(slash_ptr, slash_idx, B, Hq, Lk) -> int:
+    """Validate HOST slash lists (numpy int32 arrays). Returns ATTN_OK or raises AttnError."""
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.int32)) for x in (slash_ptr, slash_idx)]
+    ptrs = [ctypes.c_void_p(a.ctypes.data) if a.size else ctypes.c_void_p(None) for a in arrs]
+    st = load_library().attn_vertical_slash_check(*ptrs, B, Hq, Lk)
+    _check("attn_vertical_slash_check", st)
     return st
 
 

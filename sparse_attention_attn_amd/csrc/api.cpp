@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <exception>
+#include <sstream>
 #include <string>
 
 #include "../../include/attn.h"
@@ -38,6 +39,9 @@ void fill_fwd(attn::FwdArgs& a, const attn_tensor_t& q, const attn_tensor_t& k,
   a.xcd_remap = 0;
   a.blk_ptr = a.blk_idx = a.col_ptr = a.col_idx = nullptr;
   a.nkb = (Lk + 63) / 64;
+  a.sl_ptr = a.sl_idx = nullptr;
+  a.sl_bits = a.cl_bits = nullptr;
+  a.bits_words = 0;
 }
 
 }  // namespace
@@ -162,6 +166,60 @@ int attn_fwd_blocksparse(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn
   } catch (...) {
     return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
   }
+}
+
+int attn_fwd_vertical_slash(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                            float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                            int causal, float scale, const int32_t* blk_ptr,
+                            const int32_t* blk_idx, const int32_t* col_ptr,
+                            const int32_t* col_idx, const int32_t* slash_ptr,
+                            const int32_t* slash_idx, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  static const char* fn = "attn_fwd_vertical_slash";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_attention_args(fn, attn::Op::kSparse, q, k, v, &o, lse, B, Hq, Hkv, Lq,
+                                        Lk, Dqk, Dv, scale);
+    if (st != ATTN_OK) return st;
+    if (blk_ptr == nullptr || col_ptr == nullptr || slash_ptr == nullptr)
+      return attn::fail(ATTN_ERR_INVALID_ARG, fn, "blk_ptr / col_ptr / slash_ptr is NULL");
+    const size_t need = attn_vertical_slash_workspace_bytes(B, Hq, Lk);
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) {
+      std::ostringstream m;
+      m << "workspace must be non-NULL, 256-byte aligned and at least " << need << " bytes";
+      return attn::fail(ATTN_ERR_WORKSPACE, fn, m.str());
+    }
+    attn::FwdArgs a;
+    fill_fwd(a, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, causal, scale);
+    a.n_qtiles = (Lq + attn::kSparseBlockM - 1) / attn::kSparseBlockM;
+    a.blk_ptr = blk_ptr;
+    a.blk_idx = blk_idx;
+    a.col_ptr = col_ptr;
+    a.col_idx = col_idx;
+    a.sl_ptr = slash_ptr;
+    a.sl_idx = slash_idx;
+    a.bits_words = attn::vs_bits_words(Lk);
+    uint32_t* bits = static_cast<uint32_t*>(workspace);
+    a.sl_bits = bits;
+    a.cl_bits = bits + (size_t)B * Hq * a.bits_words;
+    return launch_status(fn, attn::launch_fwd_vslash(a, Dqk, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+size_t attn_vertical_slash_workspace_bytes(int B, int Hq, int Lk) {
+  if (B < 1 || Hq < 1 || Lk < 1) return 0;
+  return 2 * (size_t)B * Hq * attn::vs_bits_words(Lk) * sizeof(uint32_t);
+}
+
+int attn_vertical_slash_check(const int32_t* slash_ptr, const int32_t* slash_idx, int B, int Hq,
+                              int Lk) {
+  attn::clear_last_error();
+  return attn::check_slash_lists("attn_vertical_slash_check", slash_ptr, slash_idx, B, Hq, Lk);
 }
 
 int attn_blocksparse_check(const int32_t* blk_ptr, const int32_t* blk_idx, const int32_t* col_ptr,

@@ -61,17 +61,17 @@ struct WaveState {
   uint32_t vofs;  // lane byte offset of its transposed V reads inside a tile
 };
 
-// Math of one tile for one wave. When `masked`, kidx(local key) gives the key position (or -1
-// if the slot holds no key) and invisible keys are masked; otherwise every key is visible.
-// MFMA groups run at raised wave priority so that, with two waves per SIMD, the wave feeding
-// the matrix core wins issue arbitration and the other wave's softmax fills the gaps.
-template <int D, class KeyIdx>
-__device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, const char* st,
-                                          int row, bool masked, KeyIdx kidx, int l) {
+// Math of one tile for one wave. When `masked`, mask(s0, s1) sets the scores of invisible keys
+// to -inf (slot (block kb, j) of s_kb holds local key 32*kb + 8*(j/4) + 4*(l/32) + j%4);
+// otherwise every key is visible. MFMA groups run at raised wave priority so that, with two
+// waves per SIMD, the wave feeding the matrix core wins issue arbitration and the other wave's
+// softmax fills the gaps.
+template <int D, class Mask>
+__device__ __forceinline__ void tile_math_mask(const FwdArgs& a, WaveState<D>& ws, const char* st,
+                                               bool masked, Mask mask, int l) {
   using C = TileCfg<D>;
   const char* kt = st + ws.kofs;
   const char* vt = st + C::KT_BYTES + ws.vofs;
-  const int h = l >> 5;
 
   // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks), one K slab per operand
   f32x16 s0 = {}, s1 = {};
@@ -85,18 +85,7 @@ __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, co
   }
   __builtin_amdgcn_s_setprio(0);
 
-  // ---- mask: slot (block kb, j) holds local key 32*kb + 8*(j/4) + 4*h + j%4
-  if (masked) {
-    const int lim = a.causal ? row + a.off : 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kl = 8 * (j >> 2) + 4 * h + (j & 3);
-      const int k0i = kidx(kl);
-      const int k1i = kidx(kl + 32);
-      if (k0i < 0 || k0i > lim) s0[j] = -INFINITY;
-      if (k1i < 0 || k1i > lim) s1[j] = -INFINITY;
-    }
-  }
+  if (masked) mask(s0, s1);
 
   // ---- online softmax (exp2 domain, lazily moved reference maximum)
   float mx = -INFINITY;
@@ -146,6 +135,25 @@ __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, co
     }
   }
   __builtin_amdgcn_s_setprio(0);
+}
+
+// Key-position form: kidx(local key) gives the key position, or -1 if the slot holds no key;
+// keys beyond the causal limit of `row` are masked too.
+template <int D, class KeyIdx>
+__device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, const char* st,
+                                          int row, bool masked, KeyIdx kidx, int l) {
+  const int h = l >> 5;
+  tile_math_mask<D>(a, ws, st, masked, [&](f32x16& s0, f32x16& s1) {
+    const int lim = a.causal ? row + a.off : 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kl = 8 * (j >> 2) + 4 * h + (j & 3);
+      const int k0i = kidx(kl);
+      const int k1i = kidx(kl + 32);
+      if (k0i < 0 || k0i > lim) s0[j] = -INFINITY;
+      if (k1i < 0 || k1i > lim) s1[j] = -INFINITY;
+    }
+  }, l);
 }
 
 template <int D>
@@ -217,17 +225,27 @@ __device__ __forceinline__ int logical_block(int xcd_remap) {
 // Phase 1 walks the listed key blocks; phase 2 gathers the head's vertical columns that are
 // causally visible to the block and not already inside a listed block (so a key is never
 // counted twice), 64 at a time, in ascending key order.
+//
+// With SLASH, phase 3 adds the head's slash lines (MInference article, paragraph on the
+// vertical-slash pattern): the line at offset o >= 0 lets query row i see key i + off - o
+// (off = Lk - Lq). Setup marks the 64-key blocks any line crosses inside this query block's
+// rows; phase 3 runs each marked block that is not listed as a tile whose mask keeps a pair
+// (row, key) only when row + off - key is a listed offset and key is not a listed column (those
+// keys were counted in phase 2). The offsets and the columns of a head come as two bitmaps
+// (vs_bits_kernel); each lane loads the 96 + 64 bits its 32 scores need together with the
+// tile's copy, so the copy wait of the next step covers those loads too.
 // ------------------------------------------------------------------------------------------
 constexpr int kSeg = 512;              // columns examined per compaction pass
 constexpr int kMaxBitmapWords = 512;   // listed-block bitmap: up to 16384 key blocks (1M keys)
 
-template <int D, int NW>
+template <int D, int NW, bool SLASH>
 __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
   __shared__ uint32_t bitmap[kMaxBitmapWords];
+  __shared__ uint32_t tbits[SLASH ? kMaxBitmapWords : 1];  // blocks crossed by a slash line
   __shared__ int kept[kSeg];
   __shared__ int wave_cnt[NW];
 
@@ -265,12 +283,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
   constexpr int kListCap = 2 * kSeg;
   const bool list_in_lds = nb <= kListCap;
   for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
+  if constexpr (SLASH)
+    for (int i = tid; i < nwords; i += NT) tbits[i] = 0u;
   __syncthreads();
   for (int i = tid; i < nb; i += NT) {
     const int kbk = a.blk_idx[bstart + i];
     const bool valid = kbk >= 0 && kbk < a.nkb;
     if (valid) atomicOr(&bitmap[kbk >> 5], 1u << (kbk & 31));
     if (i < kListCap) blist[i] = (short)(valid ? kbk : -1);
+  }
+  if constexpr (SLASH) {
+    // the line at offset o meets rows q0..qlast at keys q0+off-o .. qlast+off-o (<= klim)
+    const int s1 = a.sl_ptr[bh + 1];
+    for (int i = a.sl_ptr[bh] + tid; i < s1; i += NT) {
+      const int o = a.sl_idx[i];
+      const int hi = qlast + a.off - o;
+      if (o < 0 || hi < 0) continue;
+      const int lo = max(0, q0 + a.off - o);
+      const int b0 = lo >> 6, b1 = min(hi, lkm1) >> 6;
+      if (lo > lkm1) continue;
+      atomicOr(&tbits[b0 >> 5], 1u << (b0 & 31));
+      if (b1 != b0) atomicOr(&tbits[b1 >> 5], 1u << (b1 & 31));
+    }
   }
   __syncthreads();
 
@@ -378,23 +412,137 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
     }
     __syncthreads();  // kept[] and the stages are rewritten by the next segment
   }
+
+  // ---- phase 3: slash lines, over the crossed blocks that are not listed
+  if constexpr (SLASH) {
+    const int h = l >> 5;
+    const uint32_t* sbits = a.sl_bits + (int64_t)bh * a.bits_words;
+    const uint32_t* cbits = a.cl_bits + (int64_t)bh * a.bits_words;
+    // Lane's window: bitmap bit (o + 128) of its local key c's offset is at rw - base + 59 - c.
+    const int rw = row + a.off + 69 - 4 * h;
+    uint32_t mw[2][5];
+    for (int wc = 0; wc < nwords; wc += kSeg / 32) {
+      int cnt = 0;
+      for (int rr = 0; rr < kSeg; rr += NT) {
+        const int bit = rr + tid;
+        const int wi = wc + (bit >> 5);
+        const bool keep = wi < nwords && (((tbits[wi] & ~bitmap[wi]) >> (bit & 31)) & 1u);
+        const uint64_t mask = __ballot(keep);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (l == 0) wave_cnt[w] = __popcll(mask);
+        __syncthreads();
+        int woff = 0, tot = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const int cw = wave_cnt[ww];
+          woff += (ww < w) ? cw : 0;
+          tot += cw;
+        }
+        if (keep) kept[cnt + woff + below] = 32 * wc + bit;
+        cnt += tot;
+        __syncthreads();
+      }
+      auto issue_sl = [&](auto S, int t) {
+        constexpr int s = decltype(S)::value;
+        char* st = s == 0 ? st0 : st1;
+        const int base = kept[t] * BN;
+        const uint32_t* sp = sbits + (max(rw - base, 0) >> 5);
+        mw[s][0] = sp[0];
+        mw[s][1] = sp[1];
+        mw[s][2] = sp[2];
+        mw[s][3] = cbits[base >> 5];
+        mw[s][4] = cbits[(base >> 5) + 1];
+        if (base + BN <= a.Lk) {
+          issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl,
+                                 off, w);
+        } else {
+          issue_tile_slow<D, NW>(a, st, kbp, vbp, [&](int r) { return min(base + r, lkm1); }, w,
+                                 l);
+        }
+      };
+      auto step_sl = [&](auto S, int t) {
+        constexpr int s = decltype(S)::value;
+        wait_dma_all();
+        __syncthreads();
+        if (t + 1 < cnt) issue_sl(ic<1 - s>{}, t + 1);
+        const int base = kept[t] * BN;
+        if (base > qwlast + a.off) return;  // past every row of this wave on every line
+        const int sh = max(rw - base, 0) & 31;
+        tile_math_mask<D>(a, ws, s == 0 ? st0 : st1, true, [&](f32x16& s0, f32x16& s1) {
+          // offsets: bit x of (d1:d0) is local key c = 59 - x; reversed and shifted, bit c
+          const uint32_t d0 = __builtin_amdgcn_alignbit(mw[s][1], mw[s][0], sh);
+          const uint32_t d1 = __builtin_amdgcn_alignbit(mw[s][2], mw[s][1], sh);
+          const uint32_t r0 = __builtin_bitreverse32(d1), r1 = __builtin_bitreverse32(d0);
+          // listed columns: bit c is key base + 4h + c
+          const uint32_t c0 = __builtin_amdgcn_alignbit(mw[s][4], mw[s][3], 4 * h);
+          const uint32_t c1 = mw[s][4] >> (4 * h);
+          const uint32_t vlo = ((r0 >> 4) | (r1 << 28)) & ~c0;
+          const uint32_t vhi = (r1 >> 4) & ~c1;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = 8 * (j >> 2) + (j & 3);
+            if (!((vlo >> c) & 1u)) s0[j] = -INFINITY;
+            if (!((vhi >> c) & 1u)) s1[j] = -INFINITY;
+          }
+        }, l);
+      };
+      if (cnt > 0) issue_sl(ic<0>{}, 0);
+      for (int t = 0; t < cnt; t += 2) {
+        step_sl(ic<0>{}, t);
+        if (t + 1 < cnt) step_sl(ic<1>{}, t + 1);
+      }
+      __syncthreads();  // kept[] and the stages are rewritten by the next chunk
+    }
+  }
   store_out<D>(a, ws, b, hq, row, l);
 }
 
-template <int D, int NW>
+// Per (b, h): bitmap of the listed slash offsets (bit o + 128, so a lane's window never starts
+// below bit 0) and of the listed columns (bit j), nbw words each; out-of-range entries are
+// ignored.
+__global__ __launch_bounds__(256) void vs_bits_kernel(const FwdArgs a) {
+  const int bh = (int)blockIdx.x;
+  uint32_t* sb = const_cast<uint32_t*>(a.sl_bits) + (int64_t)bh * a.bits_words;
+  uint32_t* cb = const_cast<uint32_t*>(a.cl_bits) + (int64_t)bh * a.bits_words;
+  for (int i = (int)threadIdx.x; i < a.bits_words; i += 256) {
+    sb[i] = 0u;
+    cb[i] = 0u;
+  }
+  __threadfence();
+  __syncthreads();
+  for (int i = a.sl_ptr[bh] + (int)threadIdx.x; i < a.sl_ptr[bh + 1]; i += 256) {
+    const int o = a.sl_idx[i];
+    if (o >= 0 && o < a.Lk) atomicOr(&sb[(o + 128) >> 5], 1u << ((o + 128) & 31));
+  }
+  for (int i = a.col_ptr[bh] + (int)threadIdx.x; i < a.col_ptr[bh + 1]; i += 256) {
+    const int j = a.col_idx[i];
+    if (j >= 0 && j < a.Lk) atomicOr(&cb[j >> 5], 1u << (j & 31));
+  }
+}
+
+template <int D, int NW, bool SLASH>
 hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
   FwdArgs aa = a;
   aa.xcd_remap = (nwg % 256 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_sparse_kernel<D, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0, stream, aa);
+  if constexpr (SLASH)
+    hipLaunchKernelGGL(vs_bits_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, aa);
+  hipLaunchKernelGGL((fwd_sparse_kernel<D, NW, SLASH>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+                     stream, aa);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_sparse_t<128, 2>(a, stream);
-  return launch_sparse_t<64, 2>(a, stream);
+  if (d == 128) return launch_sparse_t<128, 2, false>(a, stream);
+  return launch_sparse_t<64, 2, false>(a, stream);
+}
+
+hipError_t launch_fwd_vslash(const FwdArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_sparse_t<128, 2, true>(a, stream);
+  return launch_sparse_t<64, 2, true>(a, stream);
 }
 
 }  // namespace attn

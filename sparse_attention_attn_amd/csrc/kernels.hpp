@@ -29,7 +29,16 @@ struct FwdArgs {
   const int32_t* col_ptr;
   const int32_t* col_idx;
   int nkb;        // ceil(Lk / 64)
+  // slash lines (vertical-slash pattern): per-head offsets and the two per-head bitmaps
+  const int32_t* sl_ptr;
+  const int32_t* sl_idx;
+  const uint32_t* sl_bits;  // [B*Hq][bits_words]: bit o + 128 set for a listed offset o
+  const uint32_t* cl_bits;  // [B*Hq][bits_words]: bit j set for a listed column j
+  int bits_words;
 };
+
+// Words per head of each vertical-slash bitmap.
+inline int vs_bits_words(int Lk) { return (Lk + 255) / 32 + 2; }
 
 // Split-KV partials.
 struct SplitArgs {
@@ -92,6 +101,7 @@ constexpr int kProbeChunk = 1024;
 
 hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_build_index(const IndexArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_vslash(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);

@@ -212,6 +212,36 @@ int check_blocksparse_lists(const char* fn, const int32_t* blk_ptr, const int32_
   return ATTN_OK;
 }
 
+int check_slash_lists(const char* fn, const int32_t* slash_ptr, const int32_t* slash_idx, int B,
+                      int Hq, int Lk) {
+  if (B < 1 || Hq < 1 || Lk < 1) return fail(ATTN_ERR_INVALID_ARG, fn, "sizes must be >= 1");
+  if (slash_ptr == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "slash_ptr is NULL");
+  if (slash_ptr[0] != 0) return fail(ATTN_ERR_INVALID_ARG, fn, "slash_ptr[0] must be 0");
+  for (int64_t r = 0; r < (int64_t)B * Hq; ++r) {
+    const int32_t lo = slash_ptr[r], hi = slash_ptr[r + 1];
+    if (hi < lo) {
+      std::ostringstream s;
+      s << "slash_ptr decreases at head row " << r;
+      return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+    }
+    if (hi > lo && slash_idx == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "slash_idx is NULL");
+    for (int32_t i = lo; i < hi; ++i) {
+      const int32_t x = slash_idx[i];
+      if (x < 0 || x >= Lk) {
+        std::ostringstream s;
+        s << "slash_idx[" << i << "]=" << x << " outside [0, " << Lk << ")";
+        return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+      }
+      if (i > lo && slash_idx[i - 1] >= x) {
+        std::ostringstream s;
+        s << "slash_idx not strictly increasing at " << i;
+        return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+      }
+    }
+  }
+  return ATTN_OK;
+}
+
 int64_t index_blk_head_len(int L, int topk) {
   if (L < 1 || topk < 1) return 0;
   const int64_t nqb = (L + 63) / 64;

@@ -58,6 +58,8 @@ constexpr int kSparseMaxLk = 1 << 20;
 // Dynamic sparse-index builder (square causal sizes L = Lq = Lk).
 constexpr int kIndexMaxL = 131072;  // 2048 key blocks: one builder workgroup sorts them in LDS
 // Block-list entries per head: sum over query blocks qb of min(topk, qb + 1).
+int check_slash_lists(const char* fn, const int32_t* slash_ptr, const int32_t* slash_idx, int B,
+                      int Hq, int Lk);
 int64_t index_blk_head_len(int L, int topk);
 // Workspace layout (byte offsets, 256-byte aligned) and total size.
 struct IndexWorkspace {

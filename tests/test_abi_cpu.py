@@ -11,7 +11,7 @@ import pytest
 
 import sparse_attention_attn_amd as S
 from sparse_attention_attn_amd._lib import AttnTensorC
-from workloads import dense_causal_lists, make_blocksparse_lists
+from workloads import dense_causal_lists, make_blocksparse_lists, make_vslash_lists
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
@@ -158,6 +158,56 @@ def test_blocksparse_check_rejects(mutate, frag):
     mutate(bp, bi, cp, ci)
     with pytest.raises(S.AttnError) as e:
         S.attn_blocksparse_check(bp, bi, cp, ci, 1, 2, 1000, 1000)
+    assert e.value.status == S.ATTN_ERR_INVALID_ARG
+    assert frag in str(e.value)
+
+
+def _vslash(slash_ptr=FAKE, ws=FAKE, ws_bytes=None, Lk=4096, causal=1):
+    if ws_bytes is None:
+        ws_bytes = S.attn_vertical_slash_workspace_bytes(1, 4, Lk)
+    return _lib().attn_fwd_vertical_slash(
+        _t(), _t(), _t(), _t(), None, 1, 4, 2, 4096, Lk, 128, 128, causal, ctypes.c_float(0.1),
+        FAKE, FAKE, FAKE, FAKE, slash_ptr, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, code, frag", [
+    (dict(slash_ptr=None), S.ATTN_ERR_INVALID_ARG, "slash_ptr"),
+    (dict(ws=None), S.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=64), S.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(ws=FAKE + 16), S.ATTN_ERR_WORKSPACE, "256-byte"),
+    (dict(Lk=(1 << 20) + 64), S.ATTN_ERR_UNSUPPORTED, "limit"),
+])
+def test_vertical_slash_entry_validation(kw, code, frag):
+    assert _vslash(**kw) == code
+    assert frag in S.attn_last_error()
+
+
+def test_vertical_slash_workspace_bytes():
+    # two bitmaps per (b, h) of (Lk + 255) // 32 + 2 words each
+    assert S.attn_vertical_slash_workspace_bytes(1, 32, 131072) == 2 * 32 * (4103 + 2) * 4
+    assert S.attn_vertical_slash_workspace_bytes(2, 3, 1) == 2 * 6 * (8 + 2) * 4
+    assert S.attn_vertical_slash_workspace_bytes(0, 3, 100) == 0
+
+
+def test_vertical_slash_check_accepts_generated_lists():
+    sp, si, cp, ci = make_vslash_lists(2, 3, 5000, 11, band=100, n_far=20, n_cols=70, sink=8)
+    assert S.attn_vertical_slash_check(sp, si, 2, 3, 5000) == S.ATTN_OK
+    assert S.attn_vertical_slash_check(np.zeros(7, np.int32), [], 2, 3, 5000) == S.ATTN_OK
+
+
+@pytest.mark.parametrize("mutate,frag", [
+    (lambda sp, si: si.__setitem__(5, si[4]), "strictly increasing"),
+    (lambda sp, si: si.__setitem__(0, -1), "outside"),
+    (lambda sp, si: si.__setitem__(sp[1] - 1, 5000), "outside"),
+    (lambda sp, si: sp.__setitem__(1, -1), "decreases"),
+    (lambda sp, si: sp.__setitem__(0, 1), "slash_ptr[0]"),
+])
+def test_vertical_slash_check_rejects(mutate, frag):
+    sp, si = [np.array(x) for x in make_vslash_lists(1, 2, 5000, 12, band=50, n_far=10,
+                                                     n_cols=5, sink=1)[:2]]
+    mutate(sp, si)
+    with pytest.raises(S.AttnError) as e:
+        S.attn_vertical_slash_check(sp, si, 1, 2, 5000)
     assert e.value.status == S.ATTN_ERR_INVALID_ARG
     assert frag in str(e.value)
 

@@ -1,0 +1,192 @@
+"""GPU parity of attn_fwd_vertical_slash (block/column union plus per-head slash lines)
+against the fp64 oracle, through the C ABI.
+
+Slash line o: query row i sees key i + (Lk - Lq) - o. Cases: slashes alone, slashes with
+columns and blocks that overlap them (each key counted once), Lq < Lk alignment, D = 64,
+non-causal blocks above the diagonal, every offset listed (= dense causal), empty slash lists
+(bitwise equal to attn_fwd_blocksparse), determinism, and the 128K vertical-slash workload
+on sampled rows.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from tests.helpers import check_parity, say, to_f64
+from workloads import (WORKLOADS, make_qkv, make_vslash_lists, randn_bf16, sampled_rows)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _csr(per_head_lists):
+    ptr, parts = [0], []
+    for x in per_head_lists:
+        x = np.asarray(sorted(set(int(v) for v in x)), np.int32)
+        parts.append(x)
+        ptr.append(ptr[-1] + x.size)
+    idx = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    return np.asarray(ptr, np.int32), idx
+
+
+def _dev(x):
+    import torch
+    return torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32)).to(DEV)
+
+
+def _run(q, k, v, bp, bi, cp, ci, sp, si, causal=True, scale=None):
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Lq, Hq, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    o = torch.empty((B, Lq, Hq, v.shape[3]), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=DEV)
+    S.attn_fwd_vertical_slash(q.to(DEV), k.to(DEV), v.to(DEV), o, _dev(bp), _dev(bi), _dev(cp),
+                              _dev(ci), _dev(sp), _dev(si), lse=lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _compare(q, k, v, bp, bi, cp, ci, sp, si, label, causal=True):
+    B, Lq, Hq, D = q.shape
+    Lk = k.shape[1]
+    import sparse_attention_attn_amd as S
+    S.attn_blocksparse_check(bp, bi, cp, ci, B, Hq, Lq, Lk)
+    S.attn_vertical_slash_check(sp, si, B, Hq, Lk)
+    o, lse = _run(q, k, v, bp, bi, cp, ci, sp, si, causal)
+    fn = A.vslash_allowed_fn(bp, bi, cp, ci, sp, si, Hq, -(-Lq // 64), Lq, Lk)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
+                                 causal, allowed_fn=fn)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, label)
+
+
+def _no_blocks(B, Hq, Lq):
+    return np.zeros(B * Hq * -(-Lq // 64) + 1, np.int32), np.zeros(0, np.int32)
+
+
+def _qkv(B, Lq, Lk, Hq, Hkv, D, seed):
+    return (randn_bf16((B, Lq, Hq, D), seed), randn_bf16((B, Lk, Hkv, D), seed + 1),
+            randn_bf16((B, Lk, Hkv, D), seed + 2))
+
+
+def test_slashes_only():
+    B, Hq, Hkv, L, D = 1, 4, 2, 700, 128
+    say("vslash: slashes only")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7000)
+    rng = np.random.default_rng(1)
+    sp, si = _csr([[0, 1, 2, 63, 64, 65, 127, 200] + rng.choice(np.arange(201, L), 10, False).tolist()
+                   for _ in range(B * Hq)])
+    bp, bi = _no_blocks(B, Hq, L)
+    cp, ci = np.zeros(B * Hq + 1, np.int32), np.zeros(0, np.int32)
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, "slashes only")
+
+
+def test_slashes_columns_blocks_overlap():
+    """Slash keys that are also listed columns or inside listed blocks are counted once."""
+    B, Hq, Hkv, L, D = 2, 4, 2, 777, 128
+    say("vslash: union with overlaps")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7100)
+    rng = np.random.default_rng(2)
+    nqb = -(-L // 64)
+    blocks = []
+    for _ in range(B * Hq):
+        for qb in range(nqb):
+            blocks.append([0, qb] + rng.choice(np.arange(qb + 1), min(2, qb + 1), False).tolist())
+    bp, bi = _csr(blocks)
+    cp, ci = _csr([[0, 5, 64, 100, 300, 776] + rng.choice(L, 20, False).tolist()
+                   for _ in range(B * Hq)])
+    sp, si = _csr([list(range(0, 40)) + [64, 100, 128, 500] + rng.choice(L, 15, False).tolist()
+                   for _ in range(B * Hq)])
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, "union overlap")
+
+
+def test_bottom_right_alignment_and_d64():
+    B, Hq, Hkv, Lq, Lk, D = 1, 2, 1, 333, 1000, 64
+    say("vslash: Lq < Lk, D 64")
+    q, k, v = _qkv(B, Lq, Lk, Hq, Hkv, D, 7200)
+    rng = np.random.default_rng(3)
+    bp, bi = _no_blocks(B, Hq, Lq)
+    cp, ci = _csr([rng.choice(Lk, 30, False) for _ in range(B * Hq)])
+    sp, si = _csr([[0, 3, 17] + rng.choice(Lk, 25, False).tolist() for _ in range(B * Hq)])
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, "alignment d64")
+
+
+def test_noncausal_blocks_above_diagonal():
+    B, Hq, Hkv, L, D = 1, 2, 2, 400, 128
+    say("vslash: non-causal")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7300)
+    nqb = -(-L // 64)
+    bp, bi = _csr([[min(qb + 2, nqb - 1)] for _ in range(B * Hq) for qb in range(nqb)])
+    cp, ci = _csr([[1, 399] for _ in range(B * Hq)])
+    sp, si = _csr([[0, 9, 70] for _ in range(B * Hq)])
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, "non-causal", causal=False)
+
+
+def test_every_offset_is_dense_causal():
+    B, Hq, Hkv, L, D = 1, 2, 1, 300, 128
+    say("vslash: every offset")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7400)
+    bp, bi = _no_blocks(B, Hq, L)
+    cp, ci = np.zeros(B * Hq + 1, np.int32), np.zeros(0, np.int32)
+    sp, si = _csr([range(L) for _ in range(B * Hq)])
+    o, lse = _run(q, k, v, bp, bi, cp, ci, sp, si)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
+                                 True)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "every offset")
+
+
+def test_empty_slashes_equal_blocksparse_bitwise():
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import make_blocksparse_lists
+    B, Hq, Hkv, L, D = 1, 4, 2, 1000, 128
+    say("vslash: empty slash lists")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7500)
+    bp, bi, cp, ci = make_blocksparse_lists(B, Hq, L, L, 7503, local_blocks=4, n_cols=50)
+    sp, si = np.zeros(B * Hq + 1, np.int32), np.zeros(0, np.int32)
+    o1, l1 = _run(q, k, v, bp, bi, cp, ci, sp, si)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    S.attn_fwd_blocksparse(q.to(DEV), k.to(DEV), v.to(DEV), o2, _dev(bp), _dev(bi), _dev(cp),
+                           _dev(ci), lse=l2, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_deterministic():
+    B, Hq, Hkv, L, D = 1, 2, 1, 500, 128
+    say("vslash: determinism")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7600)
+    bp, bi = _no_blocks(B, Hq, L)
+    cp, ci = _csr([[0, 7, 300] for _ in range(B * Hq)])
+    sp, si = _csr([list(range(20)) + [77, 400] for _ in range(B * Hq)])
+    a = _run(q, k, v, bp, bi, cp, ci, sp, si)
+    b = _run(q, k, v, bp, bi, cp, ci, sp, si)
+    assert all(bool((x == y).all()) for x, y in zip(a, b))
+
+
+def test_vslash_128k_sampled_rows():
+    """The 128K vertical-slash workload (B 1, Hq 32, Hkv 8, D 128): every head's output on
+    sampled rows against the oracle on those rows."""
+    import torch
+    w = WORKLOADS["vslash_128k"]
+    say(f"vslash full size {w.name}")
+    q, k, v = make_qkv(w)
+    sp, si, cp, ci = make_vslash_lists(w.B, w.Hq, w.Lk, 1000 * w.index + 3)
+    bp, bi = _no_blocks(w.B, w.Hq, w.Lq)
+    o, lse = _run(q, k, v, bp, bi, cp, ci, sp, si, scale=w.scale)
+    rows = sampled_rows(w.Lq, 192, 1000 * w.index + 4)
+    g = w.Hq // w.Hkv
+    for h in range(w.Hq):
+        c = h
+        allowed = (A.blocksparse_row_mask(rows, w.Lk, lambda qb: np.zeros(0, np.int64),
+                                          ci[cp[c]:cp[c + 1]])
+                   | A.slash_row_mask(rows, w.Lq, w.Lk, si[sp[c]:sp[c + 1]]))
+        o_ref, lse_ref = A.attention_query_rows(q[0, rows, h].double().numpy(),
+                                                k[:, :, h // g:h // g + 1].double().numpy(),
+                                                v[:, :, h // g:h // g + 1].double().numpy(),
+                                                A.effective_scale(w.scale), True, 0, 0, rows,
+                                                w.Lq, 1, allowed)
+        check_parity(o[0, rows, h].float().cpu().double().numpy(), o_ref,
+                     lse[0, h, rows].cpu().double().numpy(), lse_ref, f"vslash_128k h={h}")

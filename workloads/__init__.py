@@ -13,6 +13,10 @@ Recipe:
   blocks kb in [qb-63, qb] (diagonal included), each remaining causal block kb <= qb chosen
   independently with probability 0.03, and 1000 vertical key columns drawn uniformly without
   replacement over [0, L) per head. Lists are sorted and unique.
+* Vertical-slash lists (MInference article, vertical-slash pattern): per head, the slash
+  offsets 0..1023 (a band of 1024 diagonals below the causal one) plus 64 offsets drawn
+  uniformly from [1024, L), and 1000 vertical columns: keys 0..63 plus 936 keys drawn
+  uniformly from [64, L). No key blocks.
 * The MLA decode grid of the FlashMLA-ETAP page (section on experiments: DeepSeek-R1's 16
   heads of dimension 576, batch sizes 16 and 32, KV lengths 512 to 64K; one or two query
   tokens per the problem statement) uses the MLA recipe above with bottom-right causal
@@ -39,6 +43,7 @@ __all__ = [
     "randn_bf16_device",
     "sampled_rows",
     "dense_causal_lists",
+    "make_vslash_lists",
 ]
 
 
@@ -55,7 +60,7 @@ class Workload:
     Dv: int
     causal: bool
     scale: float
-    kind: str           # "prefill" | "decode" | "mla_decode" | "blocksparse"
+    kind: str           # "prefill" | "decode" | "mla_decode" | "blocksparse" | "vslash"
     mla: bool = False   # V is the first Dv columns of K (no separate V tensor)
 
 
@@ -72,6 +77,8 @@ WORKLOADS = {
     "blocksparse_128k": Workload("blocksparse_128k", 5, B=1, Hq=32, Hkv=8, Lq=131072, Lk=131072,
                                  Dqk=128, Dv=128, causal=True, scale=1.0 / math.sqrt(128),
                                  kind="blocksparse"),
+    "vslash_128k": Workload("vslash_128k", 6, B=1, Hq=32, Hkv=8, Lq=131072, Lk=131072, Dqk=128,
+                            Dv=128, causal=True, scale=1.0 / math.sqrt(128), kind="vslash"),
 }
 
 
@@ -163,6 +170,29 @@ def make_blocksparse_lists(B, Hq, Lq, Lk, seed, block=64, local_blocks=64, p_ext
     col_idx = np.concatenate(col_parts) if col_parts else np.zeros(0, np.int32)
     return (np.asarray(ptr, np.int32), blk_idx.astype(np.int32),
             np.asarray(col_ptr, np.int32), col_idx.astype(np.int32))
+
+
+def make_vslash_lists(B, Hq, Lk, seed, band=1024, n_far=64, n_cols=1000, sink=64):
+    """Vertical-slash lists per (b, h): slash offsets (the band 0..band-1 below the diagonal plus
+    n_far offsets drawn uniformly without replacement from [band, Lk)) and vertical columns
+    (keys 0..sink-1 plus n_cols - sink keys drawn uniformly without replacement from
+    [sink, Lk)). Returns int32 numpy arrays (slash_ptr [B*Hq+1], slash_idx, col_ptr [B*Hq+1],
+    col_idx), sorted and unique."""
+    g = _gen(seed)
+    sp, sparts, cp, cparts = [0], [], [0], []
+    for _ in range(B * Hq):
+        nb = min(band, Lk)
+        far = torch.randperm(max(Lk - nb, 0), generator=g)[:n_far].numpy() + nb
+        offs = np.unique(np.concatenate([np.arange(nb), far])).astype(np.int32)
+        sparts.append(offs)
+        sp.append(sp[-1] + offs.size)
+        ns = min(sink, Lk)
+        rest = torch.randperm(max(Lk - ns, 0), generator=g)[:max(n_cols - ns, 0)].numpy() + ns
+        cols = np.unique(np.concatenate([np.arange(ns), rest])).astype(np.int32)
+        cparts.append(cols)
+        cp.append(cp[-1] + cols.size)
+    cat = lambda parts: np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    return (np.asarray(sp, np.int32), cat(sparts), np.asarray(cp, np.int32), cat(cparts))
 
 
 def dense_causal_lists(B, Hq, Lq, Lk, block=64):
