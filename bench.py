@@ -75,6 +75,23 @@ def blocksparse_pairs(lists, B, Hq, L):
     return total
 
 
+def vslash_pairs(slash_ptr, slash_idx, col_ptr, col_idx, B, Hq, L):
+    """Exact visible pairs of the column / slash-line union with causal masking (Lq == Lk == L,
+    no key blocks): row i sees its columns <= i and keys i - o; a key that is both is counted
+    once, and such a pair (c, o) exists for every column c and offset o with c + o < L."""
+    import numpy as np
+    sp, si, cp, ci = [np.asarray(x, np.int64) for x in (slash_ptr, slash_idx, col_ptr, col_idx)]
+    rows = np.arange(L, dtype=np.int64)
+    total = 0
+    for bh in range(B * Hq):
+        offs = np.sort(si[sp[bh]:sp[bh + 1]])
+        cols = np.sort(ci[cp[bh]:cp[bh + 1]])
+        total += int(np.searchsorted(cols, rows, side="right").sum())
+        total += int(np.searchsorted(offs, rows, side="right").sum())
+        total -= int(np.searchsorted(offs, L - 1 - cols, side="right").sum())
+    return total
+
+
 # ------------------------------------------------------------------------------ timing
 def time_steps(step, steps, warmup):
     import torch
@@ -200,6 +217,31 @@ def bench_blocksparse(w, steps, warmup):
                       "density_vs_causal": round(pairs_d / dense, 4),
                       "tflops_incl_build": round(flops_d / (ms_d * 1e-3) / 1e12, 3)}
     return res
+
+
+def bench_vslash(w, steps, warmup):
+    import numpy as np
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import make_qkv, make_vslash_lists
+    q, k, v = [t.to("cuda:0") for t in make_qkv(w)]
+    sp, si, cp, ci = make_vslash_lists(w.B, w.Hq, w.Lk, 1000 * w.index + 3)
+    nqb = -(-w.Lq // 64)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda:0")
+    bp, bi = dev(np.zeros(w.B * w.Hq * nqb + 1)), dev(np.zeros(0))
+    dsp, dsi, dcp, dci = dev(sp), dev(si), dev(cp), dev(ci)
+    o = torch.empty((w.B, w.Lq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(S.attn_vertical_slash_workspace_bytes(w.B, w.Hq, w.Lk), dtype=torch.uint8,
+                     device="cuda:0")
+    step = lambda: S.attn_fwd_vertical_slash(q, k, v, o, bp, bi, dcp, dci, dsp, dsi, lse=lse,
+                                             causal=True, scale=w.scale, workspace=ws)
+    ms, wall = time_steps(step, steps, warmup)
+    pairs = vslash_pairs(sp, si, cp, ci, w.B, w.Hq, w.Lq)
+    flops = 2 * (w.Dqk + w.Dv) * pairs
+    dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
+    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            "density_vs_causal": pairs / dense}
 
 
 def mla_causal_pairs(lq, lk):
@@ -389,6 +431,8 @@ def main():
             res[name] = bench_decode(w, args.steps * 5, args.warmup)
         elif w.kind == "blocksparse":
             res[name] = bench_blocksparse(w, max(3, args.steps // 4), min(args.warmup, 2))
+        elif w.kind == "vslash":
+            res[name] = bench_vslash(w, max(3, args.steps // 4), min(args.warmup, 2))
         log(f"  -> {res[name]}")
 
     head = WORKLOADS[HEADLINE]
