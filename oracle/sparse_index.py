@@ -24,6 +24,10 @@ the lists consumed by the block-sparse forward admit:
 2. Column lists (per query head): probe with the last `probe` query rows; each probe row's
    softmax over its causally visible keys; a key's importance is the sum of its probability
    over the probe rows; keep the top n_cols keys, ties to the lower key index.
+3. Slash lists (per query head, for the vertical-slash pattern): the same probe; the slash
+   line at offset o is the diagonal o keys below the causal one (probe row r meets key r - o);
+   its importance is the sum over probe rows of their probability on that key; keep the top
+   n_slash offsets, ties to the lower offset.
 
 Sizes are square and causal (Lq = Lk = L). Lists are sorted ascending, as the consumer needs.
 """
@@ -40,6 +44,8 @@ __all__ = [
     "select_columns",
     "build_index",
     "block_count",
+    "slash_importance",
+    "build_vslash_index",
 ]
 
 
@@ -88,6 +94,23 @@ def probe_importance(q_head: np.ndarray, k_head: np.ndarray, scale: float, probe
     return p.sum(axis=0)
 
 
+def slash_importance(q_head: np.ndarray, k_head: np.ndarray, scale: float, probe: int) -> np.ndarray:
+    """Per diagonal offset o in [0, L): the sum over the last `probe` query rows r of their
+    causal softmax probability on key r - o (rows with r < o do not meet that line)."""
+    L = q_head.shape[0]
+    rows = np.arange(max(0, L - probe), L)
+    s = scale * (q_head[rows] @ k_head.T)
+    s[np.arange(L)[None, :] > rows[:, None]] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p /= p.sum(axis=1, keepdims=True)
+    imp = np.zeros(L)
+    for a, r in enumerate(rows):
+        for o in range(r + 1):
+            imp[o] += p[a, r - o]
+    return imp
+
+
 def select_columns(importance: np.ndarray, n_cols: int) -> np.ndarray:
     """The n_cols keys of largest importance, ties to the lower index; sorted ascending."""
     order = sorted(range(importance.shape[0]), key=lambda j: (-importance[j], j))
@@ -125,3 +148,30 @@ def build_index(q, k, scale, topk, n_cols, block=64, probe=64):
     cat = lambda parts: (np.concatenate(parts) if parts else np.zeros(0)).astype(np.int32)
     return (np.asarray(blk_ptr, np.int32), cat(blk_parts), np.asarray(col_ptr, np.int32),
             cat(col_parts), scores_all, imp_all)
+
+
+def build_vslash_index(q, k, scale, n_cols, n_slash, probe=64):
+    """Vertical-slash lists for q [B, L, Hq, D], k [B, L, Hkv, D] (fp64 arrays): col_ptr
+    [B*Hq + 1], col_idx, slash_ptr [B*Hq + 1], slash_idx (int32), plus the column and slash
+    importances [B, Hq, L] for validity checks. Columns as in `build_index`; offsets are the
+    top n_slash of `slash_importance` (ties to the lower offset), sorted ascending."""
+    B, L, Hq, _ = q.shape
+    g = Hq // k.shape[2]
+    col_ptr, col_parts, sl_ptr, sl_parts = [0], [], [0], []
+    cimp = np.empty((B, Hq, L))
+    simp = np.empty((B, Hq, L))
+    for b in range(B):
+        for h in range(Hq):
+            qh = q[b, :, h, :]
+            kh = k[b, :, h // g, :]
+            cimp[b, h] = probe_importance(qh, kh, scale, probe)
+            simp[b, h] = slash_importance(qh, kh, scale, probe)
+            cols = select_columns(cimp[b, h], n_cols)
+            offs = select_columns(simp[b, h], n_slash)   # same ranking rule over offsets
+            col_parts.append(cols)
+            col_ptr.append(col_ptr[-1] + cols.size)
+            sl_parts.append(offs)
+            sl_ptr.append(sl_ptr[-1] + offs.size)
+    cat = lambda parts: (np.concatenate(parts) if parts else np.zeros(0)).astype(np.int32)
+    return (np.asarray(col_ptr, np.int32), cat(col_parts), np.asarray(sl_ptr, np.int32),
+            cat(sl_parts), cimp, simp)

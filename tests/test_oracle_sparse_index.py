@@ -144,6 +144,62 @@ def test_gqa_head_map_contiguous_groups():
     assert all(2 not in list(lists[h][5]) for h in (2, 3))
 
 
+def test_slash_importance_sums_to_probe_rows():
+    """Each probe row's probabilities sum to 1 and every visible (row, key) pair lies on
+    exactly one line (offset row - key >= 0), so the importances sum to the probe size."""
+    L, D = 300, 8
+    q, k = RNG.standard_normal((L, D)), RNG.standard_normal((L, D))
+    imp = X.slash_importance(q, k, 0.4, 64)
+    assert np.isclose(imp.sum(), 64.0, rtol=1e-12)
+    assert np.all(imp >= 0)
+
+
+def test_slash_importance_single_probe_row_reverses_columns():
+    """With one probe row r = L - 1, line o meets key L - 1 - o only: the slash importances
+    are the column importances reversed."""
+    L, D = 120, 6
+    q, k = RNG.standard_normal((L, D)), RNG.standard_normal((L, D))
+    s = X.slash_importance(q, k, 0.8, 1)
+    c = X.probe_importance(q, k, 0.8, 1)
+    assert np.allclose(s, c[::-1], rtol=1e-13, atol=1e-15)
+
+
+def test_slash_importance_equal_keys_closed_form():
+    """Equal keys: probe row r is uniform over keys 0..r, so line o collects 1/(r+1) from every
+    probe row r >= o."""
+    L, D, P = 150, 8, 64
+    q = RNG.standard_normal((L, D))
+    k = np.tile(RNG.standard_normal((1, D)), (L, 1))
+    imp = X.slash_importance(q, k, 0.7, P)
+    rows = np.arange(L - P, L)
+    expect = np.array([np.sum(1.0 / (rows[rows >= o] + 1)) for o in range(L)])
+    assert np.allclose(imp, expect, rtol=1e-12, atol=1e-14)
+
+
+def test_planted_slash_is_selected():
+    """Key r - o* made parallel to query row r for every probe row r: line o* carries most of
+    each probe row's mass and is the top offset."""
+    B, L, Hq, D, ostar = 1, 400, 1, 32, 37
+    q, k = _qk(B, L, Hq, 1, D, 21)
+    k *= 0.1
+    for r in range(L - 64, L):
+        k[0, r - ostar, 0] = 40.0 * q[0, r, 0] / np.dot(q[0, r, 0], q[0, r, 0])
+    cp, ci, sp, si, cimp, simp = X.build_vslash_index(q, k, 0.25, 4, 3)
+    assert ostar in list(si[sp[0]:sp[1]])
+    assert simp[0, 0].argmax() == ostar and simp[0, 0, ostar] > 0.5 * 64
+    assert list(ci[cp[0]:cp[1]]) == list(X.select_columns(cimp[0, 0], 4))
+
+
+def test_vslash_counts_and_order():
+    B, L, Hq, Hkv, D = 2, 200, 4, 2, 8
+    q, k = _qk(B, L, Hq, Hkv, D, 22)
+    cp, ci, sp, si, _, _ = X.build_vslash_index(q, k, 0.3, 17, 9)
+    for bh in range(B * Hq):
+        offs = si[sp[bh]:sp[bh + 1]]
+        assert offs.size == 9 and np.all(np.diff(offs) > 0) and offs[0] >= 0 and offs[-1] < L
+        assert ci[cp[bh]:cp[bh + 1]].size == 17
+
+
 # ---- planted mistakes: each must make some pin above fail ------------------------------------
 
 def _pins():
@@ -151,7 +207,11 @@ def _pins():
             test_block_scores_grow_with_key_block, test_planted_block_is_selected,
             test_probe_importance_equal_keys_closed_form, test_probe_uses_all_rows_when_short,
             test_equal_keys_columns_go_to_lowest_indices, test_planted_column_is_selected,
-            test_counts_order_and_causality, test_gqa_head_map_contiguous_groups]
+            test_counts_order_and_causality, test_gqa_head_map_contiguous_groups,
+            test_slash_importance_sums_to_probe_rows,
+            test_slash_importance_single_probe_row_reverses_columns,
+            test_slash_importance_equal_keys_closed_form, test_planted_slash_is_selected,
+            test_vslash_counts_and_order]
 
 
 def _some_pin_fails():
@@ -215,6 +275,24 @@ def _pool_first_row(x, block):
     return np.stack([x[i * block] for i in range(n)]).astype(np.float64)
 
 
+def _slash_mutant(key_of, rows_of=None):
+    def imp_fn(q_head, k_head, scale, probe):
+        L = q_head.shape[0]
+        rows = np.arange(max(0, L - probe), L) if rows_of is None else rows_of(L, probe)
+        s = scale * (q_head[rows] @ k_head.T)
+        s[np.arange(L)[None, :] > rows[:, None]] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        imp = np.zeros(L)
+        for a, r in enumerate(rows):
+            for o in range(L):
+                j = key_of(r, o)
+                if 0 <= j < L:
+                    imp[o] += p[a, j]
+        return imp
+    return imp_fn
+
+
 MUTANTS = {
     "blocks_ascending": ("select_blocks", _sel_blocks_ascending),
     "blocks_ties_high": ("select_blocks", _sel_blocks_ties_high),
@@ -224,6 +302,10 @@ MUTANTS = {
     "probe_unnormalised": ("probe_importance", _probe_unnormalised),
     "columns_ties_high": ("select_columns", _cols_ties_high),
     "pool_first_row": ("pooled_rows", _pool_first_row),
+    "slash_above_diagonal": ("slash_importance", _slash_mutant(lambda r, o: r + o)),
+    "slash_off_by_one": ("slash_importance", _slash_mutant(lambda r, o: r - o - 1)),
+    "slash_first_rows": ("slash_importance",
+                         _slash_mutant(lambda r, o: r - o, lambda L, P: np.arange(min(P, L)))),
 }
 
 
