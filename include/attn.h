@@ -212,8 +212,31 @@ int attn_build_sparse_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int
 int attn_sparse_index_sizes(int B, int Hq, int L, int topk_blocks, int n_cols,
                             int64_t* n_blk_idx, int64_t* n_col_idx);
 
-/* Workspace bytes attn_build_sparse_index needs (0 on invalid sizes). */
+/* Workspace bytes attn_build_sparse_index and attn_build_vslash_index need (0 on invalid
+ * sizes). */
 size_t attn_sparse_index_workspace_bytes(int B, int Hq, int Hkv, int L, int D);
+
+/*
+ * attn_build_vslash_index — builds, from Q and K, the column and slash-line lists that
+ * attn_fwd_vertical_slash consumes (square causal sizes: Lq = Lk = L), with the same probe as
+ * attn_build_sparse_index (the last min(64, L) query rows, each with its causal softmax over
+ * the keys; MInference article, paragraphs on the vertical-slash pattern and on dynamic
+ * indices, which name no estimator):
+ *   - columns: as attn_build_sparse_index;
+ *   - slash lines: line o (probe row r meets key r - o) scores the sum over probe rows of
+ *     their probability on that key; the top min(n_slash, L) offsets (ties to the lower
+ *     offset) are listed, sorted ascending.
+ * Outputs (DEVICE int32, caller-owned): col_ptr [B*Hq + 1], col_idx [B*Hq*min(n_cols, L)],
+ * slash_ptr [B*Hq + 1], slash_idx [B*Hq*min(n_slash, L)] (an index array may be NULL when
+ * its size is 0). workspace: as attn_build_sparse_index (attn_sparse_index_workspace_bytes).
+ * Limits: D in {64, 128}, L <= 131072, n_cols >= 0, n_slash >= 0. Errors: INVALID_ARG for bad
+ * sizes, scale, pointers or alignment; UNSUPPORTED for D or L beyond the limits; WORKSPACE;
+ * LAUNCH. Deterministic: every reduction runs in a fixed order.
+ */
+int attn_build_vslash_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int Hkv, int L,
+                            int D, float scale, int n_cols, int n_slash, int32_t* col_ptr,
+                            int32_t* col_idx, int32_t* slash_ptr, int32_t* slash_idx,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

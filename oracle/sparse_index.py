@@ -106,8 +106,7 @@ def slash_importance(q_head: np.ndarray, k_head: np.ndarray, scale: float, probe
     p /= p.sum(axis=1, keepdims=True)
     imp = np.zeros(L)
     for a, r in enumerate(rows):
-        for o in range(r + 1):
-            imp[o] += p[a, r - o]
+        imp[:r + 1] += p[a, r::-1]     # offsets 0..r meet keys r, r-1, ..., 0
     return imp
 
 

@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     attn_build_sparse_index,
     attn_sparse_index_sizes,
     attn_sparse_index_workspace_bytes,
+    attn_build_vslash_index,
     attn_status_string,
     attn_last_error,
     splitkv_decode,

@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "attn_build_sparse_index",
     "attn_sparse_index_sizes",
     "attn_sparse_index_workspace_bytes",
+    "attn_build_vslash_index",
     "attn_status_string",
     "attn_last_error",
 )
@@ -106,6 +107,9 @@ def load_library():
     lib.attn_sparse_index_sizes.restype = i32
     lib.attn_sparse_index_workspace_bytes.argtypes = [i32] * 5
     lib.attn_sparse_index_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_build_vslash_index.argtypes = [T, T, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp,
+                                            vp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_build_vslash_index.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
@@ -353,3 +357,32 @@ def attn_build_sparse_index(q, k, topk_blocks, n_cols, scale=None, outputs=None,
         ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(stream, q.device))
     _check("attn_build_sparse_index", st)
     return blk_ptr, blk_idx[:nb], col_ptr, col_idx[:nc]
+
+
+def attn_build_vslash_index(q, k, n_cols, n_slash, scale=None, outputs=None, workspace=None,
+                            stream=None):
+    """Column and slash-line lists (CSR, int32 GPU tensors: col_ptr, col_idx, slash_ptr,
+    slash_idx) for attn_fwd_vertical_slash, built from Q [B, L, Hq, D] and K [B, L, Hkv, D]
+    with the library's probe (see include/attn.h). Allocates the outputs and the workspace
+    with torch unless given."""
+    torch = _torch()
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = D ** -0.5
+    nc = B * Hq * min(int(n_cols), L)
+    ns = B * Hq * min(int(n_slash), L)
+    if outputs is None:
+        mk = lambda n: torch.empty(max(int(n), 1), dtype=torch.int32, device=q.device)
+        outputs = (mk(B * Hq + 1), mk(nc), mk(B * Hq + 1), mk(ns))
+    col_ptr, col_idx, slash_ptr, slash_idx = outputs
+    wsb = attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    st = load_library().attn_build_vslash_index(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), B, Hq, Hkv, L, D, float(scale), int(n_cols),
+        int(n_slash), _int_ptr(col_ptr, "col_ptr"), _int_ptr(col_idx, "col_idx"),
+        _int_ptr(slash_ptr, "slash_ptr"), _int_ptr(slash_idx, "slash_idx"),
+        ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(stream, q.device))
+    _check("attn_build_vslash_index", st)
+    return col_ptr, col_idx[:nc], slash_ptr, slash_idx[:ns]

@@ -243,7 +243,7 @@ int attn_build_sparse_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int
     if (st != ATTN_OK) return st;
     const attn::IndexWorkspace ws = attn::index_workspace(B, Hq, Hkv, L, D);
     char* wb = static_cast<char*>(workspace);
-    attn::IndexArgs a;
+    attn::IndexArgs a{};
     a.q = static_cast<const uint16_t*>(q.data);
     a.k = static_cast<const uint16_t*>(k.data);
     a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
@@ -261,7 +261,46 @@ int attn_build_sparse_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int
     a.stats = reinterpret_cast<float*>(wb + ws.stats);
     a.fin = reinterpret_cast<float*>(wb + ws.fin);
     a.imp = reinterpret_cast<float*>(wb + ws.imp);
+    a.simp = reinterpret_cast<float*>(wb + ws.simp);
     return launch_status(fn, attn::launch_build_index(a, D, static_cast<hipStream_t>(stream)));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_build_vslash_index(attn_tensor_t q, attn_tensor_t k, int B, int Hq, int Hkv, int L, int D,
+                            float scale, int n_cols, int n_slash, int32_t* col_ptr,
+                            int32_t* col_idx, int32_t* slash_ptr, int32_t* slash_idx,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_build_vslash_index";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_vslash_index_args(fn, q, k, B, Hq, Hkv, L, D, scale, n_cols, n_slash,
+                                           col_ptr, col_idx, slash_ptr, slash_idx, workspace,
+                                           workspace_bytes);
+    if (st != ATTN_OK) return st;
+    const attn::IndexWorkspace ws = attn::index_workspace(B, Hq, Hkv, L, D);
+    char* wb = static_cast<char*>(workspace);
+    attn::IndexArgs a{};
+    a.q = static_cast<const uint16_t*>(q.data);
+    a.k = static_cast<const uint16_t*>(k.data);
+    a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
+    a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L;
+    a.scale = scale;
+    a.sl2 = scale * kLog2e;
+    a.ncols = n_cols;
+    a.nslash = n_slash;
+    a.col_ptr = col_ptr; a.col_idx = col_idx;
+    a.sl_ptr = slash_ptr; a.sl_idx = slash_idx;
+    a.stats = reinterpret_cast<float*>(wb + ws.stats);
+    a.fin = reinterpret_cast<float*>(wb + ws.fin);
+    a.imp = reinterpret_cast<float*>(wb + ws.imp);
+    a.simp = reinterpret_cast<float*>(wb + ws.simp);
+    return launch_status(fn, attn::launch_build_vslash_index(a, D,
+                                                             static_cast<hipStream_t>(stream)));
   } catch (const std::exception& e) {
     return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
   } catch (...) {

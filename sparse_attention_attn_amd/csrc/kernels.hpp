@@ -90,6 +90,10 @@ struct IndexArgs {
   float* stats;        // workspace: probe softmax statistics [B, Hq, nchunks, 64, 2]
   float* fin;          // workspace: per probe row, max + log2(sum) over all keys [B, Hq, 64]
   float* imp;          // workspace: column importance [B, Hq, L]
+  float* simp;         // workspace: slash-line importance [B, Hq, L] (vertical-slash builder)
+  int nslash;          // slash lines listed per head (vertical-slash builder)
+  int32_t* sl_ptr;     // [B*Hq + 1] (vertical-slash builder)
+  int32_t* sl_idx;     // [B*Hq*min(nslash, L)] (vertical-slash builder)
 };
 
 // Rows per pooled block, the largest block count one list builder workgroup sorts, probe rows,
@@ -102,6 +106,7 @@ constexpr int kProbeChunk = 1024;
 hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_build_index(const IndexArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_vslash(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_build_vslash_index(const IndexArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);

@@ -462,6 +462,67 @@ __global__ __launch_bounds__(256) void probe_importance_kernel(const IndexArgs a
   }
 }
 
+// Slash lines, per (b, h, 64 offsets o0 .. o0+63): probe row r = r0 + pr meets line o at key
+// r - o, so the chunk needs keys r0 - o0 - 63 .. r0 - o0 + 63, a 128-key window. Wave w forms
+// C[row][key] = Q_probe . K^T for window keys 32w .. 32w+31 (the importance pass's layout),
+// turns it into probabilities and stores them in LDS as pl[pr][window key]; then lane t of
+// wave 0 sums line o0 + t, pl[pr][pr - t + 63] over pr in order.
+template <int D>
+__global__ __launch_bounds__(256) void probe_slash_kernel(const IndexArgs a, const float* fin,
+                                                          float* simp) {
+  constexpr int KS = D / 16;
+  __shared__ float pl[kProbeRows][128 + 1];
+  const int nsc = (a.L + 63) / 64;
+  int id = (int)blockIdx.x;
+  const int sc = id % nsc;
+  id /= nsc;
+  const int h = id % a.Hq;
+  const int b = id / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int bh = b * a.Hq + h;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int l = (int)threadIdx.x & 63;
+  const int P = min(kProbeRows, a.L);
+  const int r0 = a.L - P;
+  const int o0 = sc * 64;
+  const int kw0 = r0 - o0 - 63;  // window key 0
+  bf16x8 qop[2][KS];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) load_probe_q<D>(a, b, h, mt * 32 + (l & 31), qop[mt]);
+  float c[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      c[mt][j] = fin[bh * 64 + mt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3)];
+  const int kk = 32 * w + (l & 31);  // this lane's window key
+  const int key = kw0 + kk;
+  const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
+  bf16x8 kop[KS];
+  load_half_row<D>(kbase + (int64_t)min(max(key, 0), a.L - 1) * a.k_sl, kop);
+  f32x16 acc[2] = {};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    acc[0] = mfma32(qop[0][s], kop[s], acc[0]);
+    acc[1] = mfma32(qop[1][s], kop[s], acc[1]);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int pr = mt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3);
+      const float p = fast_exp2(fmaf(acc[mt][j], a.sl2, -c[mt][j]));
+      pl[pr][kk] = (key < 0 || key > r0 + pr) ? 0.f : p;
+    }
+  __syncthreads();
+  if (w == 0) {
+    const int o = o0 + l;
+    float t = 0.f;
+    for (int pr = 0; pr < P; ++pr) t += pl[pr][pr - l + 63];
+    if (o < a.L) simp[(int64_t)bh * a.L + o] = t;
+  }
+}
+
 // ---- column lists: one workgroup (1024 threads) per (b, h) -----------------------------------
 // Radix select (four 8-bit digits of the non-negative fp32 bit patterns) finds the n-th largest
 // importance T and how many of the keys equal to T to take. Then each wave takes a contiguous
@@ -590,7 +651,32 @@ hipError_t launch_index_t(const IndexArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_vslash_index_t(const IndexArgs& a, hipStream_t stream) {
+  const int nch = (a.L + kProbeChunk - 1) / kProbeChunk;
+  const int nsc = (a.L + 63) / 64;
+  const int nbh = a.B * a.Hq;
+  hipLaunchKernelGGL((probe_stats_kernel<D>), dim3((unsigned)(nbh * nch)), dim3(256), 0, stream,
+                     a, a.stats);
+  hipLaunchKernelGGL(probe_combine_kernel, dim3((unsigned)nbh), dim3(64), 0, stream, a.stats,
+                     a.L, nch, a.fin);
+  hipLaunchKernelGGL((probe_importance_kernel<D>), dim3((unsigned)(nbh * nch)), dim3(256), 0,
+                     stream, a, a.fin, a.imp);
+  hipLaunchKernelGGL((probe_slash_kernel<D>), dim3((unsigned)(nbh * nsc)), dim3(256), 0, stream,
+                     a, a.fin, a.simp);
+  hipLaunchKernelGGL(col_topk_kernel, dim3((unsigned)nbh), dim3(1024), 0, stream, a.imp, a.L,
+                     a.ncols, a.col_ptr, a.col_idx, nbh);
+  hipLaunchKernelGGL(col_topk_kernel, dim3((unsigned)nbh), dim3(1024), 0, stream, a.simp, a.L,
+                     a.nslash, a.sl_ptr, a.sl_idx, nbh);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_build_vslash_index(const IndexArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_vslash_index_t<128>(a, stream);
+  return launch_vslash_index_t<64>(a, stream);
+}
 
 hipError_t launch_build_index(const IndexArgs& a, int d, hipStream_t stream) {
   if (d == 128) return launch_index_t<128>(a, stream);

@@ -250,7 +250,7 @@ int64_t index_blk_head_len(int L, int topk) {
 }
 
 IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D) {
-  IndexWorkspace w{0, 0, 0, 0, 0, 0};
+  IndexWorkspace w{0, 0, 0, 0, 0, 0, 0};
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || D < 1) return w;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t nqb = (size_t)(L + 63) / 64;
@@ -261,6 +261,7 @@ IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D) {
   w.stats = off; off = up(off + (size_t)B * Hq * nch * 64 * 2 * 4);
   w.fin = off; off = up(off + (size_t)B * Hq * 64 * 4);
   w.imp = off; off = up(off + (size_t)B * Hq * L * 4);
+  w.simp = off; off = up(off + (size_t)B * Hq * L * 4);
   w.total = off;
   return w;
 }
@@ -302,6 +303,54 @@ int check_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t
     return fail(ATTN_ERR_INVALID_ARG, fn, "an output list pointer is NULL");
   if (!aligned4(blk_ptr) || !aligned4(blk_idx) || !aligned4(col_ptr) ||
       (col_idx != nullptr && !aligned4(col_idx)))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "output lists must be 4-byte aligned");
+  const size_t need = index_workspace(B, Hq, Hkv, L, D).total;
+  if (workspace == nullptr || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) {
+    std::ostringstream s;
+    s << "workspace must be non-NULL, 256-byte aligned and at least " << need << " bytes";
+    return fail(ATTN_ERR_WORKSPACE, fn, s.str());
+  }
+  return ATTN_OK;
+}
+
+int check_vslash_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k, int B,
+                            int Hq, int Hkv, int L, int D, float scale, int ncols, int nslash,
+                            const int32_t* col_ptr, const int32_t* col_idx,
+                            const int32_t* slash_ptr, const int32_t* slash_idx,
+                            const void* workspace, size_t workspace_bytes) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1) {
+    std::ostringstream s;
+    s << "sizes must be >= 1 (B=" << B << " Hq=" << Hq << " Hkv=" << Hkv << " L=" << L << ")";
+    return fail(ATTN_ERR_INVALID_ARG, fn, s.str());
+  }
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, fn, "Hq must be a multiple of Hkv");
+  if (ncols < 0) return fail(ATTN_ERR_INVALID_ARG, fn, "n_cols must be >= 0");
+  if (nslash < 0) return fail(ATTN_ERR_INVALID_ARG, fn, "n_slash must be >= 0");
+  if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, fn, "scale is not finite");
+  if (D != 64 && D != 128) {
+    std::ostringstream s;
+    s << "D=" << D << " not supported (64, 128)";
+    return fail(ATTN_ERR_UNSUPPORTED, fn, s.str());
+  }
+  if (L > kIndexMaxL) {
+    std::ostringstream s;
+    s << "L=" << L << " exceeds the index builder's limit of " << kIndexMaxL;
+    return fail(ATTN_ERR_UNSUPPORTED, fn, s.str());
+  }
+  int st;
+  if ((st = check_tensor(fn, "q", q)) != ATTN_OK) return st;
+  if ((st = check_tensor(fn, "k", k)) != ATTN_OK) return st;
+  const int64_t ncol = (int64_t)B * Hq * std::min(ncols, L);
+  const int64_t nsl = (int64_t)B * Hq * std::min(nslash, L);
+  const int64_t imax = std::numeric_limits<int32_t>::max();
+  if (ncol > imax || nsl > imax)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "an index list would exceed 2^31 entries");
+  if (col_ptr == nullptr || slash_ptr == nullptr || (ncol > 0 && col_idx == nullptr) ||
+      (nsl > 0 && slash_idx == nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "an output list pointer is NULL");
+  if (!aligned4(col_ptr) || !aligned4(slash_ptr) || (col_idx != nullptr && !aligned4(col_idx)) ||
+      (slash_idx != nullptr && !aligned4(slash_idx)))
     return fail(ATTN_ERR_INVALID_ARG, fn, "output lists must be 4-byte aligned");
   const size_t need = index_workspace(B, Hq, Hkv, L, D).total;
   if (workspace == nullptr || workspace_bytes < need ||

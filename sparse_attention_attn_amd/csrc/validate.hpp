@@ -63,13 +63,19 @@ int check_slash_lists(const char* fn, const int32_t* slash_ptr, const int32_t* s
 int64_t index_blk_head_len(int L, int topk);
 // Workspace layout (byte offsets, 256-byte aligned) and total size.
 struct IndexWorkspace {
-  size_t qbar, kbar, stats, fin, imp, total;
+  size_t qbar, kbar, stats, fin, imp, simp, total;
 };
 IndexWorkspace index_workspace(int B, int Hq, int Hkv, int L, int D);
 int check_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k, int B, int Hq,
                      int Hkv, int L, int D, float scale, int topk, int ncols,
                      const int32_t* blk_ptr, const int32_t* blk_idx, const int32_t* col_ptr,
                      const int32_t* col_idx, const void* workspace, size_t workspace_bytes);
+
+int check_vslash_index_args(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k, int B,
+                            int Hq, int Hkv, int L, int D, float scale, int ncols, int nslash,
+                            const int32_t* col_ptr, const int32_t* col_idx,
+                            const int32_t* slash_ptr, const int32_t* slash_idx,
+                            const void* workspace, size_t workspace_bytes);
 
 const char* status_string(int status);
 

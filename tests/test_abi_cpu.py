@@ -240,6 +240,28 @@ def test_build_sparse_index_validation(kw, code, frag):
     assert frag in S.attn_last_error()
 
 
+def _build_vs(ncols=16, nslash=16, ws=FAKE, ws_bytes=None, ptrs=(FAKE, FAKE, FAKE, FAKE), D=128,
+              L=1000):
+    if ws_bytes is None:
+        ws_bytes = S.attn_sparse_index_workspace_bytes(1, 4, 2, L, D)
+    return _lib().attn_build_vslash_index(_t(), _t(), 1, 4, 2, L, D, ctypes.c_float(0.1), ncols,
+                                          nslash, *ptrs, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw, code, frag", [
+    (dict(ncols=-1), S.ATTN_ERR_INVALID_ARG, "n_cols"),
+    (dict(nslash=-2), S.ATTN_ERR_INVALID_ARG, "n_slash"),
+    (dict(D=96), S.ATTN_ERR_UNSUPPORTED, "D=96"),
+    (dict(L=131073), S.ATTN_ERR_UNSUPPORTED, "limit"),
+    (dict(ptrs=(FAKE, FAKE, None, FAKE)), S.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(ptrs=(FAKE, FAKE, FAKE, FAKE + 1)), S.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(ws_bytes=100), S.ATTN_ERR_WORKSPACE, "workspace"),
+])
+def test_build_vslash_index_validation(kw, code, frag):
+    assert _build_vs(**kw) == code
+    assert frag in S.attn_last_error()
+
+
 def test_sparse_index_sizes_closed_form():
     # L = 1000: 16 query blocks; topk 8 -> 1+2+...+8 + 8*8 = 100 entries per head
     nb, nc = S.attn_sparse_index_sizes(2, 4, 1000, 8, 16)

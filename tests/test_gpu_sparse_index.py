@@ -188,3 +188,114 @@ def test_build_index_negative_scale():
     q = randn_bf16((1, 1500, 4, 128), 9600)
     k = randn_bf16((1, 1500, 2, 128), 9601)
     _compare(q, k, 6, 80, -0.08, "negative scale")
+
+
+# ---- vertical-slash lists (attn_build_vslash_index) -----------------------------------------
+def _build_vs(q, k, ncols, nslash, scale):
+    import torch
+    import sparse_attention_attn_amd as S
+    out = S.attn_build_vslash_index(q.to(DEV), k.to(DEV), ncols, nslash, scale=scale)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def _compare_vs(q, k, ncols, nslash, scale, label):
+    B, L, Hq, D = q.shape
+    cp, ci, sp, si = _build_vs(q, k, ncols, nslash, scale)
+    rcp, rci, rsp, rsi, cimp, simp = X.build_vslash_index(to_f64(q), to_f64(k),
+                                                          float(np.float32(scale)), ncols, nslash)
+    assert np.array_equal(cp, rcp) and np.array_equal(sp, rsp), f"{label}: pointers"
+    for r in range(B * Hq):
+        b, h = divmod(r, Hq)
+        _check_topk_set(ci[cp[r]:cp[r + 1]], rci[rcp[r]:rcp[r + 1]], cimp[b, h], ncols, set(),
+                        f"{label} columns b={b} h={h}")
+        _check_topk_set(si[sp[r]:sp[r + 1]], rsi[rsp[r]:rsp[r + 1]], simp[b, h], nslash, set(),
+                        f"{label} slashes b={b} h={h}")
+    return cp, ci, sp, si
+
+
+VS_SHAPES = [
+    # B, Hq, Hkv, L, D, ncols, nslash
+    (1, 4, 2, 64, 128, 10, 10),
+    (2, 4, 2, 200, 128, 30, 40),
+    (1, 2, 1, 1000, 64, 100, 70),
+    (1, 4, 4, 2049, 128, 5000, 3000),   # more than L: everything listed
+    (1, 8, 2, 3000, 128, 0, 25),
+    (1, 2, 2, 40, 128, 7, 7),           # L < 64: every row probes
+]
+
+
+@pytest.mark.parametrize("shape", VS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_build_vslash_index_matches_oracle(shape):
+    B, Hq, Hkv, L, D, ncols, nslash = shape
+    say(f"vslash index {shape}")
+    q = randn_bf16((B, L, Hq, D), 9700 + L)
+    k = randn_bf16((B, L, Hkv, D), 9701 + L)
+    _compare_vs(q, k, ncols, nslash, D ** -0.5, f"vs{shape}")
+
+
+def test_build_vslash_index_planted_diagonal():
+    B, Hq, Hkv, L, D, ostar = 1, 2, 1, 1500, 128, 333
+    say("vslash index planted diagonal")
+    q = randn_bf16((B, L, Hq, D), 9800).float()
+    k = randn_bf16((B, L, Hkv, D), 9801).float() * 0.1
+    for r in range(L - 64, L):
+        qr = q[0, r, 0]
+        k[0, r - ostar, 0] = 60.0 * qr / qr.dot(qr)
+    q, k = q.bfloat16(), k.bfloat16()
+    cp, ci, sp, si = _compare_vs(q, k, 20, 5, D ** -0.5, "planted diagonal")
+    assert ostar in list(si[sp[0]:sp[1]])
+
+
+def test_built_vslash_lists_drive_forward():
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Hq, Hkv, L, D = 1, 4, 2, 1300, 128
+    say("vslash index -> vertical-slash forward")
+    q = randn_bf16((B, L, Hq, D), 9900)
+    k = randn_bf16((B, L, Hkv, D), 9901)
+    v = randn_bf16((B, L, Hkv, D), 9902)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    cp, ci, sp, si = S.attn_build_vslash_index(qd, kd, 60, 90, scale=D ** -0.5)
+    nqb = -(-L // 64)
+    bp = torch.zeros(B * Hq * nqb + 1, dtype=torch.int32, device=DEV)
+    bi = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
+    S.attn_fwd_vertical_slash(qd, kd, vd, o, bp, bi, cp, ci, sp, si, lse=lse, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    hcp, hci, hsp, hsi = [t.cpu().numpy() for t in (cp, ci, sp, si)]
+    S.attn_vertical_slash_check(hsp, hsi, B, Hq, L)
+    fn = A.vslash_allowed_fn(np.zeros(B * Hq * nqb + 1, np.int32), np.zeros(0, np.int32), hcp,
+                             hci, hsp, hsi, Hq, nqb, L, L)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
+                                 True, allowed_fn=fn)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "vslash index -> forward")
+
+
+def test_build_vslash_index_full_size_sampled():
+    """The 128K shape, 1000 columns and 1088 lines per head: two heads against the oracle."""
+    w = WORKLOADS["vslash_128k"]
+    say(f"vslash index full size {w.name}")
+    q, k, _ = make_qkv(w)
+    ncols, nslash = 1000, 1088
+    cp, ci, sp, si = _build_vs(q, k, ncols, nslash, w.scale)
+    sc = float(np.float32(w.scale))
+    for h in (3, 30):
+        qh = q[0, :, h].double().numpy()
+        kh = k[0, :, h // (w.Hq // w.Hkv)].double().numpy()
+        cimp = X.probe_importance(qh, kh, sc, 64)
+        simp = X.slash_importance(qh, kh, sc, 64)
+        _check_topk_set(ci[cp[h]:cp[h + 1]], X.select_columns(cimp, ncols), cimp, ncols, set(),
+                        f"full columns h={h}")
+        _check_topk_set(si[sp[h]:sp[h + 1]], X.select_columns(simp, nslash), simp, nslash, set(),
+                        f"full slashes h={h}")
+
+
+def test_build_vslash_index_deterministic():
+    say("vslash index determinism")
+    q = randn_bf16((1, 2500, 4, 128), 9950)
+    k = randn_bf16((1, 2500, 2, 128), 9951)
+    a = _build_vs(q, k, 100, 200, 0.09)
+    b = _build_vs(q, k, 100, 200, 0.09)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
