@@ -240,8 +240,35 @@ def bench_vslash(w, steps, warmup):
     pairs = vslash_pairs(sp, si, cp, ci, w.B, w.Hq, w.Lq)
     flops = 2 * (w.Dqk + w.Dv) * pairs
     dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
-    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
-            "density_vs_causal": pairs / dense}
+    res = {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+           "density_vs_causal": pairs / dense}
+    # Lists built from Q and K at run time (attn_build_vslash_index), as many columns and lines
+    # as the synthetic lists. Random inputs have no diagonal structure, so the chosen lines
+    # scatter over all offsets and the forward then visits nearly every causal block.
+    ncols, nslash = 1000, int(sp[1] - sp[0])
+    nc, ns = w.B * w.Hq * min(ncols, w.Lk), w.B * w.Hq * min(nslash, w.Lk)
+    outs = (torch.empty(w.B * w.Hq + 1, dtype=torch.int32, device="cuda:0"),
+            torch.empty(nc, dtype=torch.int32, device="cuda:0"),
+            torch.empty(w.B * w.Hq + 1, dtype=torch.int32, device="cuda:0"),
+            torch.empty(ns, dtype=torch.int32, device="cuda:0"))
+    iws = torch.empty(S.attn_sparse_index_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Dqk),
+                      dtype=torch.uint8, device="cuda:0")
+    build = lambda: S.attn_build_vslash_index(q, k, ncols, nslash, scale=w.scale, outputs=outs,
+                                              workspace=iws)
+    ms_b, _ = time_steps(build, steps, warmup)
+    bcp, bci, bsp, bsi = build()
+    step_d = lambda: (build(), S.attn_fwd_vertical_slash(q, k, v, o, bp, bi, bcp, bci, bsp, bsi,
+                                                         lse=lse, causal=True, scale=w.scale,
+                                                         workspace=ws))
+    ms_d, _ = time_steps(step_d, 2, 1)
+    hl = [t.cpu().numpy() for t in (bsp, bsi, bcp, bci)]
+    pairs_d = vslash_pairs(*hl, w.B, w.Hq, w.Lq)
+    res["dynamic"] = {"index_build_ms": round(ms_b, 4), "build_plus_attention_ms": round(ms_d, 4),
+                      "n_cols": ncols, "n_slash": nslash,
+                      "density_vs_causal": round(pairs_d / dense, 4),
+                      "tflops_incl_build": round(2 * (w.Dqk + w.Dv) * pairs_d / (ms_d * 1e-3)
+                                                 / 1e12, 3)}
+    return res
 
 
 def mla_causal_pairs(lq, lk):

@@ -462,14 +462,15 @@ __global__ __launch_bounds__(256) void probe_importance_kernel(const IndexArgs a
   }
 }
 
-// Slash lines, per (b, h, 64 offsets o0 .. o0+63): probe row r = r0 + pr meets line o at key
-// r - o, so the chunk needs keys r0 - o0 - 63 .. r0 - o0 + 63, a 128-key window. Wave w forms
-// C[row][key] = Q_probe . K^T for window keys 32w .. 32w+31 (the importance pass's layout),
-// turns it into probabilities and stores them in LDS as pl[pr][window key]; then lane t of
-// wave 0 sums line o0 + t, pl[pr][pr - t + 63] over pr in order.
+// Slash lines, per (b, h, 64 offsets o0 .. o0+63), one wave: probe row r = r0 + pr meets line
+// o at key r - o, so the chunk needs keys r0 - o0 - 63 .. r0 - o0 + 63, a 128-key window. For
+// each 32-key tile of the window the wave forms C[row][key] = Q_probe . K^T (the importance
+// pass's layout, probe Q loaded once for the four tiles), turns it into probabilities and
+// stores them in LDS as pl[pr][window key]; then lane t sums line o0 + t,
+// pl[pr][pr - t + 63] over pr in order (rows >= P hold zeros).
 template <int D>
-__global__ __launch_bounds__(256) void probe_slash_kernel(const IndexArgs a, const float* fin,
-                                                          float* simp) {
+__global__ __launch_bounds__(64) void probe_slash_kernel(const IndexArgs a, const float* fin,
+                                                         float* simp) {
   constexpr int KS = D / 16;
   __shared__ float pl[kProbeRows][128 + 1];
   const int nsc = (a.L + 63) / 64;
@@ -480,8 +481,7 @@ __global__ __launch_bounds__(256) void probe_slash_kernel(const IndexArgs a, con
   const int b = id / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int bh = b * a.Hq + h;
-  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int l = (int)threadIdx.x & 63;
+  const int l = (int)threadIdx.x;
   const int P = min(kProbeRows, a.L);
   const int r0 = a.L - P;
   const int o0 = sc * 64;
@@ -495,32 +495,33 @@ __global__ __launch_bounds__(256) void probe_slash_kernel(const IndexArgs a, con
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       c[mt][j] = fin[bh * 64 + mt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3)];
-  const int kk = 32 * w + (l & 31);  // this lane's window key
-  const int key = kw0 + kk;
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hk * a.k_sh;
-  bf16x8 kop[KS];
-  load_half_row<D>(kbase + (int64_t)min(max(key, 0), a.L - 1) * a.k_sl, kop);
-  f32x16 acc[2] = {};
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    acc[0] = mfma32(qop[0][s], kop[s], acc[0]);
-    acc[1] = mfma32(qop[1][s], kop[s], acc[1]);
-  }
+  for (int kt = 0; kt < 4; ++kt) {
+    const int kk = 32 * kt + (l & 31);  // this lane's window key
+    const int key = kw0 + kk;
+    bf16x8 kop[KS];
+    load_half_row<D>(kbase + (int64_t)min(max(key, 0), a.L - 1) * a.k_sl, kop);
+    f32x16 acc[2] = {};
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int pr = mt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3);
-      const float p = fast_exp2(fmaf(acc[mt][j], a.sl2, -c[mt][j]));
-      pl[pr][kk] = (key < 0 || key > r0 + pr) ? 0.f : p;
+    for (int s = 0; s < KS; ++s) {
+      acc[0] = mfma32(qop[0][s], kop[s], acc[0]);
+      acc[1] = mfma32(qop[1][s], kop[s], acc[1]);
     }
-  __syncthreads();
-  if (w == 0) {
-    const int o = o0 + l;
-    float t = 0.f;
-    for (int pr = 0; pr < P; ++pr) t += pl[pr][pr - l + 63];
-    if (o < a.L) simp[(int64_t)bh * a.L + o] = t;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int pr = mt * 32 + 8 * (j >> 2) + 4 * (l >> 5) + (j & 3);
+        const float p = fast_exp2(fmaf(acc[mt][j], a.sl2, -c[mt][j]));
+        pl[pr][kk] = (key < 0 || key > r0 + pr) ? 0.f : p;
+      }
   }
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int pr = 0; pr < kProbeRows; ++pr) t += pl[pr][pr - l + 63];
+  if (o0 + l < a.L) simp[(int64_t)bh * a.L + o0 + l] = t;
 }
 
 // ---- column lists: one workgroup (1024 threads) per (b, h) -----------------------------------
@@ -662,7 +663,7 @@ hipError_t launch_vslash_index_t(const IndexArgs& a, hipStream_t stream) {
                      a.L, nch, a.fin);
   hipLaunchKernelGGL((probe_importance_kernel<D>), dim3((unsigned)(nbh * nch)), dim3(256), 0,
                      stream, a, a.fin, a.imp);
-  hipLaunchKernelGGL((probe_slash_kernel<D>), dim3((unsigned)(nbh * nsc)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((probe_slash_kernel<D>), dim3((unsigned)(nbh * nsc)), dim3(64), 0, stream,
                      a, a.fin, a.simp);
   hipLaunchKernelGGL(col_topk_kernel, dim3((unsigned)nbh), dim3(1024), 0, stream, a.imp, a.L,
                      a.ncols, a.col_ptr, a.col_idx, nbh);
