@@ -157,15 +157,15 @@ def bench_decode(w, steps, warmup):
     o = torch.empty((w.B, w.Lq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda:0")
     lse = torch.empty((w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
     nsp = S.attn_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.Dqk, w.Dv)
-    op = torch.empty((nsp, w.B, w.Hq, w.Lq, w.Dv), dtype=torch.float32, device="cuda:0")
-    lp = torch.empty((nsp, w.B, w.Hq, w.Lq), dtype=torch.float32, device="cuda:0")
+    # one call per step: split-KV plus the combine (attn_fwd_decode)
+    ws = torch.zeros(S.attn_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.Dqk, w.Dv),
+                     dtype=torch.uint8, device="cuda:0")
     it = [0]
 
     def step():
         i = it[0] % ncopies
         it[0] += 1
-        S.attn_fwd_splitkv(qd, ks[i], vs[i], op, lp, causal=w.causal, scale=w.scale)
-        S.attn_combine_lse(op, lp, o, lse)
+        S.attn_fwd_decode(qd, ks[i], vs[i], o, lse, causal=w.causal, scale=w.scale, workspace=ws)
 
     ms, wall = time_steps(step, steps, warmup)
     nbytes = kv_bytes + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4

@@ -111,6 +111,24 @@ int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits,
                      attn_tensor_t o, float* lse, int B, int Hq, int Lq, int Dv, void* stream);
 
 /*
+ * attn_fwd_decode — split-KV decode and its LSE combine in one call: attn_fwd_splitkv with
+ * num_splits = attn_splitkv_num_splits(...) followed by attn_combine_lse, on one stream, with
+ * the partials in the caller's workspace. Arguments as attn_fwd; o is bf16 strided like
+ * attn_fwd's, lse fp32 [B, Hq, Lq] or NULL.
+ * workspace: DEVICE buffer of at least attn_decode_workspace_bytes(...) bytes, 256-byte
+ * aligned, owned by the caller; its contents on entry do not matter. Calls that overlap on
+ * one workspace race.
+ * Errors: as attn_fwd, plus WORKSPACE for a missing, short or misaligned workspace.
+ */
+int attn_fwd_decode(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                    float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                    int causal, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes of attn_fwd_decode for these sizes (0 on invalid sizes). */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
+
+/*
  * attn_fwd_blocksparse — attention over a per-query-head union of listed key blocks and
  * vertical key columns (the block-sparse / A-shape / vertical-slash index lists), with the
  * causal mask applied on top when `causal` is set. Each key is counted once even when it is

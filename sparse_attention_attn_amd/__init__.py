@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     attn_fwd,
     attn_fwd_splitkv,
     attn_combine_lse,
+    attn_fwd_decode,
+    attn_decode_workspace_bytes,
     attn_fwd_blocksparse,
     attn_splitkv_num_splits,
     attn_splitkv_workspace_bytes,

@@ -22,6 +22,8 @@ EXPORTED_SYMBOLS = (
     "attn_splitkv_workspace_bytes",
     "attn_fwd_splitkv",
     "attn_combine_lse",
+    "attn_fwd_decode",
+    "attn_decode_workspace_bytes",
     "attn_fwd_blocksparse",
     "attn_blocksparse_check",
     "attn_fwd_vertical_slash",
@@ -86,6 +88,11 @@ def load_library():
     lib.attn_fwd_splitkv.restype = i32
     lib.attn_combine_lse.argtypes = [vp, vp, i32, T, vp, i32, i32, i32, i32, vp]
     lib.attn_combine_lse.restype = i32
+    lib.attn_fwd_decode.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                    vp, ctypes.c_size_t, vp]
+    lib.attn_fwd_decode.restype = i32
+    lib.attn_decode_workspace_bytes.argtypes = [i32] * 7
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fwd_blocksparse.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                          f32, i32, i32, ip, ip, ip, ip, vp]
     lib.attn_fwd_blocksparse.restype = i32
@@ -240,6 +247,31 @@ def splitkv_decode(q, k, v, o, lse=None, causal=False, scale=None, num_splits=No
         o_part, lse_part = workspace
     attn_fwd_splitkv(q, k, v, o_part, lse_part, causal=causal, scale=scale, stream=stream)
     attn_combine_lse(o_part, lse_part, o, lse, stream=stream)
+    return o
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv))
+
+
+def attn_fwd_decode(q, k, v, o, lse=None, causal=False, scale=None, workspace=None, stream=None):
+    """Split-KV decode plus combine in one call; the partials go to `workspace` (allocated
+    here unless given)."""
+    torch = _torch()
+    B, Lq, Hq, Dqk = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
+    if scale is None:
+        scale = Dqk ** -0.5
+    if workspace is None:
+        workspace = torch.empty(attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv),
+                                dtype=torch.uint8, device=q.device)
+    st = load_library().attn_fwd_decode(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
+        _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device))
+    _check("attn_fwd_decode", st)
     return o
 
 

@@ -115,6 +115,62 @@ int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o
   }
 }
 
+int attn_fwd_decode(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o, float* lse,
+                    int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "attn_fwd_decode";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_attention_args(fn, attn::Op::kSplit, q, k, v, &o, lse, B, Hq, Hkv, Lq,
+                                        Lk, Dqk, Dv, scale);
+    if (st != ATTN_OK) return st;
+    const attn::DecodeWorkspace ws = attn::decode_workspace(B, Hq, Hkv, Lq, Lk, Dqk, Dv);
+    if (workspace == nullptr || workspace_bytes < ws.total ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) {
+      std::ostringstream m;
+      m << "workspace must be non-NULL, 256-byte aligned and at least " << ws.total << " bytes";
+      return attn::fail(ATTN_ERR_WORKSPACE, fn, m.str());
+    }
+    char* wb = static_cast<char*>(workspace);
+    attn::SplitArgs a;
+    a.q = static_cast<const uint16_t*>(q.data);
+    a.k = static_cast<const uint16_t*>(k.data);
+    a.v = static_cast<const uint16_t*>(v.data);
+    a.o_part = reinterpret_cast<float*>(wb + ws.o_part);
+    a.lse_part = reinterpret_cast<float*>(wb + ws.lse_part);
+    a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
+    a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
+    a.v_sb = v.stride_b; a.v_sl = v.stride_l; a.v_sh = v.stride_h;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
+    a.causal = causal ? 1 : 0;
+    a.off = Lk - Lq;
+    a.sl2 = scale * kLog2e;
+    a.num_splits = ws.num_splits;
+    a.chunk = attn::split_chunk(Lk, ws.num_splits);
+    const int cols = attn::split_cols(Dqk, a.g * Lq);
+    a.ncolblk = (a.g * Lq + cols - 1) / cols;
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    st = launch_status(fn, attn::launch_splitkv(a, Dqk, Dv, sm));
+    if (st != ATTN_OK) return st;
+    attn::CombineArgs c;
+    c.o_part = a.o_part;
+    c.lse_part = a.lse_part;
+    c.o = static_cast<uint16_t*>(o.data);
+    c.lse = lse;
+    c.o_sb = o.stride_b; c.o_sl = o.stride_l; c.o_sh = o.stride_h;
+    c.B = B; c.Hq = Hq; c.Lq = Lq; c.S = ws.num_splits;
+    return launch_status(fn, attn::launch_combine(c, Dv, sm));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
+  return attn::decode_workspace(B, Hq, Hkv, Lq, Lk, Dqk, Dv).total;
+}
+
 int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits, attn_tensor_t o,
                      float* lse, int B, int Hq, int Lq, int Dv, void* stream) {
   static const char* fn = "attn_combine_lse";

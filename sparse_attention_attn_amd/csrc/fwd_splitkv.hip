@@ -419,18 +419,19 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Combine: M = max_s LSE_s, w_s = exp(LSE_s - M), LSE = M + ln Σ w_s, O = Σ w_s O_s / Σ w_s.
-// One thread per (output row, 4 consecutive output columns); the loop over splits issues
-// independent 16-byte loads.
-// ------------------------------------------------------------------------------------------
 // One workgroup per output row (b, query head, position). Its 256 threads are CPB float4
-// columns x G split groups; group g handles splits g, g+G, ... so that many partial rows are
-// loaded at once, and the groups' sums meet in LDS. With M = max_s LSE_s and w_s =
-// exp(LSE_s - M): O = sum_s w_s O_s / sum_s w_s and LSE = M + ln(sum_s w_s); a split with no
-// visible key (LSE_s = -inf) has weight 0.
+// columns x G split groups; group g takes splits g, g+G, ..., up to kCombineInFlight of them per
+// pass with every load issued before any is used (one memory round trip for up to
+// G * kCombineInFlight splits). A group keeps its own running maximum m_g; the groups meet in
+// LDS, each scaled by exp(m_g - M). A split with no visible key (LSE_s = -inf) has weight 0.
+// ------------------------------------------------------------------------------------------
+constexpr int kCombineInFlight = 16;
+
 template <int DV>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   constexpr int CPB = DV / 4;       // float4 columns per row
   constexpr int G = 256 / CPB;      // split groups
+  constexpr int U = kCombineInFlight;
   static_assert(CPB <= 256 && 256 % CPB == 0, "row must fit one workgroup");
   __shared__ float4 red[G][CPB];
   __shared__ float gmax[G];
@@ -440,55 +441,59 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int c4 = threadIdx.x % CPB;
   const int grp = threadIdx.x / CPB;
 
-  // maximum LSE over the splits
-  float mx = -INFINITY;
-  for (int s = grp; s < a.S; s += G) mx = fmaxf(mx, a.lse_part[(int64_t)s * rows + row]);
-  if (c4 == 0) gmax[grp] = mx;
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < G; ++g) M = fmaxf(M, gmax[g]);
-
-  // weighted sum of this group's splits, four partial rows in flight per step
-  float den = 0.f;
+  float m = -INFINITY, den = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -INFINITY) {
-    for (int s0 = grp; s0 < a.S; s0 += 4 * G) {
-      float ls[4];
-      float4 x[4];
+  for (int s0 = grp; s0 < a.S; s0 += U * G) {
+    float ls[U];
+    float4 x[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = s0 + u * G;
-        if (s < a.S) {
-          ls[u] = a.lse_part[(int64_t)s * rows + row];
-          x[u] = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
-        } else {
-          ls[u] = -INFINITY;
-          x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * G;
+      if (s < a.S) {
+        ls[u] = a.lse_part[(int64_t)s * rows + row];
+        x[u] = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
+      } else {
+        ls[u] = -INFINITY;
+        x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
+    }
+    float cm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - M);
-        den += w;
-        o.x += w * x[u].x;
-        o.y += w * x[u].y;
-        o.z += w * x[u].z;
-        o.w += w * x[u].w;
-      }
+    for (int u = 0; u < U; ++u) cm = fmaxf(cm, ls[u]);
+    if (cm > m) {  // move this group's reference (exp(-inf) = 0 clears the first pass)
+      const float r = expf(m - cm);
+      den *= r;
+      o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+      m = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = (ls[u] == -INFINITY) ? 0.f : expf(ls[u] - m);
+      den += w;
+      o.x += w * x[u].x;
+      o.y += w * x[u].y;
+      o.z += w * x[u].z;
+      o.w += w * x[u].w;
     }
   }
   red[grp][c4] = o;
-  if (c4 == 0) gden[grp] = den;
+  if (c4 == 0) { gmax[grp] = m; gden[grp] = den; }
   __syncthreads();
   if (grp != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) M = fmaxf(M, gmax[g]);
   float dt = 0.f;
   float4 ot = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float4 r = red[g][c4];
-    ot.x += r.x; ot.y += r.y; ot.z += r.z; ot.w += r.w;
-    dt += gden[g];
+    for (int g = 0; g < G; ++g) {
+      const float mg = gmax[g];
+      const float r = (mg == -INFINITY) ? 0.f : expf(mg - M);
+      const float4 v = red[g][c4];
+      ot.x += r * v.x; ot.y += r * v.y; ot.z += r * v.z; ot.w += r * v.w;
+      dt += r * gden[g];
+    }
   }
   const float inv = dt > 0.f ? 1.0f / dt : 0.f;
   const int pos = (int)(row % a.Lq);
@@ -510,10 +515,66 @@ hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Few splits: one thread per (row, 4 columns), 256 / (DV/4) rows per workgroup, every split's
+// partial loaded before any is used. Same formula and split order as combine_kernel's single
+// group.
+constexpr int kCombineRowsMaxS = 8;
+
+template <int DV>
+__global__ __launch_bounds__(256) void combine_rows_kernel(const CombineArgs a) {
+  constexpr int CPB = DV / 4;
+  constexpr int RPB = 256 / CPB;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPB;
+  const int c4 = threadIdx.x % CPB;
+  if (row >= rows) return;
+  float ls[kCombineRowsMaxS];
+  float4 x[kCombineRowsMaxS];
+#pragma unroll
+  for (int s = 0; s < kCombineRowsMaxS; ++s) {
+    if (s < a.S) {
+      ls[s] = a.lse_part[(int64_t)s * rows + row];
+      x[s] = *reinterpret_cast<const float4*>(a.o_part + ((int64_t)s * rows + row) * DV + 4 * c4);
+    } else {
+      ls[s] = -INFINITY;
+      x[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kCombineRowsMaxS; ++s) M = fmaxf(M, ls[s]);
+  float den = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < kCombineRowsMaxS; ++s) {
+      const float w = (ls[s] == -INFINITY) ? 0.f : expf(ls[s] - M);
+      den += w;
+      o.x += w * x[s].x; o.y += w * x[s].y; o.z += w * x[s].z; o.w += w * x[s].w;
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const int pos = (int)(row % a.Lq);
+  const int hq = (int)((row / a.Lq) % a.Hq);
+  const int b = (int)(row / ((int64_t)a.Lq * a.Hq));
+  uint16_t* dst = a.o + (int64_t)b * a.o_sb + (int64_t)pos * a.o_sl + (int64_t)hq * a.o_sh + 4 * c4;
+  uint2 pk;
+  pk.x = pack_bf16x2(o.x * inv, o.y * inv);
+  pk.y = pack_bf16x2(o.z * inv, o.w * inv);
+  *reinterpret_cast<uint2*>(dst) = pk;
+  if (a.lse != nullptr && c4 == 0) a.lse[row] = den > 0.f ? M + logf(den) : -INFINITY;
+}
+
 template <int DV>
 hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Lq;
-  hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+  if (a.S <= kCombineRowsMaxS && DV <= 128) {
+    constexpr int RPB = 256 / (DV / 4);
+    hipLaunchKernelGGL((combine_rows_kernel<DV>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<DV>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -129,6 +129,19 @@ size_t workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits) {
   return rows * (size_t)Dv * sizeof(float) + rows * sizeof(float);
 }
 
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
+  DecodeWorkspace w{0, 0, 0, 0};
+  const int s = pick_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv);
+  if (s < 1) return w;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t rows = (size_t)s * B * Hq * Lq;
+  w.num_splits = s;
+  w.o_part = 0;
+  w.lse_part = up(rows * (size_t)Dv * sizeof(float));
+  w.total = up(w.lse_part + rows * sizeof(float));
+  return w;
+}
+
 int check_combine_args(const char* fn, const float* o_part, const float* lse_part, int num_splits,
                        const attn_tensor_t& o, const float* lse, int B, int Hq, int Lq, int Dv) {
   if (B < 1 || Hq < 1 || Lq < 1 || num_splits < 1)

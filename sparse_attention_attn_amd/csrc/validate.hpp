@@ -38,6 +38,13 @@ int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
 // Keys per split: 64 * ceil(ceil(Lk / S) / 64).
 int split_chunk(int Lk, int num_splits);
+// One-call decode workspace: the split partials O_part and LSE_part; byte offsets, 256-byte
+// aligned.
+struct DecodeWorkspace {
+  int num_splits;
+  size_t o_part, lse_part, total;
+};
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
 size_t workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits);
 

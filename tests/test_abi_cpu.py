@@ -120,6 +120,22 @@ def test_blocksparse_entry_validation():
     assert f(Lk=(1 << 20) + 64) == S.ATTN_ERR_UNSUPPORTED
 
 
+def test_decode_entry_validation_and_workspace():
+    lib = _lib()
+    need = S.attn_decode_workspace_bytes(16, 32, 8, 1, 4096, 128, 128)
+    # the two partial buffers of attn_fwd_splitkv (2 splits), each 256-byte aligned
+    part = S.attn_splitkv_workspace_bytes(16, 32, 1, 128, 2)
+    assert part <= need <= part + 2 * 256
+    assert S.attn_decode_workspace_bytes(0, 32, 8, 1, 4096, 128, 128) == 0
+    f = lambda ws=FAKE, nb=need: lib.attn_fwd_decode(
+        _t(), _t(), _t(), _t(), None, 16, 32, 8, 1, 4096, 128, 128, 0, ctypes.c_float(0.1), ws,
+        nb, None)
+    assert f(ws=None) == S.ATTN_ERR_WORKSPACE
+    assert f(nb=need - 1) == S.ATTN_ERR_WORKSPACE
+    assert f(ws=FAKE + 64) == S.ATTN_ERR_WORKSPACE
+    assert "workspace" in S.attn_last_error()
+
+
 def test_num_splits_heuristic_is_pure_and_in_range():
     # the decode workloads: 128 (b, kv-head) units -> 2 splits; 8 units of MLA -> 32 splits
     assert S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128) == 2

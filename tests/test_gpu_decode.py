@@ -125,15 +125,20 @@ def test_decode_causal_flag_is_noop_for_single_query():
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
 
 
-def test_combine_alone_against_oracle():
-    """Random partials with empty splits (LSE = -inf) and an all-empty row."""
+@pytest.mark.parametrize("Sx,Dv", [(5, 512), (100, 512), (77, 128), (3, 64), (2, 128), (8, 128), (9, 64)])
+def test_combine_alone_against_oracle(Sx, Dv):
+    """Random partials with empty splits (LSE = -inf), an all-empty row, and rows whose split
+    LSEs rise or fall with the split index (so a later pass of one split group moves its
+    running maximum)."""
     import torch
     import sparse_attention_attn_amd as S
-    Sx, B, Hq, Lq, Dv = 5, 2, 3, 2, 512
-    say("combine alone")
-    g = torch.Generator().manual_seed(8400)
+    B, Hq, Lq = 2, 3, 2
+    say(f"combine alone S={Sx} Dv={Dv}")
+    g = torch.Generator().manual_seed(8400 + Sx)
     op = torch.randn((Sx, B, Hq, Lq, Dv), generator=g, dtype=torch.float32)
     lp = torch.randn((Sx, B, Hq, Lq), generator=g, dtype=torch.float32) * 3
+    lp[:, 0, 1, 0] = torch.arange(Sx, dtype=torch.float32) * 0.5
+    lp[:, 1, 0, 1] = -torch.arange(Sx, dtype=torch.float32) * 0.5
     lp[1, 0, 0, 0] = -float("inf")
     lp[:, 1, 2, 1] = -float("inf")
     op[:, 1, 2, 1] = 0.0

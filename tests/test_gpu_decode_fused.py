@@ -1,0 +1,98 @@
+"""GPU parity of the one-call decode (attn_fwd_decode: split-KV then the LSE combine, with the
+partials in the caller's workspace) against the fp64 oracle, through the C ABI; one workspace
+serves calls of several shapes."""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from tests.helpers import check_parity, say, to_f64
+from workloads import WORKLOADS, make_qkv, randn_bf16
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _run(q, k, v, causal, scale, ws=None):
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Lq, Hq, _ = q.shape
+    o = torch.empty((B, Lq, Hq, v.shape[3]), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=DEV)
+    S.attn_fwd_decode(q, k, v, o, lse, causal=causal, scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check(q, k, v, causal, scale, label, ws=None, mla=False):
+    kd = k.to(DEV)
+    o, lse = _run(q.to(DEV), kd, kd[..., :512] if mla else v.to(DEV), causal, scale, ws)
+    vf = A.mla_value_view(to_f64(k), 512) if mla else to_f64(v)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), vf, A.effective_scale(scale), causal)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, label)
+
+
+def test_decode_one_call_gqa_workload():
+    w = WORKLOADS["gqa_decode_4k"]
+    say(f"one-call decode {w.name}")
+    q, k, v = make_qkv(w)
+    _check(q, k, v, False, w.scale, "one-call gqa_decode_4k")
+
+
+SHAPES = [
+    # B, Hq, Hkv, Lq, Lk, D, causal
+    (1, 4, 1, 1, 1, 128, False),        # one key, one split
+    (3, 8, 2, 1, 4096 + 37, 128, False),
+    (2, 16, 4, 2, 3000, 128, True),     # two query tokens, bottom-right causal
+    (5, 8, 8, 1, 777, 64, False),
+    (2, 6, 2, 3, 2049, 64, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_one_call_shapes(shape):
+    B, Hq, Hkv, Lq, Lk, D, causal = shape
+    say(f"one-call decode {shape}")
+    q = randn_bf16((B, Lq, Hq, D), 8600 + Lk)
+    k = randn_bf16((B, Lk, Hkv, D), 8601 + Lk)
+    v = randn_bf16((B, Lk, Hkv, D), 8602 + Lk)
+    _check(q, k, v, causal, D ** -0.5, f"one-call {shape}")
+
+
+def test_decode_one_call_mla():
+    """The latent shape takes the two-launch path inside the same entry point."""
+    B, Hq, Lk = 2, 16, 5000
+    say("one-call decode MLA")
+    q = randn_bf16((B, 1, Hq, 576), 8700)
+    k = randn_bf16((B, Lk, 1, 576), 8701)
+    _check(q, k, None, False, 192 ** -0.5, "one-call MLA", mla=True)
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, sized for the largest shape and filled with garbage, serves calls of
+    several shapes in a row."""
+    import torch
+    import sparse_attention_attn_amd as S
+    say("one-call decode workspace reuse")
+    shapes = [(4, 32, 8, 1, 4096, 128), (2, 8, 2, 2, 1500, 64), (4, 32, 8, 1, 4096, 128),
+              (1, 4, 4, 1, 100, 128)]
+    need = max(S.attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, D)
+               for B, Hq, Hkv, Lq, Lk, D in shapes)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)
+    for i, (B, Hq, Hkv, Lq, Lk, D) in enumerate(shapes):
+        q = randn_bf16((B, Lq, Hq, D), 8800 + i)
+        k = randn_bf16((B, Lk, Hkv, D), 8810 + i)
+        v = randn_bf16((B, Lk, Hkv, D), 8820 + i)
+        _check(q, k, v, Lq > 1, D ** -0.5, f"reuse {i}", ws=ws)
+
+
+def test_decode_one_call_deterministic():
+    import torch
+    say("one-call decode determinism")
+    q = randn_bf16((8, 1, 32, 128), 8900).to(DEV)
+    k = randn_bf16((8, 3000, 8, 128), 8901).to(DEV)
+    v = randn_bf16((8, 3000, 8, 128), 8902).to(DEV)
+    a = _run(q, k, v, False, 0.088)
+    b = _run(q, k, v, False, 0.088)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
