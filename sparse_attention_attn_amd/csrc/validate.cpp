@@ -108,8 +108,12 @@ int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   const int cols = split_cols(Dqk, g * Lq);
   const int64_t colblk = ((int64_t)g * Lq + cols - 1) / cols;
   const int64_t units = (int64_t)B * Hkv * colblk;
-  const int wg_per_cu = (Dqk == 64) ? 2 : 1;  // LDS ring: 64 KiB (D=64), 128-144 KiB otherwise
-  int64_t s = (kCUs * wg_per_cu + units - 1) / units;
+  // resident workgroups per CU (LDS ring: 64 KiB for D = 64 and 128, 128-144 KiB for the
+  // latent shape); D = 128 also asks for two rounds of them, the measured best on the batched
+  // 4K GQA decode (8 splits: 49.7 us, 4 splits: 50.8 us)
+  const int wg_per_cu = (Dqk == 576) ? 1 : 2;
+  const int rounds = (Dqk == 128) ? 2 : 1;
+  int64_t s = ((int64_t)kCUs * wg_per_cu * rounds + units - 1) / units;
   const int64_t max_by_len = std::max<int64_t>(1, Lk / 256);  // at least 256 keys per split
   const int64_t max_s = (Lk + 63) / 64;
   s = std::min(s, max_by_len);
