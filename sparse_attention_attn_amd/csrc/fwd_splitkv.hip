@@ -73,10 +73,11 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   // stage being read from the stages still being filled, and does not wait for those copies.
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[NST > 2 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st3[NST > 3 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st4[NST > 4 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char st5[NST > 5 ? C::STAGE : 16];
+  // stages beyond NST are 4-byte stubs, so that a 2-stage ring fits twice in one CU's LDS
+  __shared__ __attribute__((aligned(NST > 2 ? 1024 : 4))) char st2[NST > 2 ? C::STAGE : 4];
+  __shared__ __attribute__((aligned(NST > 3 ? 1024 : 4))) char st3[NST > 3 ? C::STAGE : 4];
+  __shared__ __attribute__((aligned(NST > 4 ? 1024 : 4))) char st4[NST > 4 ? C::STAGE : 4];
+  __shared__ __attribute__((aligned(NST > 5 ? 1024 : 4))) char st5[NST > 5 ? C::STAGE : 4];
   // MLA: the 4 waves split the Dqk reduction of Sᵀ and add their partial score tiles here.
   constexpr bool KSPLIT = C::MLA;
   constexpr int QW = KSPLIT ? (C::QSTEPS + 3) / 4 : C::QSTEPS;  // Qᵀ steps held per wave
