@@ -166,8 +166,9 @@ int attn_fwd_blocksparse(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn
  *   workspace — DEVICE buffer of at least attn_vertical_slash_workspace_bytes(B, Hq, Lk)
  *       bytes, 256-byte aligned, owned by the caller; it receives two per-head bitmaps (the
  *       offsets and the columns) and holds nothing between calls.
- * Errors: as attn_fwd_blocksparse, plus INVALID_ARG when slash_ptr is NULL and WORKSPACE for
- * a missing, short or misaligned workspace.
+ * Lk may be at most 2^19 here.
+ * Errors: as attn_fwd_blocksparse, plus INVALID_ARG when slash_ptr is NULL, UNSUPPORTED for Lk
+ * above 2^19, and WORKSPACE for a missing, short or misaligned workspace.
  */
 int attn_fwd_vertical_slash(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
                             float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,

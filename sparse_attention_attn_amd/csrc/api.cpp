@@ -239,6 +239,11 @@ int attn_fwd_vertical_slash(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, a
     if (st != ATTN_OK) return st;
     if (blk_ptr == nullptr || col_ptr == nullptr || slash_ptr == nullptr)
       return attn::fail(ATTN_ERR_INVALID_ARG, fn, "blk_ptr / col_ptr / slash_ptr is NULL");
+    if (Lk > attn::kVslashMaxLk) {
+      std::ostringstream m;
+      m << "Lk=" << Lk << " exceeds the vertical-slash limit of " << attn::kVslashMaxLk;
+      return attn::fail(ATTN_ERR_UNSUPPORTED, fn, m.str());
+    }
     const size_t need = attn_vertical_slash_workspace_bytes(B, Hq, Lk);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) {

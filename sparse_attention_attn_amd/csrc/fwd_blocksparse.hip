@@ -208,10 +208,11 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, const WaveState<D>& 
 }
 
 // Maps blockIdx.x to a logical work id. The hardware deals workgroups round-robin over the 8
-// XCDs (each with its own L2) in blockIdx order. Logical ids are cut into chunks of 32 (8 query
-// blocks x 4 query heads of one KV head) and chunk c runs on XCD c % 8: the query blocks that
-// share most of their local band of key blocks meet in one L2, while all XCDs work on
-// neighbouring chunks, i.e. on the same KV head, whose K/V then fits the device-wide cache.
+// XCDs (each with its own L2) in blockIdx order. Logical ids are cut into chunks of 32 (8 pairs
+// of query blocks x 4 query heads of one KV head) and chunk c runs on XCD c % 8: the query
+// blocks that share most of their local band of key blocks meet in one L2, while all XCDs
+// work on neighbouring chunks, i.e. on the same KV head, whose K/V then fits the device-wide
+// cache.
 __device__ __forceinline__ int logical_block(int xcd_remap) {
   const int bid = (int)blockIdx.x;
   if (!xcd_remap) return bid;
@@ -221,31 +222,40 @@ __device__ __forceinline__ int logical_block(int xcd_remap) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Block-sparse forward: one workgroup per (b, query head, 64-row query block).
-// Phase 1 walks the listed key blocks; phase 2 gathers the head's vertical columns that are
-// causally visible to the block and not already inside a listed block (so a key is never
-// counted twice), 64 at a time, in ascending key order.
+// Block-sparse forward: one workgroup of 4 waves per (b, query head, pair of 64-row query
+// blocks 2p and 2p+1); waves 0-1 own the rows of block 2p, waves 2-3 those of block 2p+1, 32
+// rows each. The two blocks' lists share most of their key blocks (the local band moves by one
+// block), so the workgroup streams each key tile once for both, and a wave skips the tiles its
+// own block does not list. With two such workgroups per CU every SIMD runs two waves, which
+// hide each other's softmax and waits.
+// Phase 1 walks the union of the two listed-block sets in ascending order; phase 2 gathers the
+// head's vertical columns that are causally visible to the pair and not inside a block both
+// blocks list, 64 at a time, and each wave masks the columns inside its own listed blocks
+// (so a key is never counted twice).
 //
 // With SLASH, phase 3 adds the head's slash lines (MInference article, paragraph on the
 // vertical-slash pattern): the line at offset o >= 0 lets query row i see key i + off - o
-// (off = Lk - Lq). Setup marks the 64-key blocks any line crosses inside this query block's
-// rows; phase 3 runs each marked block that is not listed as a tile whose mask keeps a pair
-// (row, key) only when row + off - key is a listed offset and key is not a listed column (those
-// keys were counted in phase 2). The offsets and the columns of a head come as two bitmaps
-// (vs_bits_kernel); each lane loads the 96 + 64 bits its 32 scores need together with the
-// tile's copy, so the copy wait of the next step covers those loads too.
+// (off = Lk - Lq). Setup marks the 64-key blocks any line crosses inside the pair's rows;
+// phase 3 runs each marked block that the wave's own block does not list as a tile whose mask
+// keeps a pair (row, key) only when row + off - key is a listed offset and key is not a listed
+// column (those keys were counted in phase 2). The offsets and the columns of a head come as
+// two bitmaps (vs_bits_kernel); each lane loads the 96 + 64 bits its 32 scores need together
+// with the tile's copy, so the copy wait of the next step covers those loads too.
 // ------------------------------------------------------------------------------------------
-constexpr int kSeg = 512;              // columns examined per compaction pass
-constexpr int kMaxBitmapWords = 512;   // listed-block bitmap: up to 16384 key blocks (1M keys)
+constexpr int kSeg = 512;              // ids examined per compaction pass
+constexpr int kMaxBitmapWords = 512;   // listed-block bitmaps: up to 16384 key blocks (1M keys)
+constexpr int kSlashBitmapWords = kVslashMaxLk / 64 / 32;  // crossed blocks (slash variant)
+constexpr int kColMask = (1 << 29) - 1;  // column id bits of a phase-2 entry (flags above)
 
-template <int D, int NW, bool SLASH>
-__global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
+template <int D, bool SLASH>
+__global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
+  constexpr int NW = 4;
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
-  __shared__ uint32_t bitmap[kMaxBitmapWords];
-  __shared__ uint32_t tbits[SLASH ? kMaxBitmapWords : 1];  // blocks crossed by a slash line
+  __shared__ uint32_t bm[2][kMaxBitmapWords];                  // listed blocks of 2p, 2p+1
+  __shared__ uint32_t tbits[SLASH ? kSlashBitmapWords : 1];  // blocks crossed by a slash line
   __shared__ int kept[kSeg];
   __shared__ int wave_cnt[NW];
 
@@ -253,44 +263,47 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
   const int w = tid >> 6;
   const int l = tid & 63;
   const int nqb = a.n_qtiles;
+  const int npair = (nqb + 1) / 2;
   int lid = logical_block(a.xcd_remap);
   const int hg = lid % a.g;
   lid /= a.g;
-  const int qb = nqb - 1 - (lid % nqb);
-  lid /= nqb;
+  const int pr = npair - 1 - (lid % npair);
+  lid /= npair;
   const int hkv = lid % a.Hkv;
   const int b = lid / a.Hkv;
   const int hq = hkv * a.g + hg;
 
-  const int q0 = qb * 64;
-  const int qw0 = q0 + 32 * w;
+  const int qbA = 2 * pr;
+  const int myq = w >> 1;  // 0: block qbA, 1: block qbA + 1
+  const int q0 = qbA * 64;                     // first row of the workgroup
+  const int qw0 = q0 + 64 * myq + 32 * (w & 1);  // first row of this wave
   const int row = qw0 + (l & 31);
-  const int qlast = min(q0 + 64, a.Lq) - 1;
+  const bool active = qw0 < a.Lq;              // the wave has rows
+  const int qlast = min(q0 + 128, a.Lq) - 1;   // last row of the workgroup
   const int qwlast = min(qw0 + 31, a.Lq - 1);
   const int klim = a.causal ? min(a.Lk - 1, qlast + a.off) : a.Lk - 1;  // last visible key
   const int lkm1 = a.Lk - 1;
 
   const int bh = b * a.Hq + hq;
-  const int64_t lrow = (int64_t)bh * nqb + qb;
-  const int bstart = a.blk_ptr[lrow];
-  const int nb = a.blk_ptr[lrow + 1] - bstart;
   const int nwords = (a.nkb + 31) >> 5;
+  auto listed = [&](int q, int kb) -> bool { return (bm[q][kb >> 5] >> (kb & 31)) & 1u; };
 
-  // The block list is also staged in LDS (as 16-bit ids, in the column buffer that phase 2
-  // reuses later) when it fits, so the tile loop reads no global memory: a global load there
-  // would be waited for with a vmcnt wait that also drains the tile copies in flight.
-  short* blist = reinterpret_cast<short*>(kept);
-  constexpr int kListCap = 2 * kSeg;
-  const bool list_in_lds = nb <= kListCap;
-  for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
+  for (int i = tid; i < nwords; i += NT) {
+    bm[0][i] = 0u;
+    bm[1][i] = 0u;
+  }
   if constexpr (SLASH)
     for (int i = tid; i < nwords; i += NT) tbits[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < nb; i += NT) {
-    const int kbk = a.blk_idx[bstart + i];
-    const bool valid = kbk >= 0 && kbk < a.nkb;
-    if (valid) atomicOr(&bitmap[kbk >> 5], 1u << (kbk & 31));
-    if (i < kListCap) blist[i] = (short)(valid ? kbk : -1);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (qbA + q >= nqb) break;
+    const int64_t lrow = (int64_t)bh * nqb + qbA + q;
+    const int s1 = a.blk_ptr[lrow + 1];
+    for (int i = a.blk_ptr[lrow] + tid; i < s1; i += NT) {
+      const int kbk = a.blk_idx[i];
+      if (kbk >= 0 && kbk < a.nkb) atomicOr(&bm[q][kbk >> 5], 1u << (kbk & 31));
+    }
   }
   if constexpr (SLASH) {
     // the line at offset o meets rows q0..qlast at keys q0+off-o .. qlast+off-o (<= klim)
@@ -300,77 +313,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
       const int hi = qlast + a.off - o;
       if (o < 0 || hi < 0) continue;
       const int lo = max(0, q0 + a.off - o);
-      const int b0 = lo >> 6, b1 = min(hi, lkm1) >> 6;
       if (lo > lkm1) continue;
-      atomicOr(&tbits[b0 >> 5], 1u << (b0 & 31));
-      if (b1 != b0) atomicOr(&tbits[b1 >> 5], 1u << (b1 & 31));
+      for (int kb = lo >> 6; kb <= (min(hi, lkm1) >> 6); ++kb)
+        atomicOr(&tbits[kb >> 5], 1u << (kb & 31));
     }
   }
   __syncthreads();
 
-  WaveState<D> ws;
-  load_q<D>(a, ws, b, hq, row, l);
-  TileOffsets<D, NW> off;
-  off.init(a, w, l);
-  const uint16_t* kbp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-  const uint16_t* vbp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
-
-  // ---- phase 1: listed key blocks
-  auto blk_base = [&](int i) -> int {
-    if (list_in_lds) {
-      const int kbk = blist[i];
-      return kbk >= 0 ? kbk * BN : -1;  // -1: invalid id, fully masked
-    }
-    const int kbk = a.blk_idx[bstart + i];
-    return (kbk >= 0 && kbk < a.nkb) ? kbk * BN : -1;
-  };
-  auto issue_blk = [&](auto S, int i) {
-    char* st = decltype(S)::value == 0 ? st0 : st1;
-    const int base = blk_base(i);
-    if (base >= 0 && base + BN <= a.Lk) {
-      issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl, off, w);
-    } else {
-      issue_tile_slow<D, NW>(a, st, kbp, vbp,
-                             [&](int r) { return base < 0 ? 0 : min(base + r, lkm1); }, w, l);
-    }
-  };
-  auto step_blk = [&](auto S, int t) {
-    constexpr int s = decltype(S)::value;
-    wait_dma_all();
-    __syncthreads();
-    if (t + 1 < nb) issue_blk(ic<1 - s>{}, t + 1);
-    const int base = blk_base(t);
-    if (base < 0) return;
-    if (a.causal && base > qwlast + a.off) return;
-    const bool masked = base + BN > a.Lk || (a.causal && base + BN - 1 > qw0 + a.off);
-    tile_math<D>(a, ws, s == 0 ? st0 : st1, row, masked,
-                 [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
-  };
-  if (nb > 0) issue_blk(ic<0>{}, 0);
-  for (int t = 0; t < nb; t += 2) {
-    step_blk(ic<0>{}, t);
-    if (t + 1 < nb) step_blk(ic<1>{}, t + 1);
-  }
-  __syncthreads();  // stage buffers free before phase 2 reuses them
-
-  // ---- phase 2: vertical columns
-  const int cstart = a.col_ptr[bh];
-  const int cend = a.col_ptr[bh + 1];
-  for (int seg = cstart; seg < cend; seg += kSeg) {
-    if (a.col_idx[seg] > klim) break;  // sorted: nothing further is visible
-    const int segend = min(seg + kSeg, cend);
+  // Ordered compaction: the ids id0 + i (i < n) whose keep(i) holds go to kept[] in order,
+  // value(i) each; returns their count (the same in every wave).
+  auto compact = [&](int n, auto keep_fn, auto value_fn) -> int {
     int cnt = 0;
-    for (int rr = 0; rr < segend - seg; rr += NT) {
-      const int idx = seg + rr + tid;
-      bool keep = false;
-      int col = 0;
-      if (idx < segend) {
-        col = a.col_idx[idx];
-        if (col >= 0 && col <= klim) {
-          const int kbk = col >> 6;
-          keep = ((bitmap[kbk >> 5] >> (kbk & 31)) & 1u) == 0u;
-        }
-      }
+    for (int rr = 0; rr < n; rr += NT) {
+      const int i = rr + tid;
+      const bool keep = i < n && keep_fn(i);
       const uint64_t mask = __ballot(keep);
       const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -383,37 +339,108 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
         woff += (ww < w) ? cw : 0;
         tot += cw;
       }
-      if (keep) kept[cnt + woff + below] = col;
+      if (keep) kept[cnt + woff + below] = value_fn(i);
       cnt += tot;
       __syncthreads();
     }
-    const int nch = (cnt + BN - 1) / BN;
-    auto issue_col = [&](auto S, int t) {
-      char* st = decltype(S)::value == 0 ? st0 : st1;
-      const int cb = t * BN;
-      issue_tile_slow<D, NW>(a, st, kbp, vbp,
-                             [&](int r) { return kept[cb + r < cnt ? cb + r : 0]; }, w, l);
-    };
-    auto step_col = [&](auto S, int t) {
+    return cnt;
+  };
+
+  WaveState<D> ws;
+  load_q<D>(a, ws, b, hq, row, l);
+  TileOffsets<D, NW> off;
+  off.init(a, w, l);
+  const uint16_t* kbp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const uint16_t* vbp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+  // copy of the 64-key block starting at key `base` (inside the sequence) into stage S
+  auto issue_block = [&](auto S, int base) {
+    char* st = decltype(S)::value == 0 ? st0 : st1;
+    if (base + BN <= a.Lk) {
+      issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl, off, w);
+    } else {
+      issue_tile_slow<D, NW>(a, st, kbp, vbp, [&](int r) { return min(base + r, lkm1); }, w, l);
+    }
+  };
+  // the two-stage ring over tiles 0..ntl-1: step(t) waits for tile t, starts tile t+1 and
+  // runs the math of tile t
+  auto run = [&](int ntl, auto issue_fn, auto math_fn) {
+    if (ntl > 0) issue_fn(ic<0>{}, 0);
+    auto step = [&](auto S, int t) {
       constexpr int s = decltype(S)::value;
       wait_dma_all();
       __syncthreads();
-      if (t + 1 < nch) issue_col(ic<1 - s>{}, t + 1);
-      const int cb = t * BN;
-      // columns are ascending: skip if even the first one is beyond this wave's horizon
-      if (a.causal && kept[cb] > qwlast + a.off) return;
-      tile_math<D>(a, ws, s == 0 ? st0 : st1, row, true,
-                   [&](int kl) { return cb + kl < cnt ? kept[cb + kl] : -1; }, l);
+      if (t + 1 < ntl) issue_fn(ic<1 - s>{}, t + 1);
+      math_fn(S, t);
     };
-    if (nch > 0) issue_col(ic<0>{}, 0);
-    for (int t = 0; t < nch; t += 2) {
-      step_col(ic<0>{}, t);
-      if (t + 1 < nch) step_col(ic<1>{}, t + 1);
+    for (int t = 0; t < ntl; t += 2) {
+      step(ic<0>{}, t);
+      if (t + 1 < ntl) step(ic<1>{}, t + 1);
     }
-    __syncthreads();  // kept[] and the stages are rewritten by the next segment
+    __syncthreads();  // stages and kept[] free for the next pass
+  };
+
+  // ---- phase 1: the union of the two blocks' listed key blocks, 512 block ids per pass
+  for (int c0 = 0; c0 < nwords * 32; c0 += kSeg) {
+    const int cnt = compact(min(kSeg, nwords * 32 - c0),
+                            [&](int i) {
+                              const int kb = c0 + i;
+                              return (((bm[0][kb >> 5] | bm[1][kb >> 5]) >> (kb & 31)) & 1u) != 0u;
+                            },
+                            [&](int i) { return c0 + i; });
+    run(cnt, [&](auto S, int t) { issue_block(S, kept[t] * BN); },
+        [&](auto S, int t) {
+          const int kb = kept[t];
+          const int base = kb * BN;
+          if (!active || !listed(myq, kb)) return;
+          if (a.causal && base > qwlast + a.off) return;
+          const bool masked = base + BN > a.Lk || (a.causal && base + BN - 1 > qw0 + a.off);
+          tile_math<D>(a, ws, decltype(S)::value == 0 ? st0 : st1, row, masked,
+                       [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
+        });
   }
 
-  // ---- phase 3: slash lines, over the crossed blocks that are not listed
+  // ---- phase 2: vertical columns. An entry is the column id with bit 29 + q set when the
+  // column lies inside a block that block q lists.
+  const int cstart = a.col_ptr[bh];
+  const int cend = a.col_ptr[bh + 1];
+  for (int seg = cstart; seg < cend; seg += kSeg) {
+    if (a.col_idx[seg] > klim) break;  // sorted: nothing further is visible
+    const int n = min(kSeg, cend - seg);
+    const int cnt = compact(n,
+                            [&](int i) {
+                              const int col = a.col_idx[seg + i];
+                              if (col < 0 || col > klim) return false;
+                              return !(listed(0, col >> 6) && listed(1, col >> 6));
+                            },
+                            [&](int i) {
+                              const int col = a.col_idx[seg + i];
+                              return col | ((int)listed(0, col >> 6) << 29) |
+                                     ((int)listed(1, col >> 6) << 30);
+                            });
+    // cnt columns make ceil(cnt / 64) tiles; tile t gathers entries 64t .. 64t+63
+    run((cnt + BN - 1) / BN,
+        [&](auto S, int t) {
+          const int cb = t * BN;
+          issue_tile_slow<D, NW>(a, decltype(S)::value == 0 ? st0 : st1, kbp, vbp,
+                                 [&](int r) { return kept[cb + r < cnt ? cb + r : cb] & kColMask; },
+                                 w, l);
+        },
+        [&](auto S, int t) {
+          const int cb = t * BN;
+          if (!active) return;
+          // columns are ascending: skip if even the first one is beyond this wave's horizon
+          if (a.causal && (kept[cb] & kColMask) > qwlast + a.off) return;
+          tile_math<D>(a, ws, decltype(S)::value == 0 ? st0 : st1, row, true,
+                       [&](int kl) {
+                         if (cb + kl >= cnt) return -1;
+                         const int e = kept[cb + kl];
+                         return ((e >> (29 + myq)) & 1) ? -1 : (e & kColMask);
+                       }, l);
+        });
+  }
+
+  // ---- phase 3: slash lines, over the crossed blocks the wave's own block does not list
   if constexpr (SLASH) {
     const int h = l >> 5;
     const uint32_t* sbits = a.sl_bits + (int64_t)bh * a.bits_words;
@@ -421,78 +448,51 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(const FwdArgs a) {
     // Lane's window: bitmap bit (o + 128) of its local key c's offset is at rw - base + 59 - c.
     const int rw = row + a.off + 69 - 4 * h;
     uint32_t mw[2][5];
-    for (int wc = 0; wc < nwords; wc += kSeg / 32) {
-      int cnt = 0;
-      for (int rr = 0; rr < kSeg; rr += NT) {
-        const int bit = rr + tid;
-        const int wi = wc + (bit >> 5);
-        const bool keep = wi < nwords && (((tbits[wi] & ~bitmap[wi]) >> (bit & 31)) & 1u);
-        const uint64_t mask = __ballot(keep);
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        if (l == 0) wave_cnt[w] = __popcll(mask);
-        __syncthreads();
-        int woff = 0, tot = 0;
+    for (int c0 = 0; c0 < nwords * 32; c0 += kSeg) {
+      const int cnt = compact(min(kSeg, nwords * 32 - c0),
+                              [&](int i) {
+                                const int kb = c0 + i;
+                                const uint32_t both = bm[0][kb >> 5] & bm[1][kb >> 5];
+                                return (((tbits[kb >> 5] & ~both) >> (kb & 31)) & 1u) != 0u;
+                              },
+                              [&](int i) { return c0 + i; });
+      run(cnt,
+          [&](auto S, int t) {
+            constexpr int s = decltype(S)::value;
+            const int base = kept[t] * BN;
+            const uint32_t* sp = sbits + (max(rw - base, 0) >> 5);
+            mw[s][0] = sp[0];
+            mw[s][1] = sp[1];
+            mw[s][2] = sp[2];
+            mw[s][3] = cbits[base >> 5];
+            mw[s][4] = cbits[(base >> 5) + 1];
+            issue_block(S, base);
+          },
+          [&](auto S, int t) {
+            constexpr int s = decltype(S)::value;
+            const int kb = kept[t];
+            const int base = kb * BN;
+            if (!active || listed(myq, kb)) return;
+            if (base > qwlast + a.off) return;  // past every row of this wave on every line
+            const int sh = max(rw - base, 0) & 31;
+            tile_math_mask<D>(a, ws, s == 0 ? st0 : st1, true, [&](f32x16& s0, f32x16& s1) {
+              // offsets: bit x of (d1:d0) is local key c = 59 - x; reversed and shifted, bit c
+              const uint32_t d0 = __builtin_amdgcn_alignbit(mw[s][1], mw[s][0], sh);
+              const uint32_t d1 = __builtin_amdgcn_alignbit(mw[s][2], mw[s][1], sh);
+              const uint32_t r0 = __builtin_bitreverse32(d1), r1 = __builtin_bitreverse32(d0);
+              // listed columns: bit c is key base + 4h + c
+              const uint32_t c0w = __builtin_amdgcn_alignbit(mw[s][4], mw[s][3], 4 * h);
+              const uint32_t c1w = mw[s][4] >> (4 * h);
+              const uint32_t vlo = ((r0 >> 4) | (r1 << 28)) & ~c0w;
+              const uint32_t vhi = (r1 >> 4) & ~c1w;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const int cw = wave_cnt[ww];
-          woff += (ww < w) ? cw : 0;
-          tot += cw;
-        }
-        if (keep) kept[cnt + woff + below] = 32 * wc + bit;
-        cnt += tot;
-        __syncthreads();
-      }
-      auto issue_sl = [&](auto S, int t) {
-        constexpr int s = decltype(S)::value;
-        char* st = s == 0 ? st0 : st1;
-        const int base = kept[t] * BN;
-        const uint32_t* sp = sbits + (max(rw - base, 0) >> 5);
-        mw[s][0] = sp[0];
-        mw[s][1] = sp[1];
-        mw[s][2] = sp[2];
-        mw[s][3] = cbits[base >> 5];
-        mw[s][4] = cbits[(base >> 5) + 1];
-        if (base + BN <= a.Lk) {
-          issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl,
-                                 off, w);
-        } else {
-          issue_tile_slow<D, NW>(a, st, kbp, vbp, [&](int r) { return min(base + r, lkm1); }, w,
-                                 l);
-        }
-      };
-      auto step_sl = [&](auto S, int t) {
-        constexpr int s = decltype(S)::value;
-        wait_dma_all();
-        __syncthreads();
-        if (t + 1 < cnt) issue_sl(ic<1 - s>{}, t + 1);
-        const int base = kept[t] * BN;
-        if (base > qwlast + a.off) return;  // past every row of this wave on every line
-        const int sh = max(rw - base, 0) & 31;
-        tile_math_mask<D>(a, ws, s == 0 ? st0 : st1, true, [&](f32x16& s0, f32x16& s1) {
-          // offsets: bit x of (d1:d0) is local key c = 59 - x; reversed and shifted, bit c
-          const uint32_t d0 = __builtin_amdgcn_alignbit(mw[s][1], mw[s][0], sh);
-          const uint32_t d1 = __builtin_amdgcn_alignbit(mw[s][2], mw[s][1], sh);
-          const uint32_t r0 = __builtin_bitreverse32(d1), r1 = __builtin_bitreverse32(d0);
-          // listed columns: bit c is key base + 4h + c
-          const uint32_t c0 = __builtin_amdgcn_alignbit(mw[s][4], mw[s][3], 4 * h);
-          const uint32_t c1 = mw[s][4] >> (4 * h);
-          const uint32_t vlo = ((r0 >> 4) | (r1 << 28)) & ~c0;
-          const uint32_t vhi = (r1 >> 4) & ~c1;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int c = 8 * (j >> 2) + (j & 3);
-            if (!((vlo >> c) & 1u)) s0[j] = -INFINITY;
-            if (!((vhi >> c) & 1u)) s1[j] = -INFINITY;
-          }
-        }, l);
-      };
-      if (cnt > 0) issue_sl(ic<0>{}, 0);
-      for (int t = 0; t < cnt; t += 2) {
-        step_sl(ic<0>{}, t);
-        if (t + 1 < cnt) step_sl(ic<1>{}, t + 1);
-      }
-      __syncthreads();  // kept[] and the stages are rewritten by the next chunk
+              for (int j = 0; j < 16; ++j) {
+                const int c = 8 * (j >> 2) + (j & 3);
+                if (!((vlo >> c) & 1u)) s0[j] = -INFINITY;
+                if (!((vhi >> c) & 1u)) s1[j] = -INFINITY;
+              }
+            }, l);
+          });
     }
   }
   store_out<D>(a, ws, b, hq, row, l);
@@ -521,28 +521,28 @@ __global__ __launch_bounds__(256) void vs_bits_kernel(const FwdArgs a) {
   }
 }
 
-template <int D, int NW, bool SLASH>
+template <int D, bool SLASH>
 hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
-  const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
+  const int64_t nwg = (int64_t)a.B * a.Hq * ((a.n_qtiles + 1) / 2);
   FwdArgs aa = a;
   aa.xcd_remap = (nwg % 256 == 0) ? 1 : 0;
   if constexpr (SLASH)
     hipLaunchKernelGGL(vs_bits_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, aa);
-  hipLaunchKernelGGL((fwd_sparse_kernel<D, NW, SLASH>), dim3((unsigned)nwg), dim3(NW * 64), 0,
-                     stream, aa);
+  hipLaunchKernelGGL((fwd_sparse_kernel<D, SLASH>), dim3((unsigned)nwg), dim3(256), 0, stream,
+                     aa);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_sparse_t<128, 2, false>(a, stream);
-  return launch_sparse_t<64, 2, false>(a, stream);
+  if (d == 128) return launch_sparse_t<128, false>(a, stream);
+  return launch_sparse_t<64, false>(a, stream);
 }
 
 hipError_t launch_fwd_vslash(const FwdArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_sparse_t<128, 2, true>(a, stream);
-  return launch_sparse_t<64, 2, true>(a, stream);
+  if (d == 128) return launch_sparse_t<128, true>(a, stream);
+  return launch_sparse_t<64, true>(a, stream);
 }
 
 }  // namespace attn

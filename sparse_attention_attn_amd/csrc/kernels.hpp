@@ -37,6 +37,10 @@ struct FwdArgs {
   int bits_words;
 };
 
+// Longest key sequence of the vertical-slash forward (its kernel keeps three block bitmaps in
+// LDS beside two 36 KiB stages, two workgroups per CU).
+constexpr int kVslashMaxLk = 1 << 19;
+
 // Words per head of each vertical-slash bitmap.
 inline int vs_bits_words(int Lk) { return (Lk + 255) / 32 + 2; }
 

@@ -193,6 +193,7 @@ def _vslash(slash_ptr=FAKE, ws=FAKE, ws_bytes=None, Lk=4096, causal=1):
     (dict(ws_bytes=64), S.ATTN_ERR_WORKSPACE, "workspace"),
     (dict(ws=FAKE + 16), S.ATTN_ERR_WORKSPACE, "256-byte"),
     (dict(Lk=(1 << 20) + 64), S.ATTN_ERR_UNSUPPORTED, "limit"),
+    (dict(Lk=(1 << 19) + 64), S.ATTN_ERR_UNSUPPORTED, "vertical-slash limit"),
 ])
 def test_vertical_slash_entry_validation(kw, code, frag):
     assert _vslash(**kw) == code
