@@ -10,10 +10,10 @@
 // llama.cpp para optimizar la inferencia", section "¿Qué es Flash Attention y por qué es
 // crucial para llama.cpp?").
 //
-// Work decomposition: one workgroup owns 32*NW query rows of one (batch, query head); each
-// wave owns 32 rows. Keys stream through LDS in 64-key tiles (K tile + V tile), copied by
-// gfx950's asynchronous global->LDS loads into a two-stage ring so the copy of tile t+1
-// overlaps the math on tile t.
+// Work decomposition: one workgroup of 4 waves owns a pair of 64-row query blocks of one
+// (batch, query head); each wave owns 32 rows. Keys stream through LDS in 64-key tiles (K tile
+// + V tile), copied by gfx950's asynchronous global->LDS loads into a two-stage ring so the
+// copy of tile t+1 overlaps the math on tile t; a tile is copied once for both query blocks.
 //
 // Per tile and wave, the product is formed transposed, Sᵀ = K·Qᵀ, with 32x32x16 bf16 MFMA:
 // K (64 keys x D) is the A operand read from LDS, Qᵀ is the B operand held in registers for
