@@ -320,8 +320,8 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
   }
   __syncthreads();
 
-  // Ordered compaction: the ids id0 + i (i < n) whose keep(i) holds go to kept[] in order,
-  // value(i) each; returns their count (the same in every wave).
+  // Ordered compaction: for the items i < n whose keep(i) holds, value(i) goes to kept[] in
+  // the order of i; returns their count (the same in every wave).
   auto compact = [&](int n, auto keep_fn, auto value_fn) -> int {
     int cnt = 0;
     for (int rr = 0; rr < n; rr += NT) {
