@@ -93,7 +93,14 @@ def vslash_pairs(slash_ptr, slash_idx, col_ptr, col_idx, B, Hq, L):
 
 
 # ------------------------------------------------------------------------------ timing
+STEP_TIMES = {}   # last time_steps call: per-step event times (ms)
+
+
 def time_steps(step, steps, warmup):
+    """Mean ms per step over `steps` back-to-back steps (HIP events on the launch stream around
+    the whole run), and the wall time. A second pass of `steps` steps, each bracketed by its own
+    events (recorded without synchronising), gives the spread in STEP_TIMES (p10 / p50 / p90);
+    it stays out of the timed run so that those events cannot perturb it."""
     import torch
     for _ in range(warmup):
         step()
@@ -108,7 +115,40 @@ def time_steps(step, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    pick = lambda f: per[min(steps - 1, int(f * (steps - 1) + 0.5))]
+    STEP_TIMES.clear()
+    STEP_TIMES.update({"ms_p10": round(pick(0.1), 4), "ms_p50": round(pick(0.5), 4),
+                       "ms_p90": round(pick(0.9), 4)})
     return start.elapsed_time(end) / steps, wall
+
+
+def achievable_peaks():
+    """Peaks measured on this GPU with library routines, beside the published ones: a bf16 GEMM
+    (torch.matmul on contiguous 8192 x 8192 operands, fp32 accumulate) and a 1 GiB device-to-
+    device copy (read + write bytes)."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    a = torch.randn((n, n), device="cuda:0", generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda:0", generator=g).to(torch.bfloat16)
+    ms, _ = time_steps(lambda: torch.matmul(a, b), 20, 5)
+    gemm = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    ms_c, _ = time_steps(lambda: y.copy_(x), 20, 5)
+    copy = 2.0 * x.numel() / (ms_c * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_tflops": round(gemm, 1), "hbm_copy_gbs": round(copy, 1),
+            "gemm": "torch.matmul bf16 8192^3", "copy": "1 GiB device copy, read + write"}
 
 
 def kernel_source_hash(files):
@@ -140,7 +180,8 @@ def bench_prefill(w, steps, warmup):
     step = lambda: S.attn_fwd(q, k, v, o, lse, causal=w.causal, scale=w.scale)
     ms, wall = time_steps(step, steps, warmup)
     flops = 2 * (w.Dqk + w.Dv) * w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, w.causal)
-    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
+    return {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+            **STEP_TIMES}
 
 
 def bench_decode(w, steps, warmup):
@@ -170,7 +211,7 @@ def bench_decode(w, steps, warmup):
     ms, wall = time_steps(step, steps, warmup)
     nbytes = kv_bytes + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4
     return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
-            "num_splits": nsp, "kv_copies": ncopies}
+            "num_splits": nsp, "kv_copies": ncopies, **STEP_TIMES}
 
 
 def bench_blocksparse(w, steps, warmup):
@@ -189,7 +230,7 @@ def bench_blocksparse(w, steps, warmup):
     flops = 2 * (w.Dqk + w.Dv) * pairs
     dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
     res = {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
-           "density_vs_causal": pairs / dense}
+           "density_vs_causal": pairs / dense, **STEP_TIMES}
     # The same attention with lists built from Q and K at run time (attn_build_sparse_index:
     # 96 blocks per query block, 1000 columns per head, about the synthetic lists' density).
     topk, ncols = 96, 1000
@@ -241,7 +282,7 @@ def bench_vslash(w, steps, warmup):
     flops = 2 * (w.Dqk + w.Dv) * pairs
     dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
     res = {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
-           "density_vs_causal": pairs / dense}
+           "density_vs_causal": pairs / dense, **STEP_TIMES}
     # Lists built from Q and K at run time (attn_build_vslash_index), as many columns and lines
     # as the synthetic lists. Random inputs have no diagonal structure, so the chosen lines
     # scatter over all offsets and the forward then visits nearly every causal block.
@@ -421,6 +462,8 @@ def main():
                     help="skip the FlashMLA-ETAP decode grid sweep")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the peak-memory comparison at long sequence lengths")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the bf16 GEMM / device copy measurement of achievable peaks")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -486,16 +529,29 @@ def main():
                          "kernel": DENSE_KERNEL,
                          "kernel_source_sha256_16": src_hash},
         })
+    ach = None
+    if not args.no_achievable:
+        log("achievable peaks (bf16 GEMM, device copy) ...")
+        ach = achievable_peaks()
+        out["achievable_peaks"] = ach
+        if HEADLINE in res:
+            out["roofline"]["frac_of_achievable"] = round(res[HEADLINE]["tflops"] /
+                                                          ach["bf16_gemm_tflops"], 4)
     wl = {}
     for name, r in res.items():
+        pct = {kk: r[kk] for kk in ("ms_p10", "ms_p50", "ms_p90") if kk in r}
         if "gbs" in r:
             wl[name] = {"value": round(r["gbs"], 1), "unit": "GB/s", "ms": round(r["ms"], 4),
-                        "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                        **pct, "frac_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4),
                         "num_splits": r["num_splits"], "bytes": r["bytes"]}
+            if ach:
+                wl[name]["frac_of_achievable"] = round(r["gbs"] / ach["hbm_copy_gbs"], 4)
         else:
             wl[name] = {"value": round(r["tflops"], 3), "unit": "TFLOP/s", "ms": round(r["ms"], 4),
-                        "frac_of_mfma_peak": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                        **pct, "frac_of_mfma_peak": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                         "flops": r["flops"]}
+            if ach:
+                wl[name]["frac_of_achievable"] = round(r["tflops"] / ach["bf16_gemm_tflops"], 4)
             if "density_vs_causal" in r:
                 wl[name]["density_vs_causal"] = round(r["density_vs_causal"], 4)
             if "dynamic" in r:

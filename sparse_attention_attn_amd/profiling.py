@@ -15,6 +15,12 @@ Usage (after the three rocprofv3 runs, see the header of each summary for the co
     python -m sparse_attention_attn_amd.profiling summary --stats DIR --fetch DIR --write DIR \
         --calib-mib 1024 --kernel "fwd_dense_kernel<128, 4>" --workload gqa_prefill_8k \
         --command "..." --out profiles/fwd_dense_kernel_gqa_prefill_8k.md [--traffic-json F]
+
+MFMA work and clock. One `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE
+SQ_VALU_MFMA_BUSY_CYCLES` run gives, per dispatch, the bf16 MFMA flops the kernel executed
+(MOPS x 512), the GPU cycles it was active and the SIMD cycles its matrix cores were busy; the
+`mfma` subcommand sets the flops against the algorithmic count and divides the active cycles
+by the dispatch's own duration (its start and end timestamps) to give the shader clock.
 """
 
 from __future__ import annotations
@@ -84,6 +90,59 @@ def copy_factor(dispatches, calib_mib, moved_per_mib=1.0):
     if not seen or total <= 0:
         raise ValueError("no calibration copy dispatch found")
     return calib_mib * 1024.0 * moved_per_mib / total
+
+
+def read_counter_rows(counter_dir, counter):
+    """(kernel name, value, duration ns) per dispatch, in dispatch order, for one counter."""
+    path = _one(os.path.join(counter_dir, "**", "*counter_collection.csv"))
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                dur = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]),
+                             dur))
+    rows.sort()
+    return [(n, v, d) for _, n, v, d in rows]
+
+
+def mfma_summary(counter_dir, kernel, workload, command, algorithmic_flops, simds=1024, xcds=8):
+    """Per-dispatch averages of the MFMA and clock counters for `kernel` (see module doc)."""
+    def avg(counter):
+        rows = [(v, d) for n, v, d in read_counter_rows(counter_dir, counter) if kernel in n]
+        if not rows:
+            raise ValueError(f"kernel {kernel!r} not found for {counter}")
+        return (sum(v for v, _ in rows) / len(rows), sum(d for _, d in rows) / len(rows),
+                len(rows))
+    mops, dur, n = avg("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    gui, dur_g, _ = avg("GRBM_GUI_ACTIVE")
+    busy, _, _ = avg("SQ_VALU_MFMA_BUSY_CYCLES")
+    flops = mops * 512.0
+    gui /= xcds  # the CSV sums GRBM_GUI_ACTIVE over the XCDs, each of which counts every cycle
+    rec = {"workload": workload, "kernel": kernel, "command": command, "dispatches": n,
+           "mfma_flops_per_dispatch": flops, "algorithmic_flops": algorithmic_flops,
+           "executed_over_algorithmic": flops / algorithmic_flops if algorithmic_flops else None,
+           "gpu_active_cycles": gui, "dispatch_ns": dur_g,
+           "shader_clock_ghz": gui / dur_g if dur_g > 0 else None,
+           "mfma_busy_pct": 100.0 * busy / (gui * simds) if gui > 0 else None}
+    return rec
+
+
+def render_mfma_md(rec):
+    lines = [f"# {rec['kernel']} — {rec['workload']}: MFMA work and clock", "",
+             "Counter run (run from the repository root):", "", "```", rec["command"], "```", "",
+             f"- dispatches averaged: {rec['dispatches']}",
+             f"- bf16 MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): "
+             f"{rec['mfma_flops_per_dispatch']:,.0f}",
+             f"- algorithmic flops (2 (Dqk + Dv) per visible pair): {rec['algorithmic_flops']:,}",
+             f"- executed / algorithmic: {rec['executed_over_algorithmic']:.4f} (masked parts of "
+             "the diagonal tiles are computed, then discarded)",
+             f"- GPU active cycles (GRBM_GUI_ACTIVE, per XCD): {rec['gpu_active_cycles']:,.0f} over "
+             f"{rec['dispatch_ns'] / 1e3:.1f} us of dispatch: shader clock "
+             f"{rec['shader_clock_ghz']:.3f} GHz",
+             f"- MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over active cycles x 1024 SIMDs): "
+             f"{rec['mfma_busy_pct']:.1f}%", ""]
+    return "\n".join(lines)
 
 
 def per_dispatch(dispatches, kernel):
@@ -159,7 +218,20 @@ def main(argv=None):
                    help="comma list of csrc files whose hash tags the traffic record")
     s.add_argument("--out", required=True)
     s.add_argument("--traffic-json")
+    m = sub.add_parser("mfma")
+    m.add_argument("--dir", required=True)
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--algorithmic-flops", type=int, required=True)
+    m.add_argument("--out", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "mfma":
+        rec = mfma_summary(a.dir, a.kernel, a.workload, a.command, a.algorithmic_flops)
+        with open(a.out, "w") as fh:
+            fh.write(render_mfma_md(rec))
+        print(json.dumps({k: v for k, v in rec.items() if k != "command"}))
+        return
     rec, stats = summary(a.stats, a.fetch, a.write, a.calib_mib, a.kernel, a.workload,
                          a.stats_command, a.algorithmic_bytes)
     with open(a.out, "w") as fh:
