@@ -279,6 +279,33 @@ def csr_allowed_fn(blk_ptr, blk_idx, col_ptr, col_idx, hq, nqb, lk, block_m=64, 
     return fn
 
 
+def blocksparse_keys(blocks, cols, lk, block_n=64):
+    """Sorted key positions of the block/column union for one query block: every key of the
+    listed blocks and every listed column, each once, inside [0, Lk)."""
+    parts = [np.arange(int(kb) * block_n, min((int(kb) + 1) * block_n, lk), dtype=np.int64)
+             for kb in np.asarray(blocks, dtype=np.int64)]
+    parts.append(np.asarray(cols, dtype=np.int64))
+    keys = np.unique(np.concatenate(parts)) if parts else np.zeros(0, np.int64)
+    return keys[(keys >= 0) & (keys < lk)]
+
+
+def attention_rows_over_keys(q_rows, rows, k_head, v_head, scale, keys, lq, lk, causal):
+    """Attention of some query rows of one (batch, query head) when only `keys` can be visible:
+    the plain definition with the score matrix restricted to those columns (the other keys
+    have weight zero by the mask), the causal limit applied per row.
+
+    q_rows [n, Dqk]; k_head [Lk, Dqk]; v_head [Lk, Dv]; keys sorted. Returns (O [n, Dv], LSE [n]).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    s = _scores(np.asarray(q_rows, np.float64), np.asarray(k_head, np.float64)[keys],
+                np.float64(scale))
+    if causal:
+        s = np.where(keys[None, :] <= (rows + lk - lq)[:, None], s, -np.inf)
+    p, m, l = _softmax_rows(s)
+    return _weighted_values(p, np.asarray(v_head, np.float64)[keys]), _lse(m, l)
+
+
 def slash_row_mask(rows, lq, lk, offsets):
     """Visible-key mask [len(rows), Lk] of the slash lines of one (batch, query head).
 

@@ -316,3 +316,29 @@ def test_split_with_empty_trailing_split():
     o2, l2 = A.attention_splitkv(q, k, v, 0.5, False, 3)
     _assert_close(o1, o2, 1e-12)
     _assert_close(l1, l2, 1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gathered_keys_equal_dense_mask(seed):
+    """The gather form (scores over the listed keys only) equals the dense-mask form on random
+    lists, causal, with Lq < Lk."""
+    rng = np.random.default_rng(300 + seed)
+    Lq, Lk, D, bs = 150, 260, 8, 64
+    q, k, v = _rand((Lq, D), 40 + seed), _rand((Lk, D), 50 + seed), _rand((Lk, D), 60 + seed)
+    nkb = -(-Lk // bs)
+    cols = np.unique(rng.integers(0, Lk, 12))
+    for qb in range(-(-Lq // bs)):
+        blocks = np.unique(rng.integers(0, nkb, 2))
+        rows = np.arange(qb * bs, min((qb + 1) * bs, Lq))
+        keys = A.blocksparse_keys(blocks, cols, Lk, bs)
+        og, lg = A.attention_rows_over_keys(q[rows], rows, k, v, 0.6, keys, Lq, Lk, True)
+        mask = A.blocksparse_row_mask(rows, Lk, lambda _: blocks, cols, bs, bs)
+        od, ld = A.attention_query_rows(q[rows], k[None, :, None], v[None, :, None], 0.6, True,
+                                        0, 0, rows, Lq, 1, mask)
+        _assert_close(og, od, 1e-12)
+        _assert_close(lg, ld, 1e-12)
+
+
+def test_blocksparse_keys_union_counts_each_key_once():
+    keys = A.blocksparse_keys([0, 2], [1, 5, 64, 130, 300], 200, 64)
+    assert list(keys) == sorted(set(range(0, 64)) | set(range(128, 192)) | {64})
