@@ -127,29 +127,49 @@ def test_planted_columns_counted_once():
     check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "planted-cols")
 
 
-def test_blocksparse_workload_full_size_sampled_rows():
-    """The 128K block-sparse workload at full size (the launch the bench times); the oracle
-    checks 128 sampled rows (first 32, last 32, 64 seeded) of 8 query heads."""
+@pytest.fixture(scope="module")
+def sparse128k():
+    """The 128K block-sparse workload at full size, run once (the launch the bench times):
+    inputs, lists and the GPU output on 4096 sampled rows (rows 0-63, the last 64 rows and
+    3968 seeded rows)."""
     w = WORKLOADS["blocksparse_128k"]
     say(f"blocksparse_128k full size {w}")
     q, k, v = make_qkv(w)
     lists = make_blocksparse_lists(w.B, w.Hq, w.Lq, w.Lk, 1000 * w.index + 3)
     o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, w.scale)
-    rows = sampled_rows(w.Lq, 128, 1000 * w.index + 4, edge=32)
-    qf, kf, vf = to_f64(q[:, rows]), to_f64(k), to_f64(v)
-    fn = A.csr_allowed_fn(*lists, hq=w.Hq, nqb=w.Lq // 64, lk=w.Lk)
+    rows = sampled_rows(w.Lq, 4096, 1000 * w.index + 4, edge=64)
+    return (w, q, k, v, lists, rows, o[0, rows].float().cpu().numpy(),
+            lse[0][:, rows].cpu().numpy())
+
+
+@pytest.mark.parametrize("group", range(4), ids=lambda g: f"heads{8 * g}-{8 * g + 7}")
+def test_blocksparse_workload_full_size_sampled_rows(sparse128k, group):
+    """The 4096 sampled rows of 8 query heads per case (all 32 over the four cases). The
+    oracle scores each query block's sampled rows over that block's listed keys only
+    (attention_rows_over_keys), which is the plain definition restricted to the keys the mask
+    can leave visible."""
+    w, q, k, v, (bp, bi, cp, ci), rows, of, lf = sparse128k
+    nqb = w.Lq // 64
+    g = w.Hq // w.Hkv
     sc = A.effective_scale(w.scale)
-    of = o[0, rows].float().cpu().numpy().astype(np.float64)
-    lf = lse[0][:, rows].cpu().numpy().astype(np.float64)
+    qbs = rows // 64
     got_o, ref_o, got_l, ref_l = [], [], [], []
-    for h in range(0, w.Hq, 4):
-        orow, lrow = A.attention_query_rows(qf[0, :, h], kf, vf, sc, True, 0, h, rows, w.Lq, w.Hq,
-                                            fn(0, h, rows))
-        got_o.append(of[:, h])
-        ref_o.append(orow)
-        got_l.append(lf[h])
-        ref_l.append(lrow)
-    check_parity(np.stack(got_o), np.stack(ref_o), np.stack(got_l), np.stack(ref_l), "sparse128k")
+    for h in range(8 * group, 8 * group + 8):
+        kh = k[0, :, h // g].double().numpy()
+        vh = v[0, :, h // g].double().numpy()
+        cols = ci[cp[h]:cp[h + 1]]
+        for qb in np.unique(qbs):
+            sel = qbs == qb
+            rr = rows[sel]
+            keys = A.blocksparse_keys(bi[bp[h * nqb + qb]:bp[h * nqb + qb + 1]], cols, w.Lk)
+            orow, lrow = A.attention_rows_over_keys(q[0, rr, h].double().numpy(), rr, kh, vh, sc,
+                                                    keys, w.Lq, w.Lk, True)
+            got_o.append(of[sel, h])
+            ref_o.append(orow)
+            got_l.append(lf[h, sel])
+            ref_l.append(lrow)
+    check_parity(np.concatenate(got_o), np.concatenate(ref_o), np.concatenate(got_l),
+                 np.concatenate(ref_l), f"sparse128k 4096 rows, heads {8 * group}-{8 * group + 7}")
 
 
 def test_blocksparse_deterministic():
