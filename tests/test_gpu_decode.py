@@ -201,3 +201,15 @@ def test_etap_grid_point_full():
     o_ref, lse_ref = A.attention(to_f64(q), kf, A.mla_value_view(kf, 512),
                                  A.effective_scale(w.scale), True)
     check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "etap_b16_q2_k16384")
+
+
+def test_peaky_gqa_decode():
+    """Config-3 shape with Q x 4 (concentrated attention) through split-KV + combine."""
+    import torch
+    w = WORKLOADS["gqa_decode_4k"]
+    say("peaky gqa_decode_4k")
+    q, k, v = make_qkv(w)
+    q = (q.float() * 4.0).to(torch.bfloat16)
+    o, lse = _decode(q.to(DEV), k.to(DEV), v.to(DEV), False, w.scale)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(w.scale), False)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "peaky gqa_decode_4k")

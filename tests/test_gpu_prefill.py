@@ -190,3 +190,41 @@ def test_prefill_deterministic():
     o1, l1 = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, 0.088)
     o2, l2 = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, 0.088)
     assert bool((o1 == o2).all()) and bool((l1 == l2).all())
+
+
+def _peaky(t):
+    """Q scaled by 4 in fp32, then rounded to bf16: scores with 4x the spread, attention that
+    concentrates on few keys (exercises the softmax's reference moves and large weights)."""
+    import torch
+    return (t.float() * 4.0).to(torch.bfloat16)
+
+
+def test_peaky_tiny_causal():
+    w = WORKLOADS["tiny_causal"]
+    say("peaky tiny_causal")
+    q, k, v = make_qkv(w)
+    q = _peaky(q)
+    o, lse = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, w.scale)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(w.scale), True)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "peaky tiny")
+
+
+def test_peaky_gqa_prefill_8k_sampled_rows():
+    """Config-2 shape with Q x 4, 96 sampled rows of every query head."""
+    w = WORKLOADS["gqa_prefill_8k"]
+    say("peaky gqa_prefill_8k")
+    q, k, v = make_qkv(w)
+    q = _peaky(q)
+    o, lse = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, w.scale)
+    rows = sampled_rows(w.Lq, 96, 1000 * w.index + 5, edge=32)
+    qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
+    of, lf = to_f64(o), to_f64(lse)
+    sc = A.effective_scale(w.scale)
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for h in range(w.Hq):
+        orow, lrow = A.attention_rows(qf, kf, vf, sc, True, 0, h, rows)
+        got_o.append(of[0, rows, h, :])
+        ref_o.append(orow)
+        got_l.append(lf[0, h, rows])
+        ref_l.append(lrow)
+    check_parity(np.stack(got_o), np.stack(ref_o), np.stack(got_l), np.stack(ref_l), "peaky 8k")
