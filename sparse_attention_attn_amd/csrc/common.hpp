@@ -70,13 +70,6 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const char* lds_base, uint32_
   return __builtin_bit_cast(bf16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
 }
 
-// Asynchronous 16-byte global -> LDS copy. lds_wave_base must be identical across the wave;
-// lane l's bytes land at lds_wave_base + 16*l.
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const gbl_void_t*)gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // ------------------------------------------------------------------------------------------
 // LDS addressed by 32-bit byte addresses. The compiler folds a compile-time offset of up to
 // 64 KiB into the instruction's offset field, so reads at (base register + constant) need no
@@ -117,6 +110,24 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
                "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
+
+// The same copy from a per-lane 64-bit source address (rows gathered from anywhere).
+__device__ __forceinline__ void dma16_vaddr(const void* gsrc, uint32_t lds) {
+  // s_nop 4: the wait states after the SALU write of M0 (see dma16_sbase).
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc),
+               "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// 4-byte-per-lane variant: lane l's word lands at LDS address lds + 4*l.
+__device__ __forceinline__ void dma4_vaddr(const void* gsrc, uint32_t lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc),
+               "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// Waits until every vector memory instruction of this wave (copies included) has completed.
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -208,11 +208,11 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, const WaveState<D>& 
 }
 
 // Maps blockIdx.x to a logical work id. The hardware deals workgroups round-robin over the 8
-// XCDs (each with its own L2) in blockIdx order. Logical ids are cut into chunks of 32 (8 pairs
-// of query blocks x 4 query heads of one KV head) and chunk c runs on XCD c % 8: the query
-// blocks that share most of their local band of key blocks meet in one L2, while all XCDs
-// work on neighbouring chunks, i.e. on the same KV head, whose K/V then fits the device-wide
-// cache.
+// XCDs (each with its own L2) in blockIdx order. Logical ids are cut into chunks of 32 (8
+// groups of query blocks x 4 query heads of one KV head) and chunk c runs on XCD c % 8: the
+// query blocks that share most of their local band of key blocks meet in one L2, while all
+// XCDs work on neighbouring chunks, i.e. on the same KV head, whose K/V then fits the
+// device-wide cache.
 __device__ __forceinline__ int logical_block(int xcd_remap) {
   const int bid = (int)blockIdx.x;
   if (!xcd_remap) return bid;
@@ -222,64 +222,74 @@ __device__ __forceinline__ int logical_block(int xcd_remap) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Block-sparse forward: one workgroup of 4 waves per (b, query head, pair of 64-row query
-// blocks 2p and 2p+1); waves 0-1 own the rows of block 2p, waves 2-3 those of block 2p+1, 32
-// rows each. The two blocks' lists share most of their key blocks (the local band moves by one
-// block), so the workgroup streams each key tile once for both, and a wave skips the tiles its
-// own block does not list. With two such workgroups per CU every SIMD runs two waves, which
-// hide each other's softmax and waits.
-// Phase 1 walks the union of the two listed-block sets in ascending order; phase 2 gathers the
-// head's vertical columns that are causally visible to the pair and not inside a block both
-// blocks list, 64 at a time, and each wave masks the columns inside its own listed blocks
-// (so a key is never counted twice).
+// Block-sparse forward: one workgroup of 2·QB waves per (b, query head, group of QB = 2
+// consecutive 64-row query blocks QB·p .. QB·p+QB-1); waves 2q and 2q+1 own the rows of block
+// QB·p+q, 32 rows each. Neighbouring blocks' lists share most of their key blocks (the local
+// band moves by one block), so the workgroup streams each key tile once for the whole group,
+// and a wave skips the tiles its own block does not list. With two such workgroups per CU
+// every SIMD runs two waves, which hide each other's softmax and waits: while the waves of
+// one workgroup skip a tile, the other workgroup's waves keep the matrix core busy. (Four
+// blocks per workgroup, with eight waves, one workgroup per CU and a four-stage ring, shares
+// more tiles but measured slower: the workgroup barrier of every tile then idles the six
+// waves whose blocks do not list it.)
+// Phase 1 walks the union of the group's listed-block sets in ascending order; phase 2
+// gathers the head's vertical columns that are causally visible to the group and not inside
+// a block every block of the group lists, 64 at a time, and each wave masks the columns
+// inside its own listed blocks (so a key is never counted twice).
 //
 // With SLASH, phase 3 adds the head's slash lines (MInference article, paragraph on the
 // vertical-slash pattern): the line at offset o >= 0 lets query row i see key i + off - o
-// (off = Lk - Lq). Setup marks the 64-key blocks any line crosses inside the pair's rows;
+// (off = Lk - Lq). Setup marks the 64-key blocks any line crosses inside the group's rows;
 // phase 3 runs each marked block that the wave's own block does not list as a tile whose mask
 // keeps a pair (row, key) only when row + off - key is a listed offset and key is not a listed
 // column (those keys were counted in phase 2). The offsets and the columns of a head come as
-// two bitmaps (vs_bits_kernel); each lane loads the 96 + 64 bits its 32 scores need together
-// with the tile's copy, so the copy wait of the next step covers those loads too.
+// two bitmaps (vs_bits_kernel); the words of both that a tile's mask needs are copied into
+// LDS together with the tile, and each lane reads the 96 + 64 bits its 32 scores need.
 // ------------------------------------------------------------------------------------------
 constexpr int kSeg = 512;              // ids examined per compaction pass
 constexpr int kMaxBitmapWords = 512;   // listed-block bitmaps: up to 16384 key blocks (1M keys)
 constexpr int kSlashBitmapWords = kVslashMaxLk / 64 / 32;  // crossed blocks (slash variant)
-constexpr int kColMask = (1 << 29) - 1;  // column id bits of a phase-2 entry (flags above)
+constexpr int kFlagShift = 24;         // phase-2 entry: column id below, block flags above
+constexpr int kColMask = (1 << kFlagShift) - 1;
+constexpr int kMaskOffWords = 48;      // offset-bitmap words copied per slash tile
 
-template <int D, bool SLASH>
-__global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
+template <int D, bool SLASH, int QB>
+__global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
-  constexpr int NW = 4;
+  constexpr int NW = 2 * QB;
   constexpr int NT = NW * 64;
+  constexpr int NS = 2;  // ring stages
+  static_assert(QB == 2, "two query blocks per workgroup (two workgroups per CU)");
+  static_assert(kFlagShift + QB <= 31, "phase-2 flags fit an int");
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
-  __shared__ uint32_t bm[2][kMaxBitmapWords];                  // listed blocks of 2p, 2p+1
+  __shared__ uint32_t bm[QB][kMaxBitmapWords];                 // listed blocks of the group
   __shared__ uint32_t tbits[SLASH ? kSlashBitmapWords : 1];  // blocks crossed by a slash line
   __shared__ int kept[kSeg];
   __shared__ int wave_cnt[NW];
+  __shared__ uint32_t mwl[SLASH ? NS : 1][64];  // per stage: the tile's mask words (slash)
 
   const int tid = (int)threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
   const int nqb = a.n_qtiles;
-  const int npair = (nqb + 1) / 2;
+  const int ngrp = (nqb + QB - 1) / QB;
   int lid = logical_block(a.xcd_remap);
   const int hg = lid % a.g;
   lid /= a.g;
-  const int pr = npair - 1 - (lid % npair);
-  lid /= npair;
+  const int pr = ngrp - 1 - (lid % ngrp);
+  lid /= ngrp;
   const int hkv = lid % a.Hkv;
   const int b = lid / a.Hkv;
   const int hq = hkv * a.g + hg;
 
-  const int qbA = 2 * pr;
-  const int myq = w >> 1;  // 0: block qbA, 1: block qbA + 1
-  const int q0 = qbA * 64;                     // first row of the workgroup
+  const int qbA = QB * pr;
+  const int myq = w >> 1;  // this wave's block is qbA + myq
+  const int q0 = qbA * 64;                       // first row of the workgroup
   const int qw0 = q0 + 64 * myq + 32 * (w & 1);  // first row of this wave
   const int row = qw0 + (l & 31);
-  const bool active = qw0 < a.Lq;              // the wave has rows
-  const int qlast = min(q0 + 128, a.Lq) - 1;   // last row of the workgroup
+  const bool active = qw0 < a.Lq;                // the wave has rows
+  const int qlast = min(q0 + 64 * QB, a.Lq) - 1;  // last row of the workgroup
   const int qwlast = min(qw0 + 31, a.Lq - 1);
   const int klim = a.causal ? min(a.Lk - 1, qlast + a.off) : a.Lk - 1;  // last visible key
   const int lkm1 = a.Lk - 1;
@@ -287,16 +297,29 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
   const int bh = b * a.Hq + hq;
   const int nwords = (a.nkb + 31) >> 5;
   auto listed = [&](int q, int kb) -> bool { return (bm[q][kb >> 5] >> (kb & 31)) & 1u; };
+  // blocks listed by at least one / by every block of the group, word kb/32
+  auto any_word = [&](int wd) -> uint32_t {
+    uint32_t v = 0u;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) v |= bm[q][wd];
+    return v;
+  };
+  auto all_word = [&](int wd) -> uint32_t {
+    uint32_t v = ~0u;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) v &= bm[q][wd];
+    return v;
+  };
 
   for (int i = tid; i < nwords; i += NT) {
-    bm[0][i] = 0u;
-    bm[1][i] = 0u;
+#pragma unroll
+    for (int q = 0; q < QB; ++q) bm[q][i] = 0u;
   }
   if constexpr (SLASH)
     for (int i = tid; i < nwords; i += NT) tbits[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < QB; ++q) {
     if (qbA + q >= nqb) break;
     const int64_t lrow = (int64_t)bh * nqb + qbA + q;
     const int s1 = a.blk_ptr[lrow + 1];
@@ -348,44 +371,54 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
 
   WaveState<D> ws;
   load_q<D>(a, ws, b, hq, row, l);
-  TileOffsets<D, NW> off;
-  off.init(a, w, l);
+  TileByteOffsets<D, NW> boff;
+  boff.init(a, w, l);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint16_t* kbp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
+  auto stage = [&](auto S) -> char* { return decltype(S)::value == 0 ? st0 : st1; };
+  auto stage_addr = [&](auto S) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(stage(S)));
+  };
   // copy of the 64-key block starting at key `base` (inside the sequence) into stage S
   auto issue_block = [&](auto S, int base) {
-    char* st = decltype(S)::value == 0 ? st0 : st1;
     if (base + BN <= a.Lk) {
-      issue_tile_fast<D, NW>(st, kbp + (int64_t)base * a.k_sl, vbp + (int64_t)base * a.v_sl, off, w);
+      issue_tile_sbase<D, NW>(stage_addr(S), kbp + (int64_t)base * a.k_sl,
+                              vbp + (int64_t)base * a.v_sl, boff, wu);
     } else {
-      issue_tile_slow<D, NW>(a, st, kbp, vbp, [&](int r) { return min(base + r, lkm1); }, w, l);
+      issue_tile_gather<D, NW>(a, stage_addr(S), kbp, vbp, [&](int r) { return min(base + r, lkm1); },
+                               w, l);
     }
   };
-  // the two-stage ring over tiles 0..ntl-1: step(t) waits for tile t, starts tile t+1 and
-  // runs the math of tile t
+  // The two-stage ring over tiles 0..ntl-1 (tile t in stage t % 2). Step t waits for tile t
+  // (this wave's copies, then the barrier for every wave's), starts the copy of tile t+1 into
+  // the other stage, whose readers (the math of tile t-1) all passed the barrier, and runs the
+  // math of tile t. The copies are invisible to the compiler, so it adds no waits of its own
+  // before the LDS reads; the barrier carries no memory fence (nothing else needs ordering).
   auto run = [&](int ntl, auto issue_fn, auto math_fn) {
+    wait_vmcnt_visible0();  // the Q operands (and any earlier load) are in registers
     if (ntl > 0) issue_fn(ic<0>{}, 0);
     auto step = [&](auto S, int t) {
       constexpr int s = decltype(S)::value;
       wait_dma_all();
-      __syncthreads();
+      barrier_lds();
       if (t + 1 < ntl) issue_fn(ic<1 - s>{}, t + 1);
       math_fn(S, t);
     };
-    for (int t = 0; t < ntl; t += 2) {
+    for (int t = 0; t < ntl; t += NS) {
       step(ic<0>{}, t);
       if (t + 1 < ntl) step(ic<1>{}, t + 1);
     }
     __syncthreads();  // stages and kept[] free for the next pass
   };
 
-  // ---- phase 1: the union of the two blocks' listed key blocks, 512 block ids per pass
+  // ---- phase 1: the union of the group's listed key blocks, 512 block ids per pass
   for (int c0 = 0; c0 < nwords * 32; c0 += kSeg) {
     const int cnt = compact(min(kSeg, nwords * 32 - c0),
                             [&](int i) {
                               const int kb = c0 + i;
-                              return (((bm[0][kb >> 5] | bm[1][kb >> 5]) >> (kb & 31)) & 1u) != 0u;
+                              return ((any_word(kb >> 5) >> (kb & 31)) & 1u) != 0u;
                             },
                             [&](int i) { return c0 + i; });
     run(cnt, [&](auto S, int t) { issue_block(S, kept[t] * BN); },
@@ -395,13 +428,13 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
           if (!active || !listed(myq, kb)) return;
           if (a.causal && base > qwlast + a.off) return;
           const bool masked = base + BN > a.Lk || (a.causal && base + BN - 1 > qw0 + a.off);
-          tile_math<D>(a, ws, decltype(S)::value == 0 ? st0 : st1, row, masked,
+          tile_math<D>(a, ws, stage(S), row, masked,
                        [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
         });
   }
 
-  // ---- phase 2: vertical columns. An entry is the column id with bit 29 + q set when the
-  // column lies inside a block that block q lists.
+  // ---- phase 2: vertical columns. An entry is the column id with bit kFlagShift + q set
+  // when the column lies inside a block that block q of the group lists.
   const int cstart = a.col_ptr[bh];
   const int cend = a.col_ptr[bh + 1];
   for (int seg = cstart; seg < cend; seg += kSeg) {
@@ -411,31 +444,34 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
                             [&](int i) {
                               const int col = a.col_idx[seg + i];
                               if (col < 0 || col > klim) return false;
-                              return !(listed(0, col >> 6) && listed(1, col >> 6));
+                              return ((all_word(col >> 11) >> ((col >> 6) & 31)) & 1u) == 0u;
                             },
                             [&](int i) {
                               const int col = a.col_idx[seg + i];
-                              return col | ((int)listed(0, col >> 6) << 29) |
-                                     ((int)listed(1, col >> 6) << 30);
+                              int e = col;
+#pragma unroll
+                              for (int q = 0; q < QB; ++q)
+                                e |= (int)listed(q, col >> 6) << (kFlagShift + q);
+                              return e;
                             });
     // cnt columns make ceil(cnt / 64) tiles; tile t gathers entries 64t .. 64t+63
     run((cnt + BN - 1) / BN,
         [&](auto S, int t) {
           const int cb = t * BN;
-          issue_tile_slow<D, NW>(a, decltype(S)::value == 0 ? st0 : st1, kbp, vbp,
-                                 [&](int r) { return kept[cb + r < cnt ? cb + r : cb] & kColMask; },
-                                 w, l);
+          issue_tile_gather<D, NW>(
+              a, stage_addr(S), kbp, vbp,
+              [&](int r) { return kept[cb + r < cnt ? cb + r : cb] & kColMask; }, w, l);
         },
         [&](auto S, int t) {
           const int cb = t * BN;
           if (!active) return;
           // columns are ascending: skip if even the first one is beyond this wave's horizon
           if (a.causal && (kept[cb] & kColMask) > qwlast + a.off) return;
-          tile_math<D>(a, ws, decltype(S)::value == 0 ? st0 : st1, row, true,
+          tile_math<D>(a, ws, stage(S), row, true,
                        [&](int kl) {
                          if (cb + kl >= cnt) return -1;
                          const int e = kept[cb + kl];
-                         return ((e >> (29 + myq)) & 1) ? -1 : (e & kColMask);
+                         return ((e >> (kFlagShift + myq)) & 1) ? -1 : (e & kColMask);
                        }, l);
         });
   }
@@ -447,25 +483,30 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
     const uint32_t* cbits = a.cl_bits + (int64_t)bh * a.bits_words;
     // Lane's window: bitmap bit (o + 128) of its local key c's offset is at rw - base + 59 - c.
     const int rw = row + a.off + 69 - 4 * h;
-    uint32_t mw[2][5];
+    const int rw0 = q0 + a.off + 65;  // smallest rw of the group (row q0, h = 1)
+    // first offset word of the group's window for the tile at `base`
+    auto win0 = [&](int base) { return max(rw0 - base, 0) >> 5; };
     for (int c0 = 0; c0 < nwords * 32; c0 += kSeg) {
       const int cnt = compact(min(kSeg, nwords * 32 - c0),
                               [&](int i) {
                                 const int kb = c0 + i;
-                                const uint32_t both = bm[0][kb >> 5] & bm[1][kb >> 5];
-                                return (((tbits[kb >> 5] & ~both) >> (kb & 31)) & 1u) != 0u;
+                                const uint32_t all = all_word(kb >> 5);
+                                return (((tbits[kb >> 5] & ~all) >> (kb & 31)) & 1u) != 0u;
                               },
                               [&](int i) { return c0 + i; });
       run(cnt,
           [&](auto S, int t) {
             constexpr int s = decltype(S)::value;
             const int base = kept[t] * BN;
-            const uint32_t* sp = sbits + (max(rw - base, 0) >> 5);
-            mw[s][0] = sp[0];
-            mw[s][1] = sp[1];
-            mw[s][2] = sp[2];
-            mw[s][3] = cbits[base >> 5];
-            mw[s][4] = cbits[(base >> 5) + 1];
+            // Wave 0 copies the tile's mask words next to it: offset words win0 .. win0+47
+            // (the pair's rows need at most 8 of them) and the two column words of the tile;
+            // the ring's wait covers this copy with the tile's.
+            if (wu == 0) {
+              const int j0 = win0(base);
+              const uint32_t* src = l < kMaskOffWords ? sbits + min(j0 + l, a.bits_words - 1)
+                                                      : cbits + (base >> 5) + (l == kMaskOffWords + 1);
+              dma4_vaddr(src, lds_addr(&mwl[s][0]));
+            }
             issue_block(S, base);
           },
           [&](auto S, int t) {
@@ -475,21 +516,24 @@ __global__ __launch_bounds__(256, 2) void fwd_sparse_kernel(const FwdArgs a) {
             if (!active || listed(myq, kb)) return;
             if (base > qwlast + a.off) return;  // past every row of this wave on every line
             const int sh = max(rw - base, 0) & 31;
-            tile_math_mask<D>(a, ws, s == 0 ? st0 : st1, true, [&](f32x16& s0, f32x16& s1) {
+            const int j = (max(rw - base, 0) >> 5) - win0(base);
+            const uint32_t m0 = mwl[s][j], m1 = mwl[s][j + 1], m2 = mwl[s][j + 2];
+            const uint32_t m3 = mwl[s][kMaskOffWords], m4 = mwl[s][kMaskOffWords + 1];
+            tile_math_mask<D>(a, ws, stage(S), true, [&](f32x16& s0, f32x16& s1) {
               // offsets: bit x of (d1:d0) is local key c = 59 - x; reversed and shifted, bit c
-              const uint32_t d0 = __builtin_amdgcn_alignbit(mw[s][1], mw[s][0], sh);
-              const uint32_t d1 = __builtin_amdgcn_alignbit(mw[s][2], mw[s][1], sh);
+              const uint32_t d0 = __builtin_amdgcn_alignbit(m1, m0, sh);
+              const uint32_t d1 = __builtin_amdgcn_alignbit(m2, m1, sh);
               const uint32_t r0 = __builtin_bitreverse32(d1), r1 = __builtin_bitreverse32(d0);
               // listed columns: bit c is key base + 4h + c
-              const uint32_t c0w = __builtin_amdgcn_alignbit(mw[s][4], mw[s][3], 4 * h);
-              const uint32_t c1w = mw[s][4] >> (4 * h);
+              const uint32_t c0w = __builtin_amdgcn_alignbit(m4, m3, 4 * h);
+              const uint32_t c1w = m4 >> (4 * h);
               const uint32_t vlo = ((r0 >> 4) | (r1 << 28)) & ~c0w;
               const uint32_t vhi = (r1 >> 4) & ~c1w;
 #pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                const int c = 8 * (j >> 2) + (j & 3);
-                if (!((vlo >> c) & 1u)) s0[j] = -INFINITY;
-                if (!((vhi >> c) & 1u)) s1[j] = -INFINITY;
+              for (int jj = 0; jj < 16; ++jj) {
+                const int c = 8 * (jj >> 2) + (jj & 3);
+                if (!((vlo >> c) & 1u)) s0[jj] = -INFINITY;
+                if (!((vhi >> c) & 1u)) s1[jj] = -INFINITY;
               }
             }, l);
           });
@@ -521,15 +565,19 @@ __global__ __launch_bounds__(256) void vs_bits_kernel(const FwdArgs a) {
   }
 }
 
+// Query blocks per workgroup.
+constexpr int kSparseQB = 2;
+
 template <int D, bool SLASH>
 hipError_t launch_sparse_t(const FwdArgs& a, hipStream_t stream) {
-  const int64_t nwg = (int64_t)a.B * a.Hq * ((a.n_qtiles + 1) / 2);
+  constexpr int QB = kSparseQB;
+  const int64_t nwg = (int64_t)a.B * a.Hq * ((a.n_qtiles + QB - 1) / QB);
   FwdArgs aa = a;
   aa.xcd_remap = (nwg % 256 == 0) ? 1 : 0;
   if constexpr (SLASH)
     hipLaunchKernelGGL(vs_bits_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, stream, aa);
-  hipLaunchKernelGGL((fwd_sparse_kernel<D, SLASH>), dim3((unsigned)nwg), dim3(256), 0, stream,
-                     aa);
+  hipLaunchKernelGGL((fwd_sparse_kernel<D, SLASH, QB>), dim3((unsigned)nwg), dim3(2 * QB * 64),
+                     0, stream, aa);
   return hipGetLastError();
 }
 

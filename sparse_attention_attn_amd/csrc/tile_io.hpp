@@ -59,20 +59,23 @@ __device__ __forceinline__ void slot_rc(uint32_t slot, uint32_t& r, uint32_t& c)
   c = cs < (uint32_t)CPR ? cs : 0u;
 }
 
-// Copy instruction i (K instructions first, then V) of one tile. key_of(r) must return a valid
-// key row, so every load is in bounds.
+// Copy instruction i (K instructions first, then V) of one tile whose rows are gathered:
+// key_of(r) must return a valid key row, so every load is in bounds. `st` is the stage's LDS
+// address.
 template <int D, class KeyOf>
-__device__ __forceinline__ void copy_instr_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
-                                                const uint16_t* vbase, KeyOf key_of, int i, int l) {
+__device__ __forceinline__ void copy_instr_gather(const FwdArgs& a, uint32_t st,
+                                                  const uint16_t* kbase, const uint16_t* vbase,
+                                                  KeyOf key_of, int i, int l) {
   using C = TileCfg<D>;
   uint32_t r, c;
   if (i < C::KINSTR) {
     kslab_rc<D>(i, l, r, c);
-    dma16(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + i * 1024);
+    dma16_vaddr(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + (uint32_t)i * 1024u);
   } else {
     const int iv = i - C::KINSTR;
     slot_rc<C::VSPR, C::CPR>((uint32_t)iv * 64u + (uint32_t)l, r, c);
-    dma16(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8, st + C::KT_BYTES + iv * 1024);
+    dma16_vaddr(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8,
+                st + C::KT_BYTES + (uint32_t)iv * 1024u);
   }
 }
 
@@ -87,54 +90,14 @@ __device__ __forceinline__ void wait_vmcnt_n() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   }
 }
+// vmcnt(0) in a form the compiler sees: afterwards it knows that every earlier load of the
+// wave has completed and adds no waits of its own for those loads (it does not see the copies,
+// so a wait it adds for an older register load would also drain the copies in flight).
+__device__ __forceinline__ void wait_vmcnt_visible0() {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+}
 // Workgroup barrier without a memory fence (the copies it orders are waited for explicitly).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
-
-// Per-lane element offsets (relative to a tile's first key row) of this wave's copy
-// instructions, for tiles whose 64 rows are consecutive keys all inside the sequence.
-template <int D, int NW>
-struct TileOffsets {
-  static constexpr int NI = (TileCfg<D>::KINSTR + TileCfg<D>::VINSTR + NW - 1) / NW;
-  uint32_t off[NI];
-  // maxrow < 63 describes a ragged last tile: rows past maxrow re-read row maxrow, so every
-  // copy stays inside the sequence.
-  __device__ __forceinline__ void init(const FwdArgs& a, int w, int l, int maxrow = BN - 1) {
-    using C = TileCfg<D>;
-#pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      const int i = w + NW * ii;
-      uint32_t r, c;
-      if (i < C::KINSTR) {
-        kslab_rc<D>(i, l, r, c);
-        r = min(r, (uint32_t)maxrow);
-        off[ii] = r * (uint32_t)a.k_sl + c * 8u;
-      } else {
-        slot_rc<C::VSPR, C::CPR>((uint32_t)(i - C::KINSTR) * 64u + (uint32_t)l, r, c);
-        r = min(r, (uint32_t)maxrow);
-        off[ii] = r * (uint32_t)a.v_sl + c * 8u;
-      }
-    }
-  }
-};
-
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile_fast(char* st, const uint16_t* ktile,
-                                                const uint16_t* vtile, const TileOffsets<D, NW>& o,
-                                                int w) {
-  using C = TileCfg<D>;
-  // the copy instruction index, the source tile and the LDS destination are wave-uniform
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-#pragma unroll
-  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
-    const int i = wu + NW * ii;
-    if (i < C::KINSTR + C::VINSTR) {
-      const bool is_k = i < C::KINSTR;
-      const uint16_t* src = is_k ? ktile : vtile;
-      const int dst = is_k ? i * 1024 : C::KT_BYTES + (i - C::KINSTR) * 1024;
-      dma16(src + o.off[ii], st + dst);
-    }
-  }
-}
 
 // Scalar-base tile copy. Wave w of NW issues the K copy instructions w, w+NW, ... and the V
 // copy instructions w, w+NW, ... (KINSTR and VINSTR are multiples of NW), so which tensor an
@@ -188,17 +151,22 @@ __device__ __forceinline__ void issue_tile_sbase(uint32_t stage, const uint16_t*
   }
 }
 
+// Gathered tile copy: wave w of NW issues copy instructions w, w+NW, ... (K first, then V)
+// with per-lane source addresses. Like the scalar-base copy, it is invisible to the compiler:
+// the caller orders later LDS reads with an explicit vmcnt wait and a workgroup barrier.
 template <int D, int NW, class KeyOf>
-__device__ __forceinline__ void issue_tile_slow(const FwdArgs& a, char* st, const uint16_t* kbase,
-                                                const uint16_t* vbase, KeyOf key_of, int w, int l) {
+__device__ __forceinline__ void issue_tile_gather(const FwdArgs& a, uint32_t st,
+                                                  const uint16_t* kbase, const uint16_t* vbase,
+                                                  KeyOf key_of, int w, int l) {
   using C = TileCfg<D>;
+  constexpr int NI = (C::KINSTR + C::VINSTR + NW - 1) / NW;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-  for (int ii = 0; ii < TileOffsets<D, NW>::NI; ++ii) {
-    const int i = w + NW * ii;
-    if (i < C::KINSTR + C::VINSTR) copy_instr_slow<D>(a, st, kbase, vbase, key_of, i, l);
+  for (int ii = 0; ii < NI; ++ii) {
+    const int i = wu + NW * ii;
+    if (i < C::KINSTR + C::VINSTR) copy_instr_gather<D>(a, st, kbase, vbase, key_of, i, l);
   }
 }
-
 
 }  // namespace
 }  // namespace attn
