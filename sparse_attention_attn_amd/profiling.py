@@ -183,7 +183,8 @@ def render_md(rec, stats, stats_cmd, fetch_cmd, write_cmd):
     lines += ["| kernel | calls | avg µs | min µs | max µs | % of GPU time |",
               "|---|---|---|---|---|---|"]
     for s in stats:
-        lines.append(f"| `{s['name']}` | {s['calls']} | {s['avg_ns'] / 1e3:.1f} | "
+        name = s["name"] if len(s["name"]) <= 160 else s["name"][:157] + "..."
+        lines.append(f"| `{name}` | {s['calls']} | {s['avg_ns'] / 1e3:.1f} | "
                      f"{s['min_ns'] / 1e3:.1f} | {s['max_ns'] / 1e3:.1f} | {s['pct']:.2f} |")
     lines.append("")
     if "hbm_bytes_per_launch" in rec:
