@@ -32,10 +32,22 @@
 // is a per-lane base plus a compile-time offset. The copy engine writes 1 KiB per instruction;
 // V padding slots receive a duplicate chunk that is never read.
 //
-// Softmax: scores live in the exp2 domain (t = s·scale·log2 e). Each row keeps a reference
-// maximum m, moved when a tile's maximum exceeds it by more than kRescaleSlack; weights are
-// exp2(t - m) <= 2^kRescaleSlack, and the same reference serves the accumulated output, the
-// row sum and the final LSE. The output rescale runs only when some row of the wave moved.
+// Softmax: scores live in the exp2 domain (x = s·scale·log2 e). Each row keeps a reference m
+// and its weights are exp2(x - m), computed with no maximum taken. After the weights of a
+// 32-key unit, one compare per lane accepts the unit when the row already has a reference and
+// the lane's running fp32 weight sum is at most 2^64 (so no weight or accumulator can come
+// near overflow; inf and NaN fail too); otherwise the wave takes a slow path for that unit:
+// the unit's row maxima move m, the accumulators and sums are rescaled and the unit's weights
+// recomputed, before the unit's P·V. Weights may then exceed 1 (the reference can lag the true
+// maximum), which fp32 and bf16 hold with the same relative precision; two sums are kept, the
+// sum of the bf16-rounded weights, which normalises O (numerator and denominator use the same
+// weights), and the fp32 sum, which gives the LSE.
+//
+// Schedule of one tile for one wave (keys in two 32-key units u0, u1): the MFMAs of Sᵀ(u0);
+// those of Sᵀ(u1), each followed by a slice of u0's softmax on the VALU; those of P·V(u0),
+// each followed by a slice of u1's softmax; those of P·V(u1). So a single wave keeps the
+// matrix core and the VALU busy together in the middle half of the tile, and the second wave
+// of the SIMD fills the rest. Operands are read from LDS two MFMA slots ahead of their use.
 
 #include <type_traits>
 
@@ -46,94 +58,239 @@
 namespace attn {
 namespace {
 
-// Log2 headroom before the reference maximum moves. Zero keeps the eager running maximum: the
-// largest weight of every row is then exactly 1.0, which bf16 represents exactly; a stale
-// reference would let that weight pick up a bf16 rounding error of up to 2^-9 relative.
-constexpr float kRescaleSlack = 0.0f;
-
 template <int D>
 struct WaveState {
   bf16x8 qop[TileCfg<D>::KSTEPS];
   f32x16 acc[TileCfg<D>::DVB];
-  float m;        // reference maximum in the exp2 domain (same in lanes l and l^32)
-  float lsum;     // lane-partial sum of exp2(t - m)
+  float m;        // reference in the exp2 domain, -inf before any key (same in lanes l, l^32)
+  float mu;       // m where finite, +inf otherwise (every weight is then 0)
+  float lb;       // lane-partial sum of the bf16-rounded weights
+  float lf;       // lane-partial sum of the fp32 weights
   uint32_t kofs;  // lane byte offset of its K-operand reads inside a tile
   uint32_t vofs;  // lane byte offset of its transposed V reads inside a tile
 };
 
-// Math of one tile for one wave. When `masked`, mask(s0, s1) sets the scores of invisible keys
-// to -inf (slot (block kb, j) of s_kb holds local key 32*kb + 8*(j/4) + 4*(l/32) + j%4);
-// otherwise every key is visible. MFMA groups run at raised wave priority so that, with two
-// waves per SIMD, the wave feeding the matrix core wins issue arbitration and the other wave's
-// softmax fills the gaps.
+// Accepts a unit: the row has a reference and the lane's fp32 sum is at most 2^64 (bit
+// compare: inf and NaN fail).
+__device__ __forceinline__ bool unit_ok(float m, float sf) {
+  return m != -INFINITY && __builtin_bit_cast(uint32_t, sf) <= kSumLimitBits;
+}
+
+// Slow path of a unit: moves the row's reference to the larger of m and the unit's row
+// maximum, rescales the accumulators and the sums of the earlier units by exp2(m_old - m_new),
+// and recomputes the unit's weights (Pᵀ operands p) and sums sb, sf.
+template <int D>
+__device__ __forceinline__ void slow_unit(WaveState<D>& ws, const f32x16& s, float sl2,
+                                          bf16x8 (&p)[2], float& sb, float& sf) {
+  float mx = max3f(s[0], s[1], s[2]);
+#pragma unroll
+  for (int j = 3; j + 1 < 16; j += 2) mx = max3f(mx, s[j], s[j + 1]);
+  mx = fmaxf(mx, s[15]);
+  const float mnew = fmaxf(ws.m, max_halves(mx) * sl2);
+  const float munew = (mnew == -INFINITY) ? INFINITY : mnew;
+  // m_old = -inf gives 0 (nothing accumulated yet); an unchanged finite m gives 1
+  const float alpha = fast_exp2(ws.m - munew);
+#pragma unroll
+  for (int b = 0; b < TileCfg<D>::DVB; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) ws.acc[b][j] *= alpha;
+  sb = ws.lb * alpha;
+  sf = ws.lf * alpha;
+  uint32_t pk[2][4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e0 = fast_exp2(fmaf(s[8 * ks + 2 * i], sl2, -munew));
+      const float e1 = fast_exp2(fmaf(s[8 * ks + 2 * i + 1], sl2, -munew));
+      sf += e0;
+      sf += e1;
+      pk[ks][i] = pack_bf16x2(e0, e1);
+      sb = add_bf16_pair(pk[ks][i], sb);
+    }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    p[ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]));
+  ws.m = mnew;
+  ws.mu = munew;
+}
+
+// Copy instruction i (K instructions first, then V) of one tile whose rows are gathered:
+// key_of(r) must return a valid key row, so every load is in bounds. `st` is the stage's LDS
+// address; k_row_bytes / v_row_bytes are the byte strides between key rows.
+template <int D, class KeyOf>
+__device__ __forceinline__ void copy_instr_gather(uint32_t st, const uint16_t* kbase,
+                                                  const uint16_t* vbase, uint32_t k_row_bytes,
+                                                  uint32_t v_row_bytes, KeyOf key_of, int i, int l) {
+  using C = TileCfg<D>;
+  uint32_t r, c;
+  if (i < C::KINSTR) {
+    kslab_rc<D>(i, l, r, c);
+    dma16_vaddr((const char*)kbase + (int64_t)key_of((int)r) * k_row_bytes + c * 16u,
+                st + (uint32_t)i * 1024u);
+  } else {
+    const int iv = i - C::KINSTR;
+    slot_rc<C::VSPR, C::CPR>((uint32_t)iv * 64u + (uint32_t)l, r, c);
+    dma16_vaddr((const char*)vbase + (int64_t)key_of((int)r) * v_row_bytes + c * 16u,
+                st + C::KT_BYTES + (uint32_t)iv * 1024u);
+  }
+}
+
+// Scalar-base tile copy of 64 consecutive key rows with the lane offsets computed at issue:
+// K instruction i reads row 32·(i/KSTEPS) + l%32 at chunk 2·(i%KSTEPS) + l/32, i.e. the lane
+// term (l%32)·row + (l/32)·16 plus a wave-uniform term; V instructions follow the padded slot
+// map. Wave wu issues instructions wu, wu+NW, ... With LEAN, the lane id goes through an
+// opaque copy, so the V offsets are recomputed at every issue instead of being hoisted out of
+// the caller's loop into registers held for the whole kernel (for kernels short of registers).
+template <int D, int NW, bool LEAN>
+__device__ __forceinline__ void issue_tile_sbase_lean(uint32_t stage, const uint16_t* ktile,
+                                                      const uint16_t* vtile, uint32_t k_row_bytes,
+                                                      uint32_t v_row_bytes, int wu, int l) {
+  using C = TileCfg<D>;
+  if constexpr (LEAN) asm volatile("" : "+v"(l));
+  const uint32_t kl = (uint32_t)(l & 31) * k_row_bytes + (uint32_t)(l >> 5) * 16u;
+#pragma unroll
+  for (int k = 0; k < (C::KINSTR + NW - 1) / NW; ++k) {
+    const int i = wu + NW * k;
+    if ((C::KINSTR % NW) == 0 || i < C::KINSTR) {
+      const uint32_t u = (uint32_t)(32 * (i / C::KSTEPS)) * k_row_bytes +
+                         (uint32_t)(i % C::KSTEPS) * 32u;
+      dma16_sbase(ktile, kl + u, stage + (uint32_t)i * 1024u);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < (C::VINSTR + NW - 1) / NW; ++v) {
+    const int i = wu + NW * v;
+    if ((C::VINSTR % NW) == 0 || i < C::VINSTR) {
+      uint32_t r, c;
+      slot_rc<C::VSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+      dma16_sbase(vtile, r * v_row_bytes + c * 16u, stage + C::KT_BYTES + (uint32_t)i * 1024u);
+    }
+  }
+}
+
+// Gathered tile copy: wave w of NW issues copy instructions w, w+NW, ... (K first, then V)
+// with per-lane source addresses. Like the scalar-base copy, it is invisible to the compiler:
+// the caller orders later LDS reads with an explicit vmcnt wait and a workgroup barrier.
+template <int D, int NW, class KeyOf>
+__device__ __forceinline__ void issue_tile_gather(uint32_t st, const uint16_t* kbase,
+                                                  const uint16_t* vbase, uint32_t k_row_bytes,
+                                                  uint32_t v_row_bytes, KeyOf key_of, int w, int l) {
+  using C = TileCfg<D>;
+  constexpr int NI = (C::KINSTR + C::VINSTR + NW - 1) / NW;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int i = wu + NW * ii;
+    if (i < C::KINSTR + C::VINSTR)
+      copy_instr_gather<D>(st, kbase, vbase, k_row_bytes, v_row_bytes, key_of, i, l);
+  }
+}
+
+// Math of one tile for one wave. When `masked`, mask(U, s) sets the scores of invisible keys of
+// unit U (0 or 1, a compile-time constant) to -inf; slot j of s holds local key
+// 32*U + 8*(j/4) + 4*(l/32) + j%4. Otherwise every key is visible.
 template <int D, class Mask>
 __device__ __forceinline__ void tile_math_mask(const FwdArgs& a, WaveState<D>& ws, const char* st,
                                                bool masked, Mask mask, int l) {
   using C = TileCfg<D>;
-  const char* kt = st + ws.kofs;
-  const char* vt = st + C::KT_BYTES + ws.vofs;
+  constexpr int NQ = C::KSTEPS;  // MFMAs of a unit's Sᵀ
+  constexpr int NV = 2 * C::DVB;  // MFMAs of a unit's P·V
+  static_assert(NQ == NV, "the two softmax phases have the same number of slots");
+  constexpr int NITEMS = 9;       // softmax items of a unit: 8 weight groups + the last fold
+  const uint32_t kt = lds_addr(st) + ws.kofs;
+  const uint32_t vt = lds_addr(st) + C::KT_BYTES + ws.vofs;
+  const float sl2 = a.sl2;
 
-  // ---- Sᵀ = K·Qᵀ for 64 keys x 32 queries (two 32x32 blocks), one K slab per operand
-  f32x16 s0 = {}, s1 = {};
-  __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int s = 0; s < C::KSTEPS; ++s) {
-    const bf16x8 k0 = lds_read_bf16x8(kt, 1024u * s);
-    const bf16x8 k1 = lds_read_bf16x8(kt, 1024u * (C::KSTEPS + s));
-    s0 = mfma32(k0, ws.qop[s], s0);
-    s1 = mfma32(k1, ws.qop[s], s1);
-  }
-  __builtin_amdgcn_s_setprio(0);
+  // MFMA slot n of the tile: [0, NQ) Sᵀ(u0), [NQ, 2NQ) Sᵀ(u1), then P·V(u0), P·V(u1). P·V slot
+  // v covers output block v % DVB and unit k-step v / DVB (keys 16·ks .. 16·ks+15 of the unit),
+  // so consecutive MFMAs accumulate into different blocks.
+  auto operand = [&](int n) -> bf16x8 {
+    if (n < 2 * NQ) return lds_read_b128_at(kt + 1024u * (uint32_t)n);
+    const int u = (n - 2 * NQ) / NV, v = (n - 2 * NQ) % NV;
+    const uint32_t o = vt + (32u * u + 16u * (v / C::DVB)) * C::VROW + 64u * (v % C::DVB);
+    return lds_read_tr_pair_at(o, o + 8u * C::VROW);
+  };
+  bf16x8 opr[2];
+  opr[0] = operand(0);
 
-  if (masked) mask(s0, s1);
-
-  // ---- online softmax (exp2 domain, lazily moved reference maximum)
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
-  mx = fmaxf(mx, xor_shuffle(mx, 32));
-  const float tmax = mx * a.sl2;
-  const bool move = tmax > ws.m + kRescaleSlack;  // false while the tile is fully masked
-  if (__any(move)) {
-    const float mnew = move ? tmax : ws.m;
-    const float alpha = move ? fast_exp2(ws.m - mnew) : 1.0f;  // exp2(-inf) = 0 on first use
-    ws.m = mnew;
-    ws.lsum *= alpha;
-#pragma unroll
-    for (int b = 0; b < C::DVB; ++b)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ws.acc[b][j] *= alpha;
-  }
-  const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    s0[j] = fast_exp2(fmaf(s0[j], a.sl2, -muse));
-    s1[j] = fast_exp2(fmaf(s1[j], a.sl2, -muse));
-    psum += s0[j] + s1[j];
-  }
-  ws.lsum += psum;
-
-  // ---- Pᵀ operands: k-step ks covers local keys 16*ks .. 16*ks+15
-  bf16x8 pop[4];
-  pop[0] = pack_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
-  pop[1] = pack_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
-  pop[2] = pack_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
-  pop[3] = pack_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
-
-  // ---- Oᵀ += Vᵀ·Pᵀ. Operand slot i of lane l covers key 16*ks + 8*(i/4) + 4*(l/32) + i%4,
-  // fetched with two transposed reads: lane 4j+c of each 16-lane group addresses
-  // row 16*ks + 4*(l/32) + j (+8 for the second read) at column 32*b + 16*((l/16)%2) + 4c.
-  __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int b = 0; b < C::DVB; ++b) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t o = 16u * ks * C::VROW + 64u * b;
-      const bf16x8 vop = lds_read_tr_pair(vt, o, o + 8u * C::VROW);
-      ws.acc[b] = mfma32(vop, pop[ks], ws.acc[b]);
+  f32x16 s0, s1;
+  bf16x8 p0[2], p1[2];
+  float sb = ws.lb, sf = ws.lf;
+  uint32_t pk[2][4];
+  float ew[2][2];
+  // Softmax item it of unit scores s: weights of group it (scores 2·it, 2·it+1) and the fold
+  // of group it-1 into the sums and the packed operand (skewed, so no fold waits on the exp2
+  // just issued).
+  auto item = [&](auto IT, const f32x16& s) {
+    constexpr int it = decltype(IT)::value;
+    if constexpr (it < 8) {
+      ew[it & 1][0] = fast_exp2(fmaf(s[2 * it], sl2, -ws.mu));
+      ew[it & 1][1] = fast_exp2(fmaf(s[2 * it + 1], sl2, -ws.mu));
     }
-  }
+    if constexpr (it >= 1) {
+      constexpr int g = it - 1;
+      sf += ew[g & 1][0];
+      sf += ew[g & 1][1];
+      pk[g >> 2][g & 3] = pack_bf16x2(ew[g & 1][0], ew[g & 1][1]);
+      sb = add_bf16_pair(pk[g >> 2][g & 3], sb);
+    }
+  };
+  auto packed = [&](bf16x8 (&p)[2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      p[ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]));
+  };
+  // One MFMA slot: the product, then the read two slots ahead.
+  auto slot = [&](auto NI) {
+    constexpr int n = decltype(NI)::value;
+    const bf16x8 op = opr[n % 2];
+    if constexpr (n < NQ) {
+      s0 = mfma32(op, ws.qop[n], n == 0 ? f32x16{} : s0);
+    } else if constexpr (n < 2 * NQ) {
+      s1 = mfma32(op, ws.qop[n - NQ], n == NQ ? f32x16{} : s1);
+    } else if constexpr (n < 2 * NQ + NV) {
+      constexpr int v = n - 2 * NQ;
+      ws.acc[v % C::DVB] = mfma32(op, p0[v / C::DVB], ws.acc[v % C::DVB]);
+    } else {
+      constexpr int v = n - 2 * NQ - NV;
+      ws.acc[v % C::DVB] = mfma32(op, p1[v / C::DVB], ws.acc[v % C::DVB]);
+    }
+    if constexpr (n + 1 < 2 * NQ + 2 * NV) opr[(n + 1) % 2] = operand(n + 1);
+  };
+
+  // Sᵀ(u0)
+  __builtin_amdgcn_s_setprio(1);
+  static_for<0, NQ>([&](auto NI) { slot(NI); });
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+  // Sᵀ(u1) with the softmax of u0
+  if (masked) mask(icn<0>{}, s0);
+  static_for<0, NQ>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    slot(icn<NQ + i>{});
+    static_for<NITEMS * i / NQ, NITEMS * (i + 1) / NQ>([&](auto IT) { item(IT, s0); });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  packed(p0);
+  if (__builtin_expect(__any(!unit_ok(ws.m, sf)), 0)) slow_unit<D>(ws, s0, sl2, p0, sb, sf);
+  ws.lb = sb;
+  ws.lf = sf;
+  // P·V(u0) with the softmax of u1
+  if (masked) mask(icn<1>{}, s1);
+  static_for<0, NV>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    slot(icn<2 * NQ + i>{});
+    static_for<NITEMS * i / NV, NITEMS * (i + 1) / NV>([&](auto IT) { item(IT, s1); });
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  packed(p1);
+  if (__builtin_expect(__any(!unit_ok(ws.m, sf)), 0)) slow_unit<D>(ws, s1, sl2, p1, sb, sf);
+  ws.lb = sb;
+  ws.lf = sf;
+  // P·V(u1)
+  __builtin_amdgcn_s_setprio(1);
+  static_for<0, NV>([&](auto I) { slot(icn<2 * NQ + NV + decltype(I)::value>{}); });
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -143,15 +300,13 @@ template <int D, class KeyIdx>
 __device__ __forceinline__ void tile_math(const FwdArgs& a, WaveState<D>& ws, const char* st,
                                           int row, bool masked, KeyIdx kidx, int l) {
   const int h = l >> 5;
-  tile_math_mask<D>(a, ws, st, masked, [&](f32x16& s0, f32x16& s1) {
-    const int lim = a.causal ? row + a.off : 0x7fffffff;
+  const int lim = a.causal ? row + a.off : 0x7fffffff;
+  tile_math_mask<D>(a, ws, st, masked, [&](auto U, f32x16& s) {
+    constexpr int u = decltype(U)::value;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int kl = 8 * (j >> 2) + 4 * h + (j & 3);
-      const int k0i = kidx(kl);
-      const int k1i = kidx(kl + 32);
-      if (k0i < 0 || k0i > lim) s0[j] = -INFINITY;
-      if (k1i < 0 || k1i > lim) s1[j] = -INFINITY;
+      const int k = kidx(32 * u + 8 * (j >> 2) + 4 * h + (j & 3));
+      if (k < 0 || k > lim) s[j] = -INFINITY;
     }
   }, l);
 }
@@ -172,7 +327,9 @@ __device__ __forceinline__ void load_q(const FwdArgs& a, WaveState<D>& ws, int b
 #pragma unroll
   for (int bb = 0; bb < C::DVB; ++bb) ws.acc[bb] = f32x16{};
   ws.m = -INFINITY;
-  ws.lsum = 0.f;
+  ws.mu = INFINITY;
+  ws.lb = 0.f;
+  ws.lf = 0.f;
   // K operand: lane l's 16 bytes of every slab
   ws.kofs = (uint32_t)l * 16u;
   // V operand: group G = l/16, row 4*(G/2) + (l%16)/4, column 16*(G%2) + 4*(l%4)
@@ -181,15 +338,18 @@ __device__ __forceinline__ void load_q(const FwdArgs& a, WaveState<D>& ws, int b
             (uint32_t)(16 * (G & 1) + 4 * (l & 3)) * 2u;
 }
 
+// Writes the wave's rows of O (obase: row 0 of this (b, head); o_sl: row stride) and, when
+// lse_row is given (the LSE entries of this (b, head)), their LSE.
 template <int D>
-__device__ __forceinline__ void store_out(const FwdArgs& a, const WaveState<D>& ws, int b, int hq,
-                                          int row, int l) {
+__device__ __forceinline__ void store_out(const WaveState<D>& ws, uint16_t* obase, int64_t o_sl,
+                                          float* lse_row, int row, int Lq, int l) {
   using C = TileCfg<D>;
   const int h = l >> 5;
-  const float tot = ws.lsum + xor_shuffle(ws.lsum, 32);
-  if (row >= a.Lq) return;
-  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-  uint16_t* orow = a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_sl + (int64_t)hq * a.o_sh;
+  const float tb = ws.lb + other_half(ws.lb);
+  const float tf = ws.lf + other_half(ws.lf);
+  if (row >= Lq) return;
+  const float inv = tb > 0.f ? 1.0f / tb : 0.f;
+  uint16_t* orow = obase + (int64_t)row * o_sl;
 #pragma unroll
   for (int bb = 0; bb < C::DVB; ++bb) {
 #pragma unroll
@@ -201,10 +361,7 @@ __device__ __forceinline__ void store_out(const FwdArgs& a, const WaveState<D>& 
       *reinterpret_cast<uint2*>(orow + dv) = pk;
     }
   }
-  if (a.lse != nullptr && h == 0) {
-    a.lse[((int64_t)b * a.Hq + hq) * a.Lq + row] =
-        tot > 0.f ? ws.m * kLn2 + logf(tot) : -INFINITY;
-  }
+  if (lse_row != nullptr && h == 0) lse_row[row] = tf > 0.f ? ws.m * kLn2 + logf(tf) : -INFINITY;
 }
 
 // Maps blockIdx.x to a logical work id. The hardware deals workgroups round-robin over the 8
@@ -274,13 +431,15 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   const int l = tid & 63;
   const int nqb = a.n_qtiles;
   const int ngrp = (nqb + QB - 1) / QB;
+  // the work ids are workgroup-uniform: pinned to scalar registers, so are the addresses
+  // derived from them
   int lid = logical_block(a.xcd_remap);
-  const int hg = lid % a.g;
-  lid /= a.g;
-  const int pr = ngrp - 1 - (lid % ngrp);
-  lid /= ngrp;
-  const int hkv = lid % a.Hkv;
-  const int b = lid / a.Hkv;
+  const int hg = __builtin_amdgcn_readfirstlane(lid % a.g);
+  lid = __builtin_amdgcn_readfirstlane(lid / a.g);
+  const int pr = __builtin_amdgcn_readfirstlane(ngrp - 1 - (lid % ngrp));
+  lid = __builtin_amdgcn_readfirstlane(lid / ngrp);
+  const int hkv = __builtin_amdgcn_readfirstlane(lid % a.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(lid / a.Hkv);
   const int hq = hkv * a.g + hg;
 
   const int qbA = QB * pr;
@@ -296,6 +455,19 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
 
   const int bh = b * a.Hq + hq;
   const int nwords = (a.nkb + 31) >> 5;
+  // Uniform values the later phases and the epilogue need, derived here so that the kernel
+  // arguments they come from die after setup instead of holding scalar registers throughout.
+  uint16_t* const obase = a.o + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh;
+  const int64_t o_sl = a.o_sl;
+  float* const lse_row = a.lse != nullptr ? a.lse + (int64_t)bh * a.Lq : nullptr;
+  const int Lq = a.Lq;
+  const int cstart = a.col_ptr[bh];
+  const int ncols = a.col_ptr[bh + 1] - cstart;
+  const int* const cidx = a.col_idx + cstart;
+  const uint32_t* const sbits = SLASH ? a.sl_bits + (int64_t)bh * a.bits_words : nullptr;
+  const uint32_t* const cbits = SLASH ? a.cl_bits + (int64_t)bh * a.bits_words : nullptr;
+  const int bits_last = a.bits_words - 1;
+  const uint32_t k_row_bytes = (uint32_t)a.k_sl * 2u, v_row_bytes = (uint32_t)a.v_sl * 2u;
   auto listed = [&](int q, int kb) -> bool { return (bm[q][kb >> 5] >> (kb & 31)) & 1u; };
   // blocks listed by at least one / by every block of the group, word kb/32
   auto any_word = [&](int wd) -> uint32_t {
@@ -371,8 +543,6 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
 
   WaveState<D> ws;
   load_q<D>(a, ws, b, hq, row, l);
-  TileByteOffsets<D, NW> boff;
-  boff.init(a, w, l);
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint16_t* kbp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
@@ -384,11 +554,13 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   // copy of the 64-key block starting at key `base` (inside the sequence) into stage S
   auto issue_block = [&](auto S, int base) {
     if (base + BN <= a.Lk) {
-      issue_tile_sbase<D, NW>(stage_addr(S), kbp + (int64_t)base * a.k_sl,
-                              vbp + (int64_t)base * a.v_sl, boff, wu);
+      issue_tile_sbase_lean<D, NW, SLASH>(
+          stage_addr(S), (const uint16_t*)((const char*)kbp + (int64_t)base * k_row_bytes),
+          (const uint16_t*)((const char*)vbp + (int64_t)base * v_row_bytes), k_row_bytes,
+          v_row_bytes, wu, l);
     } else {
-      issue_tile_gather<D, NW>(a, stage_addr(S), kbp, vbp, [&](int r) { return min(base + r, lkm1); },
-                               w, l);
+      issue_tile_gather<D, NW>(stage_addr(S), kbp, vbp, k_row_bytes, v_row_bytes,
+                               [&](int r) { return min(base + r, lkm1); }, w, l);
     }
   };
   // The two-stage ring over tiles 0..ntl-1 (tile t in stage t % 2). Step t waits for tile t
@@ -428,26 +600,31 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
           if (!active || !listed(myq, kb)) return;
           if (a.causal && base > qwlast + a.off) return;
           const bool masked = base + BN > a.Lk || (a.causal && base + BN - 1 > qw0 + a.off);
-          tile_math<D>(a, ws, stage(S), row, masked,
-                       [&](int kl) { const int kk = base + kl; return kk < a.Lk ? kk : -1; }, l);
+          // a key is visible up to min(causal limit of the row, Lk - 1); in local terms, slot
+          // j of unit U holds key base + 4h + 32U + 8(j/4) + j%4
+          const int hi = min(a.causal ? row + a.off : 0x7fffffff, a.Lk - 1) - base - 4 * (l >> 5);
+          tile_math_mask<D>(a, ws, stage(S), masked, [&](auto U, f32x16& sc) {
+            constexpr int u = decltype(U)::value;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (32 * u + 8 * (j >> 2) + (j & 3) > hi) sc[j] = -INFINITY;
+          }, l);
         });
   }
 
   // ---- phase 2: vertical columns. An entry is the column id with bit kFlagShift + q set
   // when the column lies inside a block that block q of the group lists.
-  const int cstart = a.col_ptr[bh];
-  const int cend = a.col_ptr[bh + 1];
-  for (int seg = cstart; seg < cend; seg += kSeg) {
-    if (a.col_idx[seg] > klim) break;  // sorted: nothing further is visible
-    const int n = min(kSeg, cend - seg);
+  for (int seg = 0; seg < ncols; seg += kSeg) {
+    if (cidx[seg] > klim) break;  // sorted: nothing further is visible
+    const int n = min(kSeg, ncols - seg);
     const int cnt = compact(n,
                             [&](int i) {
-                              const int col = a.col_idx[seg + i];
+                              const int col = cidx[seg + i];
                               if (col < 0 || col > klim) return false;
                               return ((all_word(col >> 11) >> ((col >> 6) & 31)) & 1u) == 0u;
                             },
                             [&](int i) {
-                              const int col = a.col_idx[seg + i];
+                              const int col = cidx[seg + i];
                               int e = col;
 #pragma unroll
                               for (int q = 0; q < QB; ++q)
@@ -459,7 +636,7 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
         [&](auto S, int t) {
           const int cb = t * BN;
           issue_tile_gather<D, NW>(
-              a, stage_addr(S), kbp, vbp,
+              stage_addr(S), kbp, vbp, k_row_bytes, v_row_bytes,
               [&](int r) { return kept[cb + r < cnt ? cb + r : cb] & kColMask; }, w, l);
         },
         [&](auto S, int t) {
@@ -479,8 +656,6 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   // ---- phase 3: slash lines, over the crossed blocks the wave's own block does not list
   if constexpr (SLASH) {
     const int h = l >> 5;
-    const uint32_t* sbits = a.sl_bits + (int64_t)bh * a.bits_words;
-    const uint32_t* cbits = a.cl_bits + (int64_t)bh * a.bits_words;
     // Lane's window: bitmap bit (o + 128) of its local key c's offset is at rw - base + 59 - c.
     const int rw = row + a.off + 69 - 4 * h;
     const int rw0 = q0 + a.off + 65;  // smallest rw of the group (row q0, h = 1)
@@ -502,9 +677,12 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
             // (the pair's rows need at most 8 of them) and the two column words of the tile;
             // the ring's wait covers this copy with the tile's.
             if (wu == 0) {
+              int lo = l;
+              asm volatile("" : "+v"(lo));  // keep the addresses below from being hoisted
               const int j0 = win0(base);
-              const uint32_t* src = l < kMaskOffWords ? sbits + min(j0 + l, a.bits_words - 1)
-                                                      : cbits + (base >> 5) + (l == kMaskOffWords + 1);
+              const uint32_t* src = lo < kMaskOffWords
+                                        ? sbits + min(j0 + lo, bits_last)
+                                        : cbits + (base >> 5) + (lo == kMaskOffWords + 1);
               dma4_vaddr(src, lds_addr(&mwl[s][0]));
             }
             issue_block(S, base);
@@ -519,27 +697,26 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
             const int j = (max(rw - base, 0) >> 5) - win0(base);
             const uint32_t m0 = mwl[s][j], m1 = mwl[s][j + 1], m2 = mwl[s][j + 2];
             const uint32_t m3 = mwl[s][kMaskOffWords], m4 = mwl[s][kMaskOffWords + 1];
-            tile_math_mask<D>(a, ws, stage(S), true, [&](f32x16& s0, f32x16& s1) {
-              // offsets: bit x of (d1:d0) is local key c = 59 - x; reversed and shifted, bit c
-              const uint32_t d0 = __builtin_amdgcn_alignbit(m1, m0, sh);
-              const uint32_t d1 = __builtin_amdgcn_alignbit(m2, m1, sh);
-              const uint32_t r0 = __builtin_bitreverse32(d1), r1 = __builtin_bitreverse32(d0);
-              // listed columns: bit c is key base + 4h + c
-              const uint32_t c0w = __builtin_amdgcn_alignbit(m4, m3, 4 * h);
-              const uint32_t c1w = m4 >> (4 * h);
-              const uint32_t vlo = ((r0 >> 4) | (r1 << 28)) & ~c0w;
-              const uint32_t vhi = (r1 >> 4) & ~c1w;
+            // offsets: bit x of (d1:d0) is local key c = 59 - x; reversed and shifted, bit c
+            const uint32_t d0 = __builtin_amdgcn_alignbit(m1, m0, sh);
+            const uint32_t d1 = __builtin_amdgcn_alignbit(m2, m1, sh);
+            const uint32_t r0 = __builtin_bitreverse32(d1), r1 = __builtin_bitreverse32(d0);
+            // listed columns: bit c is key base + 4h + c
+            const uint32_t c0w = __builtin_amdgcn_alignbit(m4, m3, 4 * h);
+            const uint32_t c1w = m4 >> (4 * h);
+            // visible keys of unit u: bit 8*(j/4) + j%4 of vis[u] for slot j
+            const uint32_t vis0 = ((r0 >> 4) | (r1 << 28)) & ~c0w;
+            const uint32_t vis1 = (r1 >> 4) & ~c1w;
+            tile_math_mask<D>(a, ws, stage(S), true, [&](auto U, f32x16& sc) {
+              const uint32_t vis = decltype(U)::value == 0 ? vis0 : vis1;
 #pragma unroll
-              for (int jj = 0; jj < 16; ++jj) {
-                const int c = 8 * (jj >> 2) + (jj & 3);
-                if (!((vlo >> c) & 1u)) s0[jj] = -INFINITY;
-                if (!((vhi >> c) & 1u)) s1[jj] = -INFINITY;
-              }
+              for (int jj = 0; jj < 16; ++jj)
+                if (!((vis >> (8 * (jj >> 2) + (jj & 3))) & 1u)) sc[jj] = -INFINITY;
             }, l);
           });
     }
   }
-  store_out<D>(a, ws, b, hq, row, l);
+  store_out<D>(ws, obase, o_sl, lse_row, row, Lq, l);
 }
 
 // Per (b, h): bitmap of the listed slash offsets (bit o + 128, so a lane's window never starts

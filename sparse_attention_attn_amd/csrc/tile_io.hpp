@@ -59,26 +59,6 @@ __device__ __forceinline__ void slot_rc(uint32_t slot, uint32_t& r, uint32_t& c)
   c = cs < (uint32_t)CPR ? cs : 0u;
 }
 
-// Copy instruction i (K instructions first, then V) of one tile whose rows are gathered:
-// key_of(r) must return a valid key row, so every load is in bounds. `st` is the stage's LDS
-// address.
-template <int D, class KeyOf>
-__device__ __forceinline__ void copy_instr_gather(const FwdArgs& a, uint32_t st,
-                                                  const uint16_t* kbase, const uint16_t* vbase,
-                                                  KeyOf key_of, int i, int l) {
-  using C = TileCfg<D>;
-  uint32_t r, c;
-  if (i < C::KINSTR) {
-    kslab_rc<D>(i, l, r, c);
-    dma16_vaddr(kbase + (int64_t)key_of((int)r) * a.k_sl + c * 8, st + (uint32_t)i * 1024u);
-  } else {
-    const int iv = i - C::KINSTR;
-    slot_rc<C::VSPR, C::CPR>((uint32_t)iv * 64u + (uint32_t)l, r, c);
-    dma16_vaddr(vbase + (int64_t)key_of((int)r) * a.v_sl + c * 8,
-                st + C::KT_BYTES + (uint32_t)iv * 1024u);
-  }
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_n() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -148,23 +128,6 @@ __device__ __forceinline__ void issue_tile_sbase(uint32_t stage, const uint16_t*
     const int i = wu + NW * v;
     if ((C::VINSTR % NW) == 0 || i < C::VINSTR)
       dma16_sbase(vtile, o.vo[v], stage + C::KT_BYTES + (uint32_t)i * 1024u);
-  }
-}
-
-// Gathered tile copy: wave w of NW issues copy instructions w, w+NW, ... (K first, then V)
-// with per-lane source addresses. Like the scalar-base copy, it is invisible to the compiler:
-// the caller orders later LDS reads with an explicit vmcnt wait and a workgroup barrier.
-template <int D, int NW, class KeyOf>
-__device__ __forceinline__ void issue_tile_gather(const FwdArgs& a, uint32_t st,
-                                                  const uint16_t* kbase, const uint16_t* vbase,
-                                                  KeyOf key_of, int w, int l) {
-  using C = TileCfg<D>;
-  constexpr int NI = (C::KINSTR + C::VINSTR + NW - 1) / NW;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-#pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    const int i = wu + NW * ii;
-    if (i < C::KINSTR + C::VINSTR) copy_instr_gather<D>(a, st, kbase, vbase, key_of, i, l);
   }
 }
 
