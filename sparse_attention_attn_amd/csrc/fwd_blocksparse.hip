@@ -707,6 +707,8 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
             // visible keys of unit u: bit 8*(j/4) + j%4 of vis[u] for slot j
             const uint32_t vis0 = ((r0 >> 4) | (r1 << 28)) & ~c0w;
             const uint32_t vis1 = (r1 >> 4) & ~c1w;
+            // a line crossing the tile within the pair's rows may miss this wave's rows
+            if (!__any((vis0 | vis1) != 0u)) return;
             tile_math_mask<D>(a, ws, stage(S), true, [&](auto U, f32x16& sc) {
               const uint32_t vis = decltype(U)::value == 0 ? vis0 : vis1;
 #pragma unroll
