@@ -29,6 +29,9 @@
  * LSE. Optional fp32 log-sum-exp of each query row, natural log of Σ_j exp(scale·q·k_j) over
  *   the visible keys, DEVICE pointer, contiguous [B, Hq, Lq]. Pass NULL to skip it. A row with
  *   no visible key gets O = 0 and LSE = -inf.
+ * Scale. Any finite float. A negative scale reverses the order of the scores (the kernels
+ *   negate Q as they load it and use |scale|); scale 0 weighs every visible key equally, so O is
+ *   the mean of the visible value rows and LSE = ln(number of visible keys).
  * GQA. Hq must be a multiple of Hkv; query head h reads KV head h / (Hq / Hkv).
  * MLA. Pass v with the same data pointer and strides as k and Dv = 512 < Dqk = 576: V is then
  *   the first 512 columns of the latent K, read from the same memory (no copy).

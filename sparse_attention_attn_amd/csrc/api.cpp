@@ -2,6 +2,7 @@
 // Nothing here allocates device memory or synchronises; see include/attn.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <exception>
 #include <sstream>
@@ -14,6 +15,17 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// The attention kernels work with a positive exp2-domain scale. A negative scale is folded
+// into the sign of Q (the kernels negate Q as they load it), so masked scores stay -inf and
+// row maxima stay maxima. A zero scale (or one whose |scale|·log2 e is not a normal float)
+// becomes the smallest normal float: every visible key then gets weight exp2(~0) = 1 exactly,
+// as with scale 0, and masking still works (-inf times a positive number).
+void exp2_scale(float scale, float& sl2, uint32_t& qsign) {
+  qsign = scale < 0.f ? 0x80008000u : 0u;
+  const float s = std::fabs(scale) * kLog2e;
+  sl2 = std::isnormal(s) ? s : FLT_MIN;
+}
 
 int launch_status(const char* fn, hipError_t e) {
   if (e == hipSuccess) return ATTN_OK;
@@ -35,7 +47,7 @@ void fill_fwd(attn::FwdArgs& a, const attn_tensor_t& q, const attn_tensor_t& k,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
   a.causal = causal ? 1 : 0;
   a.off = Lk - Lq;
-  a.sl2 = scale * kLog2e;
+  exp2_scale(scale, a.sl2, a.qsign);
   a.xcd_remap = 0;
   a.blk_ptr = a.blk_idx = a.col_ptr = a.col_idx = nullptr;
   a.nkb = (Lk + 63) / 64;
@@ -102,7 +114,7 @@ int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
     a.causal = causal ? 1 : 0;
     a.off = Lk - Lq;
-    a.sl2 = scale * kLog2e;
+    exp2_scale(scale, a.sl2, a.qsign);
     a.num_splits = num_splits;
     a.chunk = attn::split_chunk(Lk, num_splits);
     const int cols = attn::split_cols(Dqk, a.g * Lq);
@@ -144,7 +156,7 @@ int attn_fwd_decode(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tens
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
     a.causal = causal ? 1 : 0;
     a.off = Lk - Lq;
-    a.sl2 = scale * kLog2e;
+    exp2_scale(scale, a.sl2, a.qsign);
     a.num_splits = ws.num_splits;
     a.chunk = attn::split_chunk(Lk, ws.num_splits);
     const int cols = attn::split_cols(Dqk, a.g * Lq);

@@ -52,6 +52,16 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
   uint4 u = *reinterpret_cast<const uint4*>(p);
   return __builtin_bit_cast(bf16x8, u);
 }
+// Query operand load with a sign mask XORed into every bf16 (0x80008000 negates the eight
+// values, 0 leaves them).
+__device__ __forceinline__ bf16x8 load_q_bf16x8(const bf16_t* p, uint32_t sign) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  u.x ^= sign;
+  u.y ^= sign;
+  u.z ^= sign;
+  u.w ^= sign;
+  return __builtin_bit_cast(bf16x8, u);
+}
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
 }

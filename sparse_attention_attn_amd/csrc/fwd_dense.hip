@@ -270,7 +270,7 @@ __device__ __forceinline__ void load_q_rows(const FwdArgs& a, WaveRows<D, NR>& w
       const uint16_t* qr =
           a.q + (int64_t)b * a.q_sb + (int64_t)row * a.q_sl + (int64_t)hq * a.q_sh;
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) ws.qop[r][s] = load_bf16x8(qr + 16 * s + 8 * h);
+      for (int s = 0; s < C::KSTEPS; ++s) ws.qop[r][s] = load_q_bf16x8(qr + 16 * s + 8 * h, a.qsign);
     } else {
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) ws.qop[r][s] = zero_bf16x8();

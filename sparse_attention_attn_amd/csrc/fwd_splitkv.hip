@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
       const int s = qs0 + i;
-      qop[c][i] = (col_ok[c] && s < qs1) ? load_bf16x8(qr + 32 * s + 8 * (l >> 4)) : zero_bf16x8();
+      qop[c][i] = (col_ok[c] && s < qs1) ? load_q_bf16x8(qr + 32 * s + 8 * (l >> 4), a.qsign) : zero_bf16x8();
     }
   }
   // Use the loaded operands here, before the copy ring starts: the compiler then waits for

@@ -20,7 +20,8 @@ struct FwdArgs {
   int B, Hq, Hkv, Lq, Lk, g;
   int causal;
   int off;        // Lk - Lq (bottom-right causal alignment)
-  float sl2;      // scale * log2(e)
+  float sl2;      // |scale| * log2(e), > 0 (see exp2_scale)
+  uint32_t qsign; // 0x80008000 when scale < 0: the kernels negate Q as they load it
   int n_qtiles;   // query tiles per (b, hq)
   int xcd_remap;  // grid size divisible by 8: group consecutive logical tiles per XCD
   // block-sparse lists (device pointers), unused by the dense kernel
@@ -57,7 +58,8 @@ struct SplitArgs {
   int B, Hq, Hkv, Lq, Lk, g;
   int causal;
   int off;
-  float sl2;
+  float sl2;        // |scale| * log2(e), > 0 (see exp2_scale)
+  uint32_t qsign;   // 0x80008000 when scale < 0: Q is negated as it is loaded
   int num_splits;
   int chunk;        // keys per split (multiple of 64)
   int ncolblk;      // ceil(g * Lq / split_cols(Dqk, g * Lq))
