@@ -181,3 +181,51 @@ def test_blocksparse_deterministic():
     o1, l1 = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
     o2, l2 = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
     assert bool((o1 == o2).all()) and bool((l1 == l2).all())
+
+
+def _jump_qkv(B, H, Hkv, L, D, seed):
+    """Scores that rise by about 29 (exp2 domain) per 32 keys in KV head 0, fall in KV head 1
+    and alternate in the others: weights against a reference set on earlier keys overflow fp32
+    within a few units, so the kernel has to move its reference mid-row (its slow path)."""
+    import torch
+    u = torch.full((D,), 1.0)
+    t = 20.0 * (torch.arange(L) // 32).float()
+    q = u.expand(B, L, H, D) + 0.1 * randn_bf16((B, L, H, D), seed).float()
+    k = 0.1 * randn_bf16((B, L, Hkv, D), seed + 1).float()
+    k[:, :, 0] += t[:, None] / 8.0
+    k[:, :, 1] += t.flip(0)[:, None] / 8.0
+    for h in range(2, Hkv):
+        k[:, :, h] += (t[:, None] / 8.0) * ((torch.arange(L) % 64) < 32).float()[:, None]
+    # V halved (exact): peaked rows follow single value rows, and |O| < 4 keeps bf16 output
+    # rounding below the 1e-2 bar
+    v = 0.5 * randn_bf16((B, L, Hkv, D), seed + 2).float()
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_blocksparse_reference_jumps(D):
+    say(f"blocksparse reference jumps D={D}")
+    B, Hq, Hkv, L = 1, 6, 3, 640
+    q, k, v = _jump_qkv(B, Hq, Hkv, L, D, 9700 + D)
+    lists = make_blocksparse_lists(B, Hq, L, L, 9710 + D, local_blocks=2, p_extra=0.4,
+                                   n_cols=90)
+    scale = D ** -0.5
+    for causal in (True, False):
+        o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, causal, scale)
+        o_ref, lse_ref = _oracle(q, k, v, lists, causal, scale)
+        assert np.isfinite(to_f64(o)).all()
+        check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"sparse jumps causal={causal}")
+
+
+def test_blocksparse_peaky():
+    """Q x 4 (rounded to bf16): attention concentrated on few keys of the union."""
+    import torch
+    say("blocksparse peaky")
+    B, Hq, Hkv, L, D = 1, 8, 2, 1500, 128
+    q = (randn_bf16((B, L, Hq, D), 9800).float() * 4.0).to(torch.bfloat16)
+    k = randn_bf16((B, L, Hkv, D), 9801)
+    v = randn_bf16((B, L, Hkv, D), 9802) * 0.5  # |O| < 4 (see _jump_qkv)
+    lists = make_blocksparse_lists(B, Hq, L, L, 9803, local_blocks=4, p_extra=0.1, n_cols=200)
+    o, lse = _run(q.to(DEV), k.to(DEV), v.to(DEV), lists, True, D ** -0.5)
+    o_ref, lse_ref = _oracle(q, k, v, lists, True, D ** -0.5)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "sparse peaky")

@@ -190,3 +190,27 @@ def test_vslash_128k_sampled_rows():
                                                 w.Lq, 1, allowed)
         check_parity(o[0, rows, h].float().cpu().double().numpy(), o_ref,
                      lse[0, h, rows].cpu().double().numpy(), lse_ref, f"vslash_128k h={h}")
+
+
+def test_vslash_reference_jumps():
+    """Rising / falling / alternating scores (as in the block-sparse reference-jump test) over
+    columns and slash lines only: the first keys a row meets come from phase 2 or phase 3, and
+    later lines raise the row's maximum by far more than fp32 weights can hold."""
+    import torch
+    say("vslash reference jumps")
+    B, Hq, Hkv, L, D = 1, 6, 3, 640, 128
+    u = torch.full((D,), 1.0)
+    t = 20.0 * (torch.arange(L) // 32).float()
+    q = (u.expand(B, L, Hq, D) + 0.1 * randn_bf16((B, L, Hq, D), 9900).float()).to(torch.bfloat16)
+    kf = 0.1 * randn_bf16((B, L, Hkv, D), 9901).float()
+    kf[:, :, 0] += t[:, None] / 8.0
+    kf[:, :, 1] += t.flip(0)[:, None] / 8.0
+    kf[:, :, 2] += (t[:, None] / 8.0) * ((torch.arange(L) % 64) < 32).float()[:, None]
+    k = kf.to(torch.bfloat16)
+    v = randn_bf16((B, L, Hkv, D), 9902) * 0.5  # peaked rows: keeps |O| < 4
+    rng = np.random.default_rng(9903)
+    bp, bi = _no_blocks(B, Hq, L)
+    cp, ci = _csr([rng.choice(L, 40, replace=False) for _ in range(B * Hq)])
+    sp, si = _csr([np.concatenate([np.arange(0, 8), rng.integers(8, L, 20)])
+                   for _ in range(B * Hq)])
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, "vslash jumps")
