@@ -115,17 +115,46 @@ __device__ __forceinline__ void slow_unit(WaveState<D>& ws, const f32x16& s, flo
   ws.mu = munew;
 }
 
-// Copy instruction i (K instructions first, then V) of one tile whose rows are gathered:
-// key_of(r) must return a valid key row, so every load is in bounds. `st` is the stage's LDS
-// address; k_row_bytes / v_row_bytes are the byte strides between key rows.
+// LDS tile of this kernel. K differs from the dense kernel's operand-order slabs: rows are
+// stored row-major, each followed by one 16-byte pad slot (2D + 16 bytes per row). A copy
+// instruction (64 lanes x 16 bytes, landing contiguously) then reads whole key rows, so its
+// loads cover full cache lines; with the slab order each instruction touched 32 rows at 32
+// bytes each, and the tiles here come from scattered blocks that are not in L2 (timing-only
+// copies: 13.0 -> 10.9 ms of copy time at the 128K workload). The pad makes the row stride an
+// odd number of 16-byte slots, so the MFMA operand read (16 consecutive rows of one chunk per
+// quarter wave) hits distinct banks, and k-step s of a lane is its base address plus 32·s.
+// V is the padded row-major tile shared with the dense kernel.
+template <int D>
+struct SpCfg {
+  using T = TileCfg<D>;
+  static constexpr int CPR = T::CPR;
+  static constexpr int KSTEPS = T::KSTEPS;
+  static constexpr int DVB = T::DVB;
+  static constexpr int KSPR = CPR + 1;        // 16-byte slots per K row (one pad slot)
+  static constexpr int KROW = 16 * KSPR;      // bytes per K row
+  static constexpr int KT_BYTES = BN * KROW;  // = 1024 * KSPR
+  static constexpr int KINSTR = KT_BYTES / 1024;
+  static constexpr int VROW = T::VROW;
+  static constexpr int VSPR = T::VSPR;
+  static constexpr int VT_BYTES = T::VT_BYTES;
+  static constexpr int VINSTR = T::VINSTR;
+  static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES;
+  static_assert(KT_BYTES % 1024 == 0, "whole KiB K tiles");
+};
+
+// Copy instruction i (K instructions first, then V) of one tile: copy slot q = 64·i' + l of
+// the K (or V) part holds row q / SPR at chunk q % SPR (pad slots re-read chunk 0 of their
+// row). key_of(r) returns the key of tile row r and must be a valid key, so every load is in
+// bounds. `st` is the stage's LDS address; k_row_bytes / v_row_bytes are the byte strides
+// between key rows.
 template <int D, class KeyOf>
 __device__ __forceinline__ void copy_instr_gather(uint32_t st, const uint16_t* kbase,
                                                   const uint16_t* vbase, uint32_t k_row_bytes,
                                                   uint32_t v_row_bytes, KeyOf key_of, int i, int l) {
-  using C = TileCfg<D>;
+  using C = SpCfg<D>;
   uint32_t r, c;
   if (i < C::KINSTR) {
-    kslab_rc<D>(i, l, r, c);
+    slot_rc<C::KSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
     dma16_vaddr((const char*)kbase + (int64_t)key_of((int)r) * k_row_bytes + c * 16u,
                 st + (uint32_t)i * 1024u);
   } else {
@@ -136,26 +165,24 @@ __device__ __forceinline__ void copy_instr_gather(uint32_t st, const uint16_t* k
   }
 }
 
-// Scalar-base tile copy of 64 consecutive key rows with the lane offsets computed at issue:
-// K instruction i reads row 32·(i/KSTEPS) + l%32 at chunk 2·(i%KSTEPS) + l/32, i.e. the lane
-// term (l%32)·row + (l/32)·16 plus a wave-uniform term; V instructions follow the padded slot
-// map. Wave wu issues instructions wu, wu+NW, ... With LEAN, the lane id goes through an
-// opaque copy, so the V offsets are recomputed at every issue instead of being hoisted out of
-// the caller's loop into registers held for the whole kernel (for kernels short of registers).
+// Scalar-base copy of a tile of 64 consecutive key rows (the same slot maps, per-lane offsets
+// from the tile's first row). Wave wu issues instructions wu, wu+NW, ... With LEAN, the lane id
+// goes through an opaque copy, so the offsets are recomputed at every issue instead of being
+// hoisted out of the caller's loop into registers held for the whole kernel (for kernels short
+// of registers).
 template <int D, int NW, bool LEAN>
 __device__ __forceinline__ void issue_tile_sbase_lean(uint32_t stage, const uint16_t* ktile,
                                                       const uint16_t* vtile, uint32_t k_row_bytes,
                                                       uint32_t v_row_bytes, int wu, int l) {
-  using C = TileCfg<D>;
+  using C = SpCfg<D>;
   if constexpr (LEAN) asm volatile("" : "+v"(l));
-  const uint32_t kl = (uint32_t)(l & 31) * k_row_bytes + (uint32_t)(l >> 5) * 16u;
 #pragma unroll
   for (int k = 0; k < (C::KINSTR + NW - 1) / NW; ++k) {
     const int i = wu + NW * k;
     if ((C::KINSTR % NW) == 0 || i < C::KINSTR) {
-      const uint32_t u = (uint32_t)(32 * (i / C::KSTEPS)) * k_row_bytes +
-                         (uint32_t)(i % C::KSTEPS) * 32u;
-      dma16_sbase(ktile, kl + u, stage + (uint32_t)i * 1024u);
+      uint32_t r, c;
+      slot_rc<C::KSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+      dma16_sbase(ktile, r * k_row_bytes + c * 16u, stage + (uint32_t)i * 1024u);
     }
   }
 #pragma unroll
@@ -176,7 +203,7 @@ template <int D, int NW, class KeyOf>
 __device__ __forceinline__ void issue_tile_gather(uint32_t st, const uint16_t* kbase,
                                                   const uint16_t* vbase, uint32_t k_row_bytes,
                                                   uint32_t v_row_bytes, KeyOf key_of, int w, int l) {
-  using C = TileCfg<D>;
+  using C = SpCfg<D>;
   constexpr int NI = (C::KINSTR + C::VINSTR + NW - 1) / NW;
   const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
@@ -193,7 +220,7 @@ __device__ __forceinline__ void issue_tile_gather(uint32_t st, const uint16_t* k
 template <int D, class Mask>
 __device__ __forceinline__ void tile_math_mask(const FwdArgs& a, WaveState<D>& ws, const char* st,
                                                bool masked, Mask mask, int l) {
-  using C = TileCfg<D>;
+  using C = SpCfg<D>;
   constexpr int NQ = C::KSTEPS;  // MFMAs of a unit's Sᵀ
   constexpr int NV = 2 * C::DVB;  // MFMAs of a unit's P·V
   static_assert(NQ == NV, "the two softmax phases have the same number of slots");
@@ -206,7 +233,8 @@ __device__ __forceinline__ void tile_math_mask(const FwdArgs& a, WaveState<D>& w
   // v covers output block v % DVB and unit k-step v / DVB (keys 16·ks .. 16·ks+15 of the unit),
   // so consecutive MFMAs accumulate into different blocks.
   auto operand = [&](int n) -> bf16x8 {
-    if (n < 2 * NQ) return lds_read_b128_at(kt + 1024u * (uint32_t)n);
+    // K: row 32·u + l%32 of unit u = n / NQ, chunk 2·s + l/32 of k-step s = n % NQ
+    if (n < 2 * NQ) return lds_read_b128_at(kt + (uint32_t)(32 * C::KROW * (n / NQ) + 32 * (n % NQ)));
     const int u = (n - 2 * NQ) / NV, v = (n - 2 * NQ) % NV;
     const uint32_t o = vt + (32u * u + 16u * (v / C::DVB)) * C::VROW + 64u * (v % C::DVB);
     return lds_read_tr_pair_at(o, o + 8u * C::VROW);
@@ -330,8 +358,8 @@ __device__ __forceinline__ void load_q(const FwdArgs& a, WaveState<D>& ws, int b
   ws.mu = INFINITY;
   ws.lb = 0.f;
   ws.lf = 0.f;
-  // K operand: lane l's 16 bytes of every slab
-  ws.kofs = (uint32_t)l * 16u;
+  // K operand: row l%32 of the unit, chunk l/32 of the k-step
+  ws.kofs = (uint32_t)(l & 31) * (uint32_t)SpCfg<D>::KROW + (uint32_t)(l >> 5) * 16u;
   // V operand: group G = l/16, row 4*(G/2) + (l%16)/4, column 16*(G%2) + 4*(l%4)
   const int G = l >> 4;
   ws.vofs = (uint32_t)(4 * (G >> 1) + ((l & 15) >> 2)) * C::VROW +
@@ -403,7 +431,7 @@ __device__ __forceinline__ int logical_block(int xcd_remap) {
 // two bitmaps (vs_bits_kernel); the words of both that a tile's mask needs are copied into
 // LDS together with the tile, and each lane reads the 96 + 64 bits its 32 scores need.
 // ------------------------------------------------------------------------------------------
-constexpr int kSeg = 512;              // ids examined per compaction pass
+constexpr int kSeg = 256;              // ids examined per compaction pass
 constexpr int kMaxBitmapWords = 512;   // listed-block bitmaps: up to 16384 key blocks (1M keys)
 constexpr int kSlashBitmapWords = kVslashMaxLk / 64 / 32;  // crossed blocks (slash variant)
 constexpr int kFlagShift = 24;         // phase-2 entry: column id below, block flags above
@@ -412,7 +440,10 @@ constexpr int kMaskOffWords = 48;      // offset-bitmap words copied per slash t
 
 template <int D, bool SLASH, int QB>
 __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArgs a) {
-  using C = TileCfg<D>;
+  using C = SpCfg<D>;
+  // listed-block bitmap words: the slash variant's shorter key limit frees LDS for its own
+  // bitmap and mask words (two workgroups per CU need at most 80 KiB each)
+  constexpr int BMW = SLASH ? kVslashMaxLk / 64 / 32 : kMaxBitmapWords;
   constexpr int NW = 2 * QB;
   constexpr int NT = NW * 64;
   constexpr int NS = 2;  // ring stages
@@ -420,11 +451,11 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   static_assert(kFlagShift + QB <= 31, "phase-2 flags fit an int");
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
-  __shared__ uint32_t bm[QB][kMaxBitmapWords];                 // listed blocks of the group
+  __shared__ uint32_t bm[QB][BMW];                             // listed blocks of the group
   __shared__ uint32_t tbits[SLASH ? kSlashBitmapWords : 1];  // blocks crossed by a slash line
   __shared__ int kept[kSeg];
   __shared__ int wave_cnt[NW];
-  __shared__ uint32_t mwl[SLASH ? NS : 1][64];  // per stage: the tile's mask words (slash)
+  __shared__ uint32_t mwl[SLASH ? NS : 1][SLASH ? 64 : 1];  // per stage: a slash tile's mask words
 
   const int tid = (int)threadIdx.x;
   const int w = tid >> 6;
