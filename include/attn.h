@@ -67,7 +67,7 @@ typedef struct attn_tensor {
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1,  /* a size, stride, alignment, pointer or scale is invalid */
-  ATTN_ERR_UNSUPPORTED = -2,  /* valid arguments that this build has no kernel for */
+  ATTN_ERR_UNSUPPORTED = -2,  /* valid arguments that the library has no kernel for */
   ATTN_ERR_WORKSPACE = -3,    /* split-KV partial buffers missing */
   ATTN_ERR_LAUNCH = -4        /* the HIP runtime refused the launch (message in last_error) */
 } attn_status_t;

@@ -14,7 +14,7 @@ What the pages fix and what they leave open:
 * "SparseAccelerate: Acelerando Modelos de Lenguaje", section "Patrones de Atención Dispersa
   Dinámicos": per-head dynamic patterns chosen for the input.
 
-The pages name no estimator. The one computed here is this build's reading, the plainest that
+The pages name no estimator. The one computed here is a reading of them, the plainest that
 the lists consumed by the block-sparse forward admit:
 
 1. Block lists (per query head, per 64-row query block qb): mean-pool the query block's rows

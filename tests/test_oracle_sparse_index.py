@@ -1,6 +1,6 @@
 """Pins of the sparse-index oracle (CPU only), and planted mistakes that the pins must catch.
 
-The estimator is this build's reading (the pages name none), so it is pinned by closed forms
+The estimator is a reading of the pages (they name none), so it is pinned by closed forms
 of its own definition that any plausible slip breaks: equal keys (ties and the diagonal),
 block scores built to grow with the key block (ranking direction, causality), probe
 importances of equal keys (causal softmax normalisation), planted blocks and columns, list
