@@ -147,11 +147,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
-__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
-                                              float a5, float a6, float a7) {
-  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3),
-                                               pack_bf16x2(a4, a5), pack_bf16x2(a6, a7)));
-}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -59,23 +59,14 @@ __device__ __forceinline__ void slot_rc(uint32_t slot, uint32_t& r, uint32_t& c)
   c = cs < (uint32_t)CPR ? cs : 0u;
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  if constexpr (N == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    // gfx9 encoding: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14; expcnt and lgkmcnt at
-    // their maxima (no wait on them)
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  }
-}
 // vmcnt(0) in a form the compiler sees: afterwards it knows that every earlier load of the
 // wave has completed and adds no waits of its own for those loads (it does not see the copies,
 // so a wait it adds for an older register load would also drain the copies in flight).
 __device__ __forceinline__ void wait_vmcnt_visible0() {
+  // gfx9 encoding: vmcnt 0 (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 }
+
 // Workgroup barrier without a memory fence (the copies it orders are waited for explicitly).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
