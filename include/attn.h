@@ -116,7 +116,8 @@ int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits,
 /*
  * attn_fwd_decode — split-KV decode and its LSE combine in one call: attn_fwd_splitkv with
  * num_splits = attn_splitkv_num_splits(...) followed by attn_combine_lse, on one stream, with
- * the partials in the caller's workspace. Arguments as attn_fwd; o is bf16 strided like
+ * the partials in the caller's workspace. When that count is 1, the split kernel writes O and
+ * LSE itself and no combine is launched (same values bit for bit). Arguments as attn_fwd; o is bf16 strided like
  * attn_fwd's, lse fp32 [B, Hq, Lq] or NULL.
  * workspace: DEVICE buffer of at least attn_decode_workspace_bytes(...) bytes, 256-byte
  * aligned, owned by the caller; its contents on entry do not matter. Calls that overlap on

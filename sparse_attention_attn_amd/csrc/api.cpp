@@ -115,6 +115,9 @@ int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o
     a.causal = causal ? 1 : 0;
     a.off = Lk - Lq;
     exp2_scale(scale, a.sl2, a.qsign);
+    a.o = nullptr;  // the partials are this entry point's output, even for one split
+    a.o_sb = a.o_sl = a.o_sh = 0;
+    a.lse = nullptr;
     a.num_splits = num_splits;
     a.chunk = attn::split_chunk(Lk, num_splits);
     const int cols = attn::split_cols(Dqk, a.g * Lq);
@@ -162,8 +165,13 @@ int attn_fwd_decode(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tens
     const int cols = attn::split_cols(Dqk, a.g * Lq);
     a.ncolblk = (a.g * Lq + cols - 1) / cols;
     hipStream_t sm = static_cast<hipStream_t>(stream);
+    // One split: the split kernel writes O and LSE itself (the combine would only copy them).
+    const bool direct = ws.num_splits == 1;
+    a.o = direct ? static_cast<uint16_t*>(o.data) : nullptr;
+    a.o_sb = o.stride_b; a.o_sl = o.stride_l; a.o_sh = o.stride_h;
+    a.lse = direct ? lse : nullptr;
     st = launch_status(fn, attn::launch_splitkv(a, Dqk, Dv, sm));
-    if (st != ATTN_OK) return st;
+    if (st != ATTN_OK || direct) return st;
     attn::CombineArgs c;
     c.o_part = a.o_part;
     c.lse_part = a.lse_part;

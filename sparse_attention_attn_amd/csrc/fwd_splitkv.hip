@@ -406,6 +406,22 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     tf = tf + xor_shuffle(tf, 32);
     if (!col_ok[c]) continue;
     const float inv = tb > 0.f ? 1.0f / tb : 0.f;
+    if (a.o != nullptr) {  // the only split: final O and LSE, no combine
+      uint16_t* orow = a.o + (int64_t)b * a.o_sb + (int64_t)pos[c] * a.o_sl +
+                       (int64_t)hq[c] * a.o_sh;
+#pragma unroll
+      for (int i = 0; i < C::DVB; ++i) {
+        const int dv = w * C::DVW + 16 * i + 4 * G;
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[c][i][0] * inv, acc[c][i][1] * inv);
+        pk.y = pack_bf16x2(acc[c][i][2] * inv, acc[c][i][3] * inv);
+        *reinterpret_cast<uint2*>(orow + dv) = pk;
+      }
+      if (a.lse != nullptr && w == 0 && G == 0)
+        a.lse[((int64_t)b * a.Hq + hq[c]) * a.Lq + pos[c]] =
+            tf > 0.f ? m[c] * kLn2 + logf(tf) : -INFINITY;
+      continue;
+    }
     const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq[c]) * a.Lq + pos[c];
     float* op = a.o_part + prow * DV;
 #pragma unroll

@@ -63,6 +63,11 @@ struct SplitArgs {
   int num_splits;
   int chunk;        // keys per split (multiple of 64)
   int ncolblk;      // ceil(g * Lq / split_cols(Dqk, g * Lq))
+  // One split only: when o is set, the kernel writes the final O (bf16, strided like attn_fwd's
+  // O) and LSE (fp32 [B, Hq, Lq] or nullptr) instead of the partials, and no combine follows.
+  uint16_t* o;
+  int64_t o_sb, o_sl, o_sh;
+  float* lse;
 };
 
 struct CombineArgs {

@@ -47,6 +47,8 @@ SHAPES = [
     (2, 16, 4, 2, 3000, 128, True),     # two query tokens, bottom-right causal
     (5, 8, 8, 1, 777, 64, False),
     (2, 6, 2, 3, 2049, 64, True),
+    (2, 16, 4, 2, 300, 128, True),      # one split (under 512 keys): O and LSE written directly
+    (128, 32, 8, 1, 1024, 128, False),  # one split (1024 units fill the GPU): direct too
 ]
 
 
@@ -96,3 +98,33 @@ def test_decode_one_call_deterministic():
     a = _run(q, k, v, False, 0.088)
     b = _run(q, k, v, False, 0.088)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_one_call_mla_one_split():
+    """The MLA latent shape with one split (400 keys): the split kernel writes O and LSE."""
+    import sparse_attention_attn_amd as S
+    B, Hq, Lq, Lk = 2, 16, 1, 400
+    say("one-call MLA decode, one split")
+    assert S.attn_splitkv_num_splits(B, Hq, 1, Lq, Lk, 576, 512) == 1
+    q = randn_bf16((B, Lq, Hq, 576), 8700)
+    k = randn_bf16((B, Lk, 1, 576), 8701)
+    _check(q, k, None, True, 192 ** -0.5, "one-call MLA one split", mla=True)
+
+
+def test_decode_one_split_equals_partials_path():
+    """One split through attn_fwd_decode (direct outputs) equals attn_fwd_splitkv with one split
+    followed by attn_combine_lse, bit for bit."""
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Hq, Hkv, Lq, Lk, D = 2, 16, 4, 2, 300, 128
+    say("one split: direct outputs vs partials + combine")
+    q = randn_bf16((B, Lq, Hq, D), 8710).to(DEV)
+    k = randn_bf16((B, Lk, Hkv, D), 8711).to(DEV)
+    v = randn_bf16((B, Lk, Hkv, D), 8712).to(DEV)
+    assert S.attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, D, D) == 1
+    o1, l1 = _run(q, k, v, True, D ** -0.5)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    S.splitkv_decode(q, k, v, o2, l2, causal=True, scale=D ** -0.5, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
