@@ -5,10 +5,10 @@
 // statistics kept on chip ("Activar Flash Attention con llama.cpp para optimizar la
 // inferencia", section "¿Qué es Flash Attention y por qué es crucial para llama.cpp?").
 //
-// Work decomposition. One workgroup (one per CU) owns 256 query rows of one (batch, query
-// head). Its waves own NR 32-row MFMA blocks each: NR = 1 gives 8 waves (two per SIMD, so each
-// SIMD also interleaves two instruction streams); NR = 2 gives 4 waves (one per SIMD) whose
-// K and V operand reads from LDS each feed two MFMAs.
+// Work decomposition. One workgroup of 8 waves owns 256 query rows of one (batch, query head);
+// each wave owns one 32-row MFMA block, so every SIMD interleaves the instruction streams of two
+// waves. (128-row workgroups of 4 waves, two per CU, measured 3% slower: each then streams its
+// own copy of every K/V tile.)
 //
 // Per 64-key tile and wave, the products are formed transposed (the Sᵀ accumulator holds 16
 // keys of ONE query per lane, so the same registers, rounded to bf16, are the B operand Pᵀ of
@@ -18,9 +18,11 @@
 // Software pipeline. Iteration t of a wave issues the MFMAs of Sᵀ(t+1) and of Oᵀ += Vᵀ(t-1)·
 // Pᵀ(t-1) and, independent of both, the softmax of tile t (max, exp2, bf16 packing, sums) on
 // the vector ALU, so a single wave keeps the matrix core and the VALU busy at the same time.
-// K/V tiles stream through a 4-stage LDS ring filled by asynchronous global->LDS copies:
-// iteration t copies tile t+2 while tiles t+1 (K read) and t-1 (V read) are in use. One
-// workgroup barrier per iteration frees the stage of tile t-2.
+// K/V tiles stream through a 2-stage LDS ring filled by asynchronous global->LDS copies. A stage
+// holds K of tile t and V of tile t-1, the two operands that the same pipeline steps read, so
+// two stages hide one tile of copy latency: iteration t copies the pair (K(t+2), V(t+1)) while
+// the pair (K(t+1), V(t)) is in use. One workgroup barrier per iteration frees the stage of the
+// pair (K(t), V(t-1)).
 //
 // Softmax. Scores live in the exp2 domain (x = s·scale·log2 e). Each row keeps a reference m,
 // the largest score seen when it was last set, and weights are exp2(x - m). The reference is
@@ -42,7 +44,10 @@
 namespace attn {
 namespace {
 
-constexpr int kStages = 4;
+constexpr int kStages = 2;
+// Waves per workgroup (each owns 32 query rows) and workgroups resident per CU.
+constexpr int kDenseWaves = kDenseBlockM / 32;
+constexpr int kDenseWgPerCu = kDenseWaves == 4 ? 2 : 1;
 // MFMA slots between an operand's LDS read and its use.
 #ifndef ATTN_DENSE_READ_AHEAD
 #define ATTN_DENSE_READ_AHEAD 2
@@ -329,14 +334,16 @@ __device__ __forceinline__ int logical_block_xcd(int xcd_remap) {
 //
 // Pipeline. Keys are processed in 32-key units u (unit u = half u%2 of tile u/2). Step j issues
 // the MFMAs of Sᵀ(u = j+1) and of Oᵀ += Vᵀ(j-1)·Pᵀ(j-1), and the softmax of unit j. Score and
-// weight registers alternate between two sets by unit parity. Step 2t+1 (second half of tile
-// t) opens with the wait for tile t+1, the workgroup barrier, and the copy of tile t+2 into
-// the stage of tile t-2, whose last reader was step 2t-2.
+// weight registers alternate between two sets by unit parity. Steps 2t-1 and 2t read K of tile
+// t and V of tile t-1: together they form the LDS pair t, held in stage t%2. Step 2t+1 (second
+// half of tile t) opens with the wait for pair t+1, the workgroup barrier, and the copy of pair
+// t+2 into the stage of pair t, whose last reader was step 2t.
 template <int D, int NR>
-__global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(kDenseWaves * 64, kDenseWgPerCu) void fwd_dense_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
-  constexpr int NW = 8 / NR;
+  constexpr int NW = kDenseWaves;
   constexpr int BM = 32 * NR * NW;
+  static_assert(BM == kDenseBlockM, "rows per workgroup");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * C::STAGE_BYTES];
   const uint32_t lds0 = lds_addr(smem);
 
@@ -370,7 +377,8 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
   }
 
   TileByteOffsets<D, NW> off;
-  off.init(a, w, l);
+  off.init_k(a, w, l);
+  off.init_v(a, w, l);
   const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
@@ -381,17 +389,23 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
   if (a.causal) nfull = min(nfull, max(0, qw0 + a.off + 1) / 32);
   nfull = __builtin_amdgcn_readfirstlane(nfull);
 
-  auto stage_addr = [&](int t) -> uint32_t { return lds0 + (uint32_t)(t & 3) * C::STAGE_BYTES; };
-  // Copies tile t (t < ntiles, issued in increasing order) into its stage. A ragged last tile
-  // re-reads its last key row in the missing rows, so every copy stays inside the sequence; as
-  // it is the last tile copied, its clamped offsets replace the full-tile ones in place.
+  auto stage_addr = [&](int t) -> uint32_t { return lds0 + (uint32_t)(t & 1) * C::STAGE_BYTES; };
+  // Copies pair t (issued in increasing order of t <= ntiles) into its stage: K of tile t when
+  // t < ntiles and V of tile t-1 when t >= 1. A ragged last tile re-reads its last key row in
+  // the missing rows, so every copy stays inside the sequence; as it is the last K (V) tile
+  // copied, its clamped offsets replace the full-tile ones in place.
   auto issue = [&](int t) {
-    const int base = t * BN;
-    const uint16_t* kt = kb + (int64_t)base * a.k_sl;
-    const uint16_t* vt = vb + (int64_t)base * a.v_sl;
     const uint32_t st = __builtin_amdgcn_readfirstlane(stage_addr(t));
-    if (base + BN > a.Lk) off.init(a, w, l, a.Lk - 1 - base);
-    issue_tile_sbase<D, NW>(st, kt, vt, off, wu);
+    if (t < ntiles) {
+      const int base = t * BN;
+      if (base + BN > a.Lk) off.init_k(a, w, l, a.Lk - 1 - base);
+      issue_k_sbase<D, NW>(st, kb + (int64_t)base * a.k_sl, off, wu);
+    }
+    if (t >= 1) {
+      const int base = (t - 1) * BN;
+      if (base + BN > a.Lk) off.init_v(a, w, l, a.Lk - 1 - base);
+      issue_v_sbase<D, NW>(st + C::KT_BYTES, vb + (int64_t)base * a.v_sl, off, wu);
+    }
   };
 
   f32x16 sc[2][NR];     // Sᵀ register sets (unit parity, row block)
@@ -402,13 +416,14 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
   const uint32_t vofs = C::KT_BYTES + (uint32_t)(4 * (G >> 1) + ((l & 15) >> 2)) * C::VROW +
                         (uint32_t)(16 * (G & 1) + 4 * (l & 3)) * 2u;
 
-  // Prologue: tile 0 copied and waited for, tile 1 in flight; the V part of stage 3 (read by
-  // the P·V of "unit -1", whose weights are zero) is cleared so that it holds finite values.
+  // Prologue: pair 0 (K of tile 0) copied and waited for, pair 1 in flight. The V part of
+  // stage 0 (read by the P·V of "unit -1", whose weights are zero) is cleared so that it holds
+  // finite values.
   issue(0);
   {
-    char* v3 = smem + 3 * C::STAGE_BYTES + C::KT_BYTES;
+    char* v0 = smem + C::KT_BYTES;
     for (int i = tid; i < C::VT_BYTES / 16; i += NW * 64)
-      *reinterpret_cast<uint4*>(v3 + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(v0 + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -416,25 +431,26 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
     for (int ks = 0; ks < 2; ++ks) pw[1][r][ks] = zero_bf16x8();
   wait_dma_all();
   __syncthreads();
-  if (ntiles > 1) issue(1);
+  issue(1);
   qk_unit<D, NR>(ws, stage_addr(0) + kofs, 0, sc[0]);
 
-  // Step j = 2t + H.
+  // Step j = 2t + H reads pair t + H.
   auto step = [&](auto HI, int t) {
     constexpr int H = decltype(HI)::value;
     const int j = 2 * t + H;
     if constexpr (H == 1) {
-      wait_dma_all();  // tile t+1 landed (this wave's copies) ...
+      wait_dma_all();  // pair t+1 landed (this wave's copies) ...
       barrier_lds();   // ... for every wave, and every wave is done with step 2t
-      if (t + 2 < ntiles) issue(t + 2);
+      if (t + 2 <= ntiles) issue(t + 2);
     }
     float sb[NR], sf[NR];
     bool ok;
     if (j >= nfull) mask_unit<NR>(sc[H], j, qw0, a.Lk, a.causal, a.off, l);
     // Sᵀ(j+1): H = 0 -> second half of tile t; H = 1 -> first half of tile t+1.
     // P·V of unit j-1: H = 0 -> second half of tile t-1; H = 1 -> first half of tile t.
-    fused_step<D, NR>(ws, sc[H], sc[1 - H], pw[1 - H], pw[H], stage_addr(t + H) + kofs, 1 - H,
-                      stage_addr(t + 3 + H) + vofs, 1 - H, a.sl2, sb, sf, ok);
+    const uint32_t st = stage_addr(t + H);
+    fused_step<D, NR>(ws, sc[H], sc[1 - H], pw[1 - H], pw[H], st + kofs, 1 - H, st + vofs, 1 - H,
+                      a.sl2, sb, sf, ok);
     anchor_weights<NR>(pw[H], sb, sf);
     if (__builtin_expect(__any(!ok), 0)) {
       slow_unit<D, NR>(ws, sc[H], pw[H], a.sl2);
@@ -447,8 +463,9 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
     }
   };
 
-  // 2*ntiles + 1 steps; the last one only finishes the P·V of the last unit. The loop body is
-  // a whole tile with a single exit, so the accumulators keep their registers across it.
+  // 2*ntiles + 1 steps; the last one only finishes the P·V of the last unit (its Sᵀ reads a
+  // K part that holds no tile and is never used). The loop body is a whole tile with a single
+  // exit, so the accumulators keep their registers across it.
   for (int t = 0; t < ntiles; ++t) {
     step(icn<0>{}, t);
     step(icn<1>{}, t);
@@ -460,7 +477,7 @@ __global__ __launch_bounds__((8 / NR) * 64, 1) void fwd_dense_kernel(const FwdAr
 
 template <int D>
 hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = 8 / kDenseNR;
+  constexpr int NW = kDenseWaves;
   const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
   FwdArgs aa = a;
   aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;

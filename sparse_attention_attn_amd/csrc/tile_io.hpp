@@ -70,18 +70,19 @@ __device__ __forceinline__ void wait_vmcnt_visible0() {
 // Workgroup barrier without a memory fence (the copies it orders are waited for explicitly).
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
-// Scalar-base tile copy. Wave w of NW issues the K copy instructions w, w+NW, ... and the V
+// Scalar-base tile copies. Wave w of NW issues the K copy instructions w, w+NW, ... and the V
 // copy instructions w, w+NW, ... (KINSTR and VINSTR are multiples of NW), so which tensor an
 // instruction reads is fixed at compile time. `ko` / `vo` hold the lane's byte offsets
 // relative to the tile's first key row; maxrow < 63 describes a ragged last tile (rows past
-// maxrow re-read row maxrow, so every copy stays inside the sequence).
+// maxrow re-read row maxrow, so every copy stays inside the sequence). The K and V offsets are
+// set separately because a K tile and a V tile of one LDS stage may belong to different keys.
 template <int D, int NW>
 struct TileByteOffsets {
   static constexpr int KI = (TileCfg<D>::KINSTR + NW - 1) / NW;
   static constexpr int VI = (TileCfg<D>::VINSTR + NW - 1) / NW;
   uint32_t ko[KI];
   uint32_t vo[VI];
-  __device__ __forceinline__ void init(const FwdArgs& a, int w, int l, int maxrow = BN - 1) {
+  __device__ __forceinline__ void init_k(const FwdArgs& a, int w, int l, int maxrow = BN - 1) {
     using C = TileCfg<D>;
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
@@ -90,6 +91,9 @@ struct TileByteOffsets {
       r = min(r, (uint32_t)maxrow);
       ko[k] = (r * (uint32_t)a.k_sl + c * 8u) * 2u;
     }
+  }
+  __device__ __forceinline__ void init_v(const FwdArgs& a, int w, int l, int maxrow = BN - 1) {
+    using C = TileCfg<D>;
 #pragma unroll
     for (int v = 0; v < VI; ++v) {
       uint32_t r, c;
@@ -100,25 +104,28 @@ struct TileByteOffsets {
   }
 };
 
-// Copies one tile (K rows from ktile, V rows from vtile, both wave-uniform) into the stage at
-// LDS address `stage` (wave-uniform) with the scalar-base copy instruction. Wave wu issues the
-// K instructions wu, wu+NW, ... and the V instructions wu, wu+NW, ... that exist.
+// Copies one K tile (rows from ktile, wave-uniform) to LDS address `kdst` (wave-uniform) with
+// the scalar-base copy instruction; wave wu issues the K instructions wu, wu+NW, ...
 template <int D, int NW>
-__device__ __forceinline__ void issue_tile_sbase(uint32_t stage, const uint16_t* ktile,
-                                                 const uint16_t* vtile,
-                                                 const TileByteOffsets<D, NW>& o, int wu) {
+__device__ __forceinline__ void issue_k_sbase(uint32_t kdst, const uint16_t* ktile,
+                                              const TileByteOffsets<D, NW>& o, int wu) {
   using C = TileCfg<D>;
 #pragma unroll
   for (int k = 0; k < TileByteOffsets<D, NW>::KI; ++k) {
     const int i = wu + NW * k;
-    if ((C::KINSTR % NW) == 0 || i < C::KINSTR)
-      dma16_sbase(ktile, o.ko[k], stage + (uint32_t)i * 1024u);
+    if ((C::KINSTR % NW) == 0 || i < C::KINSTR) dma16_sbase(ktile, o.ko[k], kdst + (uint32_t)i * 1024u);
   }
+}
+
+// The same for one V tile (padded rows) at LDS address `vdst`.
+template <int D, int NW>
+__device__ __forceinline__ void issue_v_sbase(uint32_t vdst, const uint16_t* vtile,
+                                              const TileByteOffsets<D, NW>& o, int wu) {
+  using C = TileCfg<D>;
 #pragma unroll
   for (int v = 0; v < TileByteOffsets<D, NW>::VI; ++v) {
     const int i = wu + NW * v;
-    if ((C::VINSTR % NW) == 0 || i < C::VINSTR)
-      dma16_sbase(vtile, o.vo[v], stage + C::KT_BYTES + (uint32_t)i * 1024u);
+    if ((C::VINSTR % NW) == 0 || i < C::VINSTR) dma16_sbase(vtile, o.vo[v], vdst + (uint32_t)i * 1024u);
   }
 }
 
