@@ -180,12 +180,85 @@ def _stream(stream, device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# Shape checks. The C ABI receives raw pointers and cannot see buffer sizes, so every wrapper
+# checks here, before any pointer is taken, that the tensors agree with the sizes it passes: a
+# mismatch would otherwise become an out-of-bounds device access. They run before the GPU
+# placement checks, so they hold for CPU tensors too.
+def _shape(t, name, want):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} must have shape {tuple(want)}, got {tuple(t.shape)}")
+
+
+def _rank(t, name, n, what):
+    if t.dim() != n:
+        raise ValueError(f"{name} must be {what}, got shape {tuple(t.shape)}")
+
+
+def _numel_at_least(t, name, n):
+    if t.numel() < n:
+        raise ValueError(f"{name} must hold at least {n} elements, got {t.numel()}")
+
+
+def _bytes_at_least(t, name, n):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < n:
+        raise ValueError(f"{name} must hold at least {n} bytes, got "
+                         f"{t.numel() * t.element_size()}")
+
+
+def _numel(t, name, n):
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+
+
+def _one_device(named):
+    devs = {str(t.device) for _, t in named if t is not None}
+    if len(devs) > 1:
+        names = ", ".join(f"{n}: {t.device}" for n, t in named if t is not None)
+        raise ValueError(f"all tensors must be on one device ({names})")
+
+
+def _qkv_sizes(q, k, v):
+    """(B, Lq, Hq, Dqk, Lk, Hkv, Dv) after checking that q, k, v agree."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _rank(t, n, 4, "[B, L, H, D]")
+    B, Lq, Hq, Dqk = q.shape
+    Bk, Lk, Hkv, Dk = k.shape
+    Bv, Lv, Hv, Dv = v.shape
+    if Bk != B or Bv != B:
+        raise ValueError(f"batch sizes differ: q {B}, k {Bk}, v {Bv}")
+    if Lv != Lk or Hv != Hkv:
+        raise ValueError(f"k [{Bk}, {Lk}, {Hkv}, {Dk}] and v [{Bv}, {Lv}, {Hv}, {Dv}] must agree "
+                         "on length and heads")
+    if Dk != Dqk:
+        raise ValueError(f"k head dim {Dk} differs from q head dim {Dqk}")
+    return B, Lq, Hq, Dqk, Lk, Hkv, Dv
+
+
+def _index_qk_sizes(q, k):
+    """(B, L, Hq, D) of the index builders' square inputs, after checking q and k agree."""
+    _rank(q, "q", 4, "[B, L, Hq, D]")
+    _rank(k, "k", 4, "[B, L, Hkv, D]")
+    B, L, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != L or k.shape[3] != D:
+        raise ValueError(f"k {tuple(k.shape)} must be [B, L, Hkv, D] with q's B, L and D "
+                         f"(q {tuple(q.shape)})")
+    return B, L, Hq, D
+
+
+def _check_out(o, lse, B, Lq, Hq, Dv):
+    _shape(o, "o", (B, Lq, Hq, Dv))
+    if lse is not None:
+        _numel(lse, "lse", B * Hq * Lq)
+
+
 # ------------------------------------------------------------------------------- entry points
 def attn_fwd(q, k, v, o, lse=None, causal=True, scale=None, stream=None):
     """Dense attention forward: O (and LSE [B, Hq, Lq] fp32 if given) from Q, K, V."""
-    B, Lq, Hq, Dqk = q.shape
-    Lk, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
+    _check_out(o, lse, B, Lq, Hq, Dv)
+    _one_device([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)])
     if scale is None:
         scale = Dqk ** -0.5
     st = load_library().attn_fwd(
@@ -206,10 +279,12 @@ def attn_splitkv_workspace_bytes(B, Hq, Lq, Dv, num_splits) -> int:
 
 def attn_fwd_splitkv(q, k, v, o_part, lse_part, causal=False, scale=None, stream=None):
     """Per-split partials: o_part fp32 [S, B, Hq, Lq, Dv], lse_part fp32 [S, B, Hq, Lq]."""
-    B, Lq, Hq, Dqk = q.shape
-    Lk, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
+    _rank(o_part, "o_part", 5, "[S, B, Hq, Lq, Dv]")
     S = o_part.shape[0]
+    _shape(o_part, "o_part", (S, B, Hq, Lq, Dv))
+    _shape(lse_part, "lse_part", (S, B, Hq, Lq))
+    _one_device([("q", q), ("k", k), ("v", v), ("o_part", o_part), ("lse_part", lse_part)])
     if scale is None:
         scale = Dqk ** -0.5
     st = load_library().attn_fwd_splitkv(
@@ -222,7 +297,11 @@ def attn_fwd_splitkv(q, k, v, o_part, lse_part, causal=False, scale=None, stream
 
 def attn_combine_lse(o_part, lse_part, o, lse=None, stream=None):
     """Merge split partials into O (bf16 [B, Lq, Hq, Dv], strided) and LSE."""
+    _rank(o_part, "o_part", 5, "[S, B, Hq, Lq, Dv]")
     S, B, Hq, Lq, Dv = o_part.shape
+    _shape(lse_part, "lse_part", (S, B, Hq, Lq))
+    _check_out(o, lse, B, Lq, Hq, Dv)
+    _one_device([("o_part", o_part), ("lse_part", lse_part), ("o", o), ("lse", lse)])
     st = load_library().attn_combine_lse(
         _opt_ptr(o_part, "o_part"), _opt_ptr(lse_part, "lse_part"), S, _tensor_desc(o, "o"),
         _opt_ptr(lse, "lse"), B, Hq, Lq, Dv, _stream(stream, o.device))
@@ -236,9 +315,7 @@ def splitkv_decode(q, k, v, o, lse=None, causal=False, scale=None, num_splits=No
 
     The MLA latent shape passes v = k[..., :512] (a view of k: same pointer and strides)."""
     torch = _torch()
-    B, Lq, Hq, Dqk = q.shape
-    Lk, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
     S = num_splits or attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv)
     if workspace is None:
         o_part = torch.empty((S, B, Hq, Lq, Dv), dtype=torch.float32, device=q.device)
@@ -258,14 +335,15 @@ def attn_fwd_decode(q, k, v, o, lse=None, causal=False, scale=None, workspace=No
     """Split-KV decode plus combine in one call; the partials go to `workspace` (allocated
     here unless given)."""
     torch = _torch()
-    B, Lq, Hq, Dqk = q.shape
-    Lk, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
+    _check_out(o, lse, B, Lq, Hq, Dv)
     if scale is None:
         scale = Dqk ** -0.5
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv)
     if workspace is None:
-        workspace = torch.empty(attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv),
-                                dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _bytes_at_least(workspace, "workspace", need)
+    _one_device([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("workspace", workspace)])
     st = load_library().attn_fwd_decode(
         _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
         _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
@@ -285,10 +363,16 @@ def _int_ptr(a, name):
 
 def attn_fwd_blocksparse(q, k, v, o, blk_ptr, blk_idx, col_ptr, col_idx, lse=None, causal=True,
                          scale=None, block_m=64, block_n=64, stream=None):
-    """Block-sparse forward over CSR lists (int32 GPU tensors, layout in include/attn.h)."""
-    B, Lq, Hq, Dqk = q.shape
-    Lk, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    """Block-sparse forward over CSR lists (int32 GPU tensors, layout in include/attn.h).
+
+    The list contents are read on the GPU and not checked here (attn_blocksparse_check checks
+    host copies); their pointer arrays must have the sizes the layout fixes."""
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
+    _check_out(o, lse, B, Lq, Hq, Dv)
+    _numel(blk_ptr, "blk_ptr", B * Hq * (-(-Lq // 64)) + 1)
+    _numel(col_ptr, "col_ptr", B * Hq + 1)
+    _one_device([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("blk_ptr", blk_ptr),
+                 ("blk_idx", blk_idx), ("col_ptr", col_ptr), ("col_idx", col_idx)])
     if scale is None:
         scale = Dqk ** -0.5
     st = load_library().attn_fwd_blocksparse(
@@ -321,14 +405,20 @@ def attn_fwd_vertical_slash(q, k, v, o, blk_ptr, blk_idx, col_ptr, col_idx, slas
     """Block-sparse forward with per-head slash lines added to the union (int32 GPU tensors,
     layout in include/attn.h). Allocates the bitmap workspace with torch unless given."""
     torch = _torch()
-    B, Lq, Hq, Dqk = q.shape
-    Lk, Hkv = k.shape[1], k.shape[2]
-    Dv = v.shape[3]
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
+    _check_out(o, lse, B, Lq, Hq, Dv)
+    _numel(blk_ptr, "blk_ptr", B * Hq * (-(-Lq // 64)) + 1)
+    _numel(col_ptr, "col_ptr", B * Hq + 1)
+    _numel(slash_ptr, "slash_ptr", B * Hq + 1)
     if scale is None:
         scale = Dqk ** -0.5
     wsb = attn_vertical_slash_workspace_bytes(B, Hq, Lk)
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _bytes_at_least(workspace, "workspace", wsb)
+    _one_device([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("blk_ptr", blk_ptr),
+                 ("blk_idx", blk_idx), ("col_ptr", col_ptr), ("col_idx", col_idx),
+                 ("slash_ptr", slash_ptr), ("slash_idx", slash_idx), ("workspace", workspace)])
     st = load_library().attn_fwd_vertical_slash(
         _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
         _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
@@ -369,24 +459,32 @@ def attn_build_sparse_index(q, k, topk_blocks, n_cols, scale=None, outputs=None,
     estimator (see include/attn.h). Allocates the outputs and the workspace with torch unless
     given."""
     torch = _torch()
-    B, L, Hq, D = q.shape
+    B, L, Hq, D = _index_qk_sizes(q, k)
     Hkv = k.shape[2]
     if scale is None:
         scale = D ** -0.5
     nb, nc = attn_sparse_index_sizes(B, Hq, L, topk_blocks, n_cols)
+    nqb = -(-L // 64)
     if outputs is None:
-        nqb = -(-L // 64)
         mk = lambda n: torch.empty(max(int(n), 1), dtype=torch.int32, device=q.device)
         outputs = (mk(B * Hq * nqb + 1), mk(nb), mk(B * Hq + 1), mk(nc))
     blk_ptr, blk_idx, col_ptr, col_idx = outputs
+    _numel(blk_ptr, "blk_ptr", B * Hq * nqb + 1)
+    _numel_at_least(blk_idx, "blk_idx", nb)
+    _numel(col_ptr, "col_ptr", B * Hq + 1)
+    _numel_at_least(col_idx, "col_idx", nc)
     wsb = attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D)
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _bytes_at_least(workspace, "workspace", wsb)
+    _one_device([("q", q), ("k", k), ("blk_ptr", blk_ptr), ("blk_idx", blk_idx),
+                 ("col_ptr", col_ptr), ("col_idx", col_idx), ("workspace", workspace)])
     st = load_library().attn_build_sparse_index(
         _tensor_desc(q, "q"), _tensor_desc(k, "k"), B, Hq, Hkv, L, D, float(scale),
         int(topk_blocks), int(n_cols), _int_ptr(blk_ptr, "blk_ptr"), _int_ptr(blk_idx, "blk_idx"),
         _int_ptr(col_ptr, "col_ptr"), _int_ptr(col_idx, "col_idx"),
-        ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(stream, q.device))
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device))
     _check("attn_build_sparse_index", st)
     return blk_ptr, blk_idx[:nb], col_ptr, col_idx[:nc]
 
@@ -398,23 +496,31 @@ def attn_build_vslash_index(q, k, n_cols, n_slash, scale=None, outputs=None, wor
     with the library's probe (see include/attn.h). Allocates the outputs and the workspace
     with torch unless given."""
     torch = _torch()
-    B, L, Hq, D = q.shape
+    B, L, Hq, D = _index_qk_sizes(q, k)
     Hkv = k.shape[2]
     if scale is None:
         scale = D ** -0.5
-    nc = B * Hq * min(int(n_cols), L)
-    ns = B * Hq * min(int(n_slash), L)
+    nc = B * Hq * min(max(int(n_cols), 0), L)
+    ns = B * Hq * min(max(int(n_slash), 0), L)
     if outputs is None:
         mk = lambda n: torch.empty(max(int(n), 1), dtype=torch.int32, device=q.device)
         outputs = (mk(B * Hq + 1), mk(nc), mk(B * Hq + 1), mk(ns))
     col_ptr, col_idx, slash_ptr, slash_idx = outputs
+    _numel(col_ptr, "col_ptr", B * Hq + 1)
+    _numel_at_least(col_idx, "col_idx", nc)
+    _numel(slash_ptr, "slash_ptr", B * Hq + 1)
+    _numel_at_least(slash_idx, "slash_idx", ns)
     wsb = attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D)
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    _bytes_at_least(workspace, "workspace", wsb)
+    _one_device([("q", q), ("k", k), ("col_ptr", col_ptr), ("col_idx", col_idx),
+                 ("slash_ptr", slash_ptr), ("slash_idx", slash_idx), ("workspace", workspace)])
     st = load_library().attn_build_vslash_index(
         _tensor_desc(q, "q"), _tensor_desc(k, "k"), B, Hq, Hkv, L, D, float(scale), int(n_cols),
         int(n_slash), _int_ptr(col_ptr, "col_ptr"), _int_ptr(col_idx, "col_idx"),
         _int_ptr(slash_ptr, "slash_ptr"), _int_ptr(slash_idx, "slash_idx"),
-        ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), _stream(stream, q.device))
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device))
     _check("attn_build_vslash_index", st)
     return col_ptr, col_idx[:nc], slash_ptr, slash_idx[:ns]

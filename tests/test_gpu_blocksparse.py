@@ -169,7 +169,8 @@ def test_blocksparse_workload_full_size_sampled_rows(sparse128k, group):
             got_l.append(lf[h, sel])
             ref_l.append(lrow)
     check_parity(np.concatenate(got_o), np.concatenate(ref_o), np.concatenate(got_l),
-                 np.concatenate(ref_l), f"sparse128k 4096 rows, heads {8 * group}-{8 * group + 7}")
+                 np.concatenate(ref_l), f"sparse128k 4096 rows, heads {8 * group}-{8 * group + 7}",
+                 record="blocksparse_128k")
 
 
 def test_blocksparse_deterministic():

@@ -25,19 +25,52 @@ def _run(q, k, v, causal, scale, ws=None):
     return o, lse
 
 
-def _check(q, k, v, causal, scale, label, ws=None, mla=False):
+def _check(q, k, v, causal, scale, label, ws=None, mla=False, record=None):
     kd = k.to(DEV)
     o, lse = _run(q.to(DEV), kd, kd[..., :512] if mla else v.to(DEV), causal, scale, ws)
     vf = A.mla_value_view(to_f64(k), 512) if mla else to_f64(v)
     o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), vf, A.effective_scale(scale), causal)
-    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, label)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, label, record=record)
+
+
+def _splits(q, k, v):
+    import sparse_attention_attn_amd as S
+    B, Lq, Hq, Dqk = q.shape
+    return S.attn_splitkv_num_splits(B, Hq, k.shape[2], Lq, k.shape[1], Dqk, v.shape[3])
 
 
 def test_decode_one_call_gqa_workload():
+    """The batched GQA decode workload at full size, through the call the bench times."""
     w = WORKLOADS["gqa_decode_4k"]
     say(f"one-call decode {w.name}")
     q, k, v = make_qkv(w)
-    _check(q, k, v, False, w.scale, "one-call gqa_decode_4k")
+    _check(q, k, v, False, w.scale, "one-call gqa_decode_4k", record="gqa_decode_4k")
+
+
+def test_decode_one_call_mla_workload():
+    """The MLA decode workload at full size (B 8, 16 heads, 65536 latent keys), through the
+    call the bench times."""
+    w = WORKLOADS["mla_decode_64k"]
+    say(f"one-call decode {w.name}")
+    q, k, _ = make_qkv(w)
+    _check(q, k, None, False, w.scale, "one-call mla_decode_64k", mla=True,
+           record="mla_decode_64k")
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 1, 2, 300, 576, 512, True),
+                                   (2, 8, 2, 1, 300, 64, 64, False)],
+                         ids=["mla_lq2_two_colblocks", "d64"])
+def test_decode_one_call_direct_path(shape):
+    """One split: the split kernel writes O and LSE itself. The MLA shape with two query tokens
+    (32 query columns, two 16-column blocks writing O) and D = 64 reach that path too."""
+    B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal = shape
+    say(f"one-call decode direct {shape}")
+    q = randn_bf16((B, Lq, Hq, Dqk), 8800 + Dqk)
+    k = randn_bf16((B, Lk, Hkv, Dqk), 8801 + Dqk)
+    mla = Dqk == 576
+    v = None if mla else randn_bf16((B, Lk, Hkv, Dv), 8802 + Dqk)
+    assert _splits(q, k, k[..., :512] if mla else v) == 1
+    _check(q, k, v, causal, (192 if mla else Dqk) ** -0.5, f"direct {shape}", mla=mla)
 
 
 SHAPES = [

@@ -34,8 +34,9 @@ def _replays_match(run, outs, label):
         del noise
 
 
-@pytest.mark.parametrize("shape", [(16, 32, 8, 1, 4096, 128, 128), (4, 16, 1, 2, 3000, 576, 512)],
-                         ids=["gqa", "mla"])
+@pytest.mark.parametrize("shape", [(16, 32, 8, 1, 4096, 128, 128), (4, 16, 1, 2, 3000, 576, 512),
+                                   (2, 16, 4, 2, 300, 128, 128)],
+                         ids=["gqa", "mla", "one_split_direct"])
 def test_decode_graph_replays_equal_eager(shape):
     import torch
     import sparse_attention_attn_amd as S
@@ -46,8 +47,10 @@ def test_decode_graph_replays_equal_eager(shape):
     v = k[..., :Dv] if Dqk != Dv else randn_bf16((B, Lk, Hkv, Dv), 8952).to(DEV)
     o = torch.empty((B, Lq, Hq, Dv), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=DEV)
-    ws = torch.empty(S.attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv),
+    ws = torch.empty(max(256, S.attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv)),
                      dtype=torch.uint8, device=DEV)
+    if Lk < 512:
+        assert S.attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, Dqk, Dv) == 1
     _replays_match(lambda: S.attn_fwd_decode(q, k, v, o, lse, causal=Lq > 1, workspace=ws),
                    [o, lse], f"decode {shape}")
 

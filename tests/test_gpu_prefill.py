@@ -36,7 +36,7 @@ def test_tiny_causal_workload_full():
     q, k, v = make_qkv(w)
     o, lse = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, w.scale)
     o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(w.scale), True)
-    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "tiny_causal")
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, "tiny_causal", record="tiny_causal")
 
 
 SHAPES = [
@@ -87,25 +87,24 @@ def test_prefill_strided_packed_qkv():
     assert float(obuf[:, :, 0].abs().max()) == 0.0 and float(obuf[:, :, 1 + Hq:].abs().max()) == 0.0
 
 
-def test_gqa_prefill_8k_full_size_sampled_rows():
-    """The Llama-3-8B-shaped workload at full size; the oracle checks 96 sampled rows of every
-    query head (first 32, last 32, 32 seeded)."""
+def test_gqa_prefill_8k_full_size_all_rows():
+    """The Llama-3-8B-shaped workload at full size, every element of O and LSE (all 8192 rows
+    of all 32 query heads) against the fp64 oracle, one head at a time."""
     w = WORKLOADS["gqa_prefill_8k"]
     say(f"gqa_prefill_8k full size {w}")
     q, k, v = make_qkv(w)
     o, lse = _run_fwd(q.to(DEV), k.to(DEV), v.to(DEV), True, w.scale)
-    rows = sampled_rows(w.Lq, 96, 1000 * w.index + 4, edge=32)
+    rows = np.arange(w.Lq)
     qf, kf, vf = to_f64(q), to_f64(k), to_f64(v)
     of, lf = to_f64(o), to_f64(lse)
     sc = A.effective_scale(w.scale)
-    got_o, ref_o, got_l, ref_l = [], [], [], []
+    got_o = np.empty((w.Hq, w.Lq, w.Dv))
+    ref_o = np.empty((w.Hq, w.Lq, w.Dv))
+    ref_l = np.empty((w.Hq, w.Lq))
     for h in range(w.Hq):
-        orow, lrow = A.attention_rows(qf, kf, vf, sc, True, 0, h, rows)
-        got_o.append(of[0, rows, h, :])
-        ref_o.append(orow)
-        got_l.append(lf[0, h, rows])
-        ref_l.append(lrow)
-    check_parity(np.stack(got_o), np.stack(ref_o), np.stack(got_l), np.stack(ref_l), "gqa_8k")
+        ref_o[h], ref_l[h] = A.attention_rows(qf, kf, vf, sc, True, 0, h, rows)
+        got_o[h] = of[0, :, h, :]
+    check_parity(got_o, ref_o, lf[0], ref_l, "gqa_8k all rows", record="gqa_prefill_8k")
 
 
 def test_closed_forms_on_gpu():
