@@ -132,6 +132,32 @@ int attn_fwd_decode(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tens
 /* Workspace bytes of attn_fwd_decode for these sizes (0 on invalid sizes). */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
+/* Size of the library's per-device scratch array used by attn_fwd_decode_noalloc (16 MiB). */
+#define ATTN_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_fwd_decode_noalloc — attn_fwd_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc. It
+ * computes exactly what attn_fwd_decode computes (same kernels, same split count, bitwise the
+ * same O and LSE), but the split-KV partials go to a scratch array that the library holds in
+ * device memory, ATTN_DECODE_SCRATCH_BYTES per GPU, kept from the first call on that GPU until
+ * the process ends. The call allocates nothing; the caller still passes inputs and outputs as
+ * for attn_fwd_decode.
+ * The scratch belongs to the GPU that runs `stream` (the current device for the NULL stream);
+ * its address is looked up once per GPU, on that GPU's first call.
+ * Concurrency: every call on one GPU shares that GPU's scratch, which keeps the last call's
+ * partials. Calls on one stream are ordered and safe; calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race and may return
+ * wrong results.
+ * Errors: as attn_fwd_decode, with WORKSPACE when these sizes need more than one split and
+ * attn_decode_workspace_bytes(...) exceeds ATTN_DECODE_SCRATCH_BYTES (use attn_fwd_decode
+ * with a workspace then), and LAUNCH when the scratch address cannot be looked up. A call
+ * with one split needs no partials and takes any size.
+ */
+int attn_fwd_decode_noalloc(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                            float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                            int causal, float scale, void* stream);
+
 /*
  * attn_fwd_blocksparse — attention over a per-query-head union of listed key blocks and
  * vertical key columns (the block-sparse / A-shape / vertical-slash index lists), with the

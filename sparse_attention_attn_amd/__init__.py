@@ -24,6 +24,8 @@ from ._lib import (  # noqa: F401
     attn_combine_lse,
     attn_fwd_decode,
     attn_decode_workspace_bytes,
+    attn_fwd_decode_noalloc,
+    ATTN_DECODE_SCRATCH_BYTES,
     attn_fwd_blocksparse,
     attn_splitkv_num_splits,
     attn_splitkv_workspace_bytes,

@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "attn_combine_lse",
     "attn_fwd_decode",
     "attn_decode_workspace_bytes",
+    "attn_fwd_decode_noalloc",
     "attn_fwd_blocksparse",
     "attn_blocksparse_check",
     "attn_fwd_vertical_slash",
@@ -91,6 +92,9 @@ def load_library():
     lib.attn_fwd_decode.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                     vp, ctypes.c_size_t, vp]
     lib.attn_fwd_decode.restype = i32
+    lib.attn_fwd_decode_noalloc.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, vp]
+    lib.attn_fwd_decode_noalloc.restype = i32
     lib.attn_decode_workspace_bytes.argtypes = [i32] * 7
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fwd_blocksparse.argtypes = [T, T, T, T, vp, i32, i32, i32, i32, i32, i32, i32, i32,
@@ -350,6 +354,26 @@ def attn_fwd_decode(q, k, v, o, lse=None, causal=False, scale=None, workspace=No
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
         _stream(stream, q.device))
     _check("attn_fwd_decode", st)
+    return o
+
+
+# Size of the library's per-device scratch array (ATTN_DECODE_SCRATCH_BYTES in include/attn.h).
+ATTN_DECODE_SCRATCH_BYTES = 16 << 20
+
+
+def attn_fwd_decode_noalloc(q, k, v, o, lse=None, causal=False, scale=None, stream=None):
+    """attn_fwd_decode with the partials in the library's per-device scratch array: allocates
+    nothing (for callers that cannot allocate). Calls that overlap on one GPU race."""
+    B, Lq, Hq, Dqk, Lk, Hkv, Dv = _qkv_sizes(q, k, v)
+    _check_out(o, lse, B, Lq, Hq, Dv)
+    _one_device([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)])
+    if scale is None:
+        scale = Dqk ** -0.5
+    st = load_library().attn_fwd_decode_noalloc(
+        _tensor_desc(q, "q"), _tensor_desc(k, "k"), _tensor_desc(v, "v"), _tensor_desc(o, "o"),
+        _opt_ptr(lse, "lse"), B, Hq, Hkv, Lq, Lk, Dqk, Dv, int(bool(causal)), float(scale),
+        _stream(stream, q.device))
+    _check("attn_fwd_decode_noalloc", st)
     return o
 
 

@@ -5,6 +5,7 @@
 #include <cfloat>
 #include <cmath>
 #include <exception>
+#include <mutex>
 #include <sstream>
 #include <string>
 
@@ -54,6 +55,95 @@ void fill_fwd(attn::FwdArgs& a, const attn_tensor_t& q, const attn_tensor_t& k,
   a.sl_ptr = a.sl_idx = nullptr;
   a.sl_bits = a.cl_bits = nullptr;
   a.bits_words = 0;
+}
+
+// Split-KV decode into a checked workspace `wb` laid out by `ws`: the split kernel, then the
+// combine (or the split kernel alone writing O and LSE when there is one split).
+int decode_launch(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k,
+                  const attn_tensor_t& v, const attn_tensor_t& o, float* lse, int B, int Hq,
+                  int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal, float scale, char* wb,
+                  const attn::DecodeWorkspace& ws, hipStream_t sm) {
+  attn::SplitArgs a;
+  a.q = static_cast<const uint16_t*>(q.data);
+  a.k = static_cast<const uint16_t*>(k.data);
+  a.v = static_cast<const uint16_t*>(v.data);
+  a.o_part = reinterpret_cast<float*>(wb + ws.o_part);
+  a.lse_part = reinterpret_cast<float*>(wb + ws.lse_part);
+  a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
+  a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
+  a.v_sb = v.stride_b; a.v_sl = v.stride_l; a.v_sh = v.stride_h;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.off = Lk - Lq;
+  exp2_scale(scale, a.sl2, a.qsign);
+  a.num_splits = ws.num_splits;
+  a.chunk = attn::split_chunk(Lk, ws.num_splits);
+  const int cols = attn::split_cols(Dqk, a.g * Lq);
+  a.ncolblk = (a.g * Lq + cols - 1) / cols;
+  // One split: the split kernel writes O and LSE itself (the combine would only copy them).
+  const bool direct = ws.num_splits == 1;
+  a.o = direct ? static_cast<uint16_t*>(o.data) : nullptr;
+  a.o_sb = o.stride_b; a.o_sl = o.stride_l; a.o_sh = o.stride_h;
+  a.lse = direct ? lse : nullptr;
+  int st = launch_status(fn, attn::launch_splitkv(a, Dqk, Dv, sm));
+  if (st != ATTN_OK || direct) return st;
+  attn::CombineArgs c;
+  c.o_part = a.o_part;
+  c.lse_part = a.lse_part;
+  c.o = static_cast<uint16_t*>(o.data);
+  c.lse = lse;
+  c.o_sb = o.stride_b; c.o_sl = o.stride_l; c.o_sh = o.stride_h;
+  c.B = B; c.Hq = Hq; c.Lq = Lq; c.S = ws.num_splits;
+  return launch_status(fn, attn::launch_combine(c, Dv, sm));
+}
+
+}  // namespace
+
+// Scratch of attn_fwd_decode_noalloc: the split-KV partials of callers that cannot allocate.
+// In host code this name only stands in for the array; each device holds its own copy at its
+// own address, which scratch_for_stream looks up once per device (hipGetSymbolAddress).
+static __device__ __align__(256) char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, set once
+
+// Device address of `scratch` on the device that runs `stream` (the current device for the
+// null stream). The first call on a device looks it up with that device current.
+int scratch_for_stream(const char* fn, hipStream_t stream, char** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return attn::fail(ATTN_ERR_LAUNCH, fn, hipGetErrorString(e));
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return attn::fail(ATTN_ERR_LAUNCH, fn, hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    std::ostringstream m;
+    m << "device " << dev << " is beyond the " << kMaxDevices << " devices the scratch table holds";
+    return attn::fail(ATTN_ERR_UNSUPPORTED, fn, m.str());
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return attn::fail(ATTN_ERR_LAUNCH, fn, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || p == nullptr) {
+      std::ostringstream m;
+      m << "hipGetSymbolAddress of the scratch array failed on device " << dev << ": "
+        << (e != hipSuccess ? hipGetErrorString(e) : "null address");
+      return attn::fail(ATTN_ERR_LAUNCH, fn, m.str());
+    }
+    if (e2 != hipSuccess) return attn::fail(ATTN_ERR_LAUNCH, fn, hipGetErrorString(e2));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -146,40 +236,38 @@ int attn_fwd_decode(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tens
       m << "workspace must be non-NULL, 256-byte aligned and at least " << ws.total << " bytes";
       return attn::fail(ATTN_ERR_WORKSPACE, fn, m.str());
     }
-    char* wb = static_cast<char*>(workspace);
-    attn::SplitArgs a;
-    a.q = static_cast<const uint16_t*>(q.data);
-    a.k = static_cast<const uint16_t*>(k.data);
-    a.v = static_cast<const uint16_t*>(v.data);
-    a.o_part = reinterpret_cast<float*>(wb + ws.o_part);
-    a.lse_part = reinterpret_cast<float*>(wb + ws.lse_part);
-    a.q_sb = q.stride_b; a.q_sl = q.stride_l; a.q_sh = q.stride_h;
-    a.k_sb = k.stride_b; a.k_sl = k.stride_l; a.k_sh = k.stride_h;
-    a.v_sb = v.stride_b; a.v_sl = v.stride_l; a.v_sh = v.stride_h;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.g = Hq / Hkv;
-    a.causal = causal ? 1 : 0;
-    a.off = Lk - Lq;
-    exp2_scale(scale, a.sl2, a.qsign);
-    a.num_splits = ws.num_splits;
-    a.chunk = attn::split_chunk(Lk, ws.num_splits);
-    const int cols = attn::split_cols(Dqk, a.g * Lq);
-    a.ncolblk = (a.g * Lq + cols - 1) / cols;
+    return decode_launch(fn, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal, scale,
+                         static_cast<char*>(workspace), ws, static_cast<hipStream_t>(stream));
+  } catch (const std::exception& e) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
+  } catch (...) {
+    return attn::fail(ATTN_ERR_LAUNCH, fn, "unknown exception");
+  }
+}
+
+int attn_fwd_decode_noalloc(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
+                            float* lse, int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv,
+                            int causal, float scale, void* stream) {
+  static const char* fn = "attn_fwd_decode_noalloc";
+  try {
+    attn::clear_last_error();
+    int st = attn::check_attention_args(fn, attn::Op::kSplit, q, k, v, &o, lse, B, Hq, Hkv, Lq,
+                                        Lk, Dqk, Dv, scale);
+    if (st != ATTN_OK) return st;
+    const attn::DecodeWorkspace ws = attn::decode_workspace(B, Hq, Hkv, Lq, Lk, Dqk, Dv);
+    // With one split the split kernel writes O and LSE directly and no partials exist.
+    if (ws.num_splits > 1 && ws.total > (size_t)ATTN_DECODE_SCRATCH_BYTES) {
+      std::ostringstream m;
+      m << "these sizes need " << ws.total << " bytes of split-KV partials, more than the "
+        << ATTN_DECODE_SCRATCH_BYTES << "-byte scratch array; call attn_fwd_decode with a "
+        << "workspace instead";
+      return attn::fail(ATTN_ERR_WORKSPACE, fn, m.str());
+    }
     hipStream_t sm = static_cast<hipStream_t>(stream);
-    // One split: the split kernel writes O and LSE itself (the combine would only copy them).
-    const bool direct = ws.num_splits == 1;
-    a.o = direct ? static_cast<uint16_t*>(o.data) : nullptr;
-    a.o_sb = o.stride_b; a.o_sl = o.stride_l; a.o_sh = o.stride_h;
-    a.lse = direct ? lse : nullptr;
-    st = launch_status(fn, attn::launch_splitkv(a, Dqk, Dv, sm));
-    if (st != ATTN_OK || direct) return st;
-    attn::CombineArgs c;
-    c.o_part = a.o_part;
-    c.lse_part = a.lse_part;
-    c.o = static_cast<uint16_t*>(o.data);
-    c.lse = lse;
-    c.o_sb = o.stride_b; c.o_sl = o.stride_l; c.o_sh = o.stride_h;
-    c.B = B; c.Hq = Hq; c.Lq = Lq; c.S = ws.num_splits;
-    return launch_status(fn, attn::launch_combine(c, Dv, sm));
+    char* wb = nullptr;
+    if ((st = scratch_for_stream(fn, sm, &wb)) != ATTN_OK) return st;
+    return decode_launch(fn, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal, scale, wb, ws,
+                         sm);
   } catch (const std::exception& e) {
     return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
   } catch (...) {
