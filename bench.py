@@ -464,6 +464,82 @@ def cpu_baseline(w, budget_s):
                       f"{w.name}, all visible keys, fp64 numpy; {el:.1f} s"}
 
 
+def oracle_timings(threads_all, budget_s=15.0):
+    """The fp64 oracle, as it stands, timed on the other workloads (beside the headline entry of
+    cpu_baseline): the tiny causal prefill, the GQA decode and the MLA decode in full, each on
+    all host threads and on one thread; the 128K block-sparse prefill on its 4096 sampled query
+    rows (rows 0-63, the last 64 and 3968 seeded rows) of all 32 heads, each query block's rows
+    over that block's listed keys, with a x32 linear extrapolation to all 131072 rows labelled
+    as such. Rates use the GPU rows' algorithmic counts: TFLOP/s of visible pairs for prefill,
+    GB/s of K/V (+ Q, O, LSE) bytes for decode."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as A
+    from workloads import WORKLOADS, make_blocksparse_lists, make_qkv, sampled_rows
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    out = []
+
+    def run_full(w, threads):
+        q, k, v = make_qkv(w)
+        qf, kf = f64(q), f64(k)
+        vf = A.mla_value_view(kf, w.Dv) if w.mla else f64(v)
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            A.attention(qf, kf, vf, A.effective_scale(w.scale), w.causal)
+            el = time.perf_counter() - t0
+        rec = {"workload": w.name, "threads": threads, "seconds": round(el, 3),
+               "sample": "whole workload"}
+        if w.kind == "prefill":
+            fl = 2 * (w.Dqk + w.Dv) * w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, w.causal)
+            rec.update({"value": fl / el / 1e12, "unit": "TFLOP/s"})
+        else:
+            nbytes = k.numel() * 2 + (0 if w.mla else v.numel() * 2) + q.numel() * 2 + \
+                w.B * w.Lq * w.Hq * w.Dv * 2 + w.B * w.Hq * w.Lq * 4
+            rec.update({"value": nbytes / el / 1e9, "unit": "GB/s"})
+        return rec
+
+    for name in ("tiny_causal", "gqa_decode_4k", "mla_decode_64k"):
+        for th in sorted({threads_all, 1}, reverse=True):
+            out.append(run_full(WORKLOADS[name], th))
+            log(f"  oracle {out[-1]}")
+
+    w = WORKLOADS["blocksparse_128k"]
+    q, k, v = make_qkv(w)
+    bp, bi, cp, ci = make_blocksparse_lists(w.B, w.Hq, w.Lq, w.Lk, 1000 * w.index + 3)
+    rows = sampled_rows(w.Lq, 4096, 1000 * w.index + 4, edge=64)
+    nqb = -(-w.Lq // 64)
+    sc = A.effective_scale(w.scale)
+    qbs = rows // 64
+    pairs = 0
+    el = 0.0
+    heads = 0
+    for h in range(w.Hq):
+        if el >= budget_s:
+            break
+        heads += 1
+        kh = f64(k[0, :, h // (w.Hq // w.Hkv)])
+        vh = f64(v[0, :, h // (w.Hq // w.Hkv)])
+        qh = f64(q[0, rows, h])
+        cols = ci[cp[h]:cp[h + 1]]
+        t0 = time.perf_counter()
+        for qb in np.unique(qbs):
+            sel = qbs == qb
+            keys = A.blocksparse_keys(bi[bp[h * nqb + qb]:bp[h * nqb + qb + 1]], cols, w.Lk)
+            A.attention_rows_over_keys(qh[sel], rows[sel], kh, vh, sc, keys, w.Lq, w.Lk, True)
+            pairs += int(np.sum(np.searchsorted(keys, rows[sel], side="right")))
+        el += time.perf_counter() - t0
+    fl = 2 * (w.Dqk + w.Dv) * pairs
+    out.append({"workload": w.name, "threads": threads_all, "seconds": round(el, 3),
+                "value": fl / el / 1e12, "unit": "TFLOP/s",
+                "sample": f"{len(rows)} of {w.Lq} query rows x {heads} of {w.Hq} heads, over "
+                          f"each query block's listed keys ({pairs} visible pairs)",
+                "extrapolated_seconds_whole_workload": round(
+                    el * (w.Lq / len(rows)) * (w.Hq / heads), 1),
+                "extrapolation": f"linear: x{w.Lq // len(rows)} rows, x{w.Hq / heads:g} heads"})
+    log(f"  oracle {out[-1]}")
+    return out
+
+
 # ------------------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -479,6 +555,8 @@ def main():
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the bf16 GEMM / device copy measurement of achievable peaks")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-oracle-others", action="store_true",
+                    help="time the oracle on the headline workload only")
     ap.add_argument("--min-warmup-ms", type=float, default=300.0,
                     help="keep warming up (untimed) until this much wall time has passed")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -590,6 +668,9 @@ def main():
     if not args.no_cpu_baseline and HEADLINE in res:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
+        if not args.no_oracle_others:
+            log("oracle on the other workloads ...")
+            out["cpu_baseline"]["other_workloads"] = oracle_timings(out["cpu_baseline"]["cores"])
     print(json.dumps(out), flush=True)
 
 
