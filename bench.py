@@ -430,6 +430,129 @@ def bench_memory(lengths, eager_max):
     return out
 
 
+def bench_crossover(lengths, topk=96, n_cols=1000, steps=3, warmup=2):
+    """Dense causal attention (attn_fwd) against the dynamic sparse path (attn_build_sparse_index
+    then attn_fwd_blocksparse on the built lists) as the sequence grows, at B 1, Hq 32, Hkv 8,
+    D 128, with the index budget of the 128K workload at every length (96 key blocks per query
+    block, 1000 columns per head). Inputs: seeded device N(0, 1) in bf16."""
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import randn_bf16_device
+    B, Hq, Hkv, D = 1, 32, 8, 128
+    scale = D ** -0.5
+    out = []
+    for L in lengths:
+        q = randn_bf16_device((B, L, Hq, D), 7000 + L)
+        k = randn_bf16_device((B, L, Hkv, D), 7001 + L)
+        v = randn_bf16_device((B, L, Hkv, D), 7002 + L)
+        o = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device="cuda:0")
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda:0")
+        ms_dense, _ = time_steps(lambda: S.attn_fwd(q, k, v, o, lse, causal=True, scale=scale),
+                                 steps, warmup)
+        nb, nc = S.attn_sparse_index_sizes(B, Hq, L, topk, n_cols)
+        nqb = -(-L // 64)
+        outs = (torch.empty(B * Hq * nqb + 1, dtype=torch.int32, device="cuda:0"),
+                torch.empty(max(nb, 1), dtype=torch.int32, device="cuda:0"),
+                torch.empty(B * Hq + 1, dtype=torch.int32, device="cuda:0"),
+                torch.empty(max(nc, 1), dtype=torch.int32, device="cuda:0"))
+        ws = torch.empty(S.attn_sparse_index_workspace_bytes(B, Hq, Hkv, L, D), dtype=torch.uint8,
+                         device="cuda:0")
+        build = lambda: S.attn_build_sparse_index(q, k, topk, n_cols, scale=scale, outputs=outs,
+                                                  workspace=ws)
+        ms_build, _ = time_steps(build, steps, warmup)
+        lists = build()
+        ms_sparse, _ = time_steps(lambda: S.attn_fwd_blocksparse(q, k, v, o, *lists, lse=lse,
+                                                                 causal=True, scale=scale),
+                                  steps, warmup)
+        torch.cuda.synchronize()
+        hl = [t.cpu().numpy() for t in lists]
+        pairs = blocksparse_pairs(hl, B, Hq, L)
+        dense_pairs = B * Hq * dense_causal_pairs(L, L, True)
+        rec = {"L": L, "dense_ms": round(ms_dense, 4), "build_ms": round(ms_build, 4),
+               "sparse_ms": round(ms_sparse, 4),
+               "build_plus_sparse_ms": round(ms_build + ms_sparse, 4),
+               "density_vs_causal": round(pairs / dense_pairs, 4),
+               "speedup_vs_dense": round(ms_dense / (ms_build + ms_sparse), 3)}
+        out.append(rec)
+        log(f"  crossover {rec}")
+        del q, k, v, o, lse, outs, ws, lists
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_entry_memory():
+    """Peak device memory of the other entry points at long context, above the op's inputs and
+    outputs, with the workspaces the binding allocates for the call counted (torch's peak
+    counter; the library itself allocates nothing): block-sparse, vertical-slash and both index
+    builders at the 128K workloads' shape, the GQA decode and the MLA decode at 131072 keys."""
+    import numpy as np
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import make_blocksparse_lists, make_vslash_lists, randn_bf16_device
+    dev = "cuda:0"
+    out = []
+
+    def measure(name, tensors, fn, note):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        fn()
+        torch.cuda.synchronize()
+        extra = torch.cuda.max_memory_allocated() - base
+        io = sum(t.numel() * t.element_size() for t in tensors)
+        rec = {"entry": name, "inputs_outputs_bytes": int(io), "extra_bytes": int(extra),
+               "note": note}
+        out.append(rec)
+        log(f"  entry memory {rec}")
+
+    B, Hq, Hkv, L, D = 1, 32, 8, 131072, 128
+    q = randn_bf16_device((B, L, Hq, D), 8100)
+    k = randn_bf16_device((B, L, Hkv, D), 8101)
+    v = randn_bf16_device((B, L, Hkv, D), 8102)
+    o = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    bl = [torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+          for x in make_blocksparse_lists(B, Hq, L, L, 5003)]
+    measure("attn_fwd_blocksparse", [q, k, v, o, lse] + bl,
+            lambda: S.attn_fwd_blocksparse(q, k, v, o, *bl, lse=lse, causal=True),
+            "B 1, Hq 32, Hkv 8, D 128, L 131072; index lists counted as inputs")
+    sp, si, cp, ci = [torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+                      for x in make_vslash_lists(B, Hq, L, 6003)]
+    nqb = -(-L // 64)
+    bp0 = torch.zeros(B * Hq * nqb + 1, dtype=torch.int32, device=dev)
+    bi0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    measure("attn_fwd_vertical_slash", [q, k, v, o, lse, sp, si, cp, ci, bp0, bi0],
+            lambda: S.attn_fwd_vertical_slash(q, k, v, o, bp0, bi0, cp, ci, sp, si, lse=lse),
+            "same shape; extra = the two per-head bitmaps of its workspace")
+    measure("attn_build_sparse_index", [q, k],
+            lambda: S.attn_build_sparse_index(q, k, 96, 1000),
+            "same shape, 96 blocks per query block, 1000 columns; extra = output lists + "
+            "workspace")
+    measure("attn_build_vslash_index", [q, k],
+            lambda: S.attn_build_vslash_index(q, k, 1000, 1088),
+            "same shape, 1000 columns, 1088 slash lines; extra = output lists + workspace")
+    del q, k, v, o, lse, bl, sp, si, cp, ci, bp0, bi0
+    torch.cuda.empty_cache()
+    for (Bd, Hqd, Hkvd, Dqk, Dv, name) in ((16, 32, 8, 128, 128, "GQA"), (8, 16, 1, 576, 512, "MLA")):
+        Lk = 131072
+        qd = randn_bf16_device((Bd, 1, Hqd, Dqk), 8200)
+        kd = randn_bf16_device((Bd, Lk, Hkvd, Dqk), 8201)
+        vd = kd[..., :Dv] if Dqk != Dv else randn_bf16_device((Bd, Lk, Hkvd, Dv), 8202)
+        od = torch.empty((Bd, 1, Hqd, Dv), dtype=torch.bfloat16, device=dev)
+        ld = torch.empty((Bd, Hqd, 1), dtype=torch.float32, device=dev)
+        ins = [qd, kd, od, ld] + ([] if Dqk != Dv else [vd])
+        measure(f"attn_fwd_decode ({name})", ins,
+                lambda: S.attn_fwd_decode(qd, kd, vd, od, ld),
+                f"B {Bd}, Hq {Hqd}, Hkv {Hkvd}, Dqk {Dqk}, Dv {Dv}, 131072 keys; extra = the "
+                "split-KV partials workspace")
+        measure(f"attn_fwd_decode_noalloc ({name})", ins,
+                lambda: S.attn_fwd_decode_noalloc(qd, kd, vd, od, ld),
+                "same shape; partials in the library's static scratch array")
+        del qd, kd, vd, od, ld
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, budget_s):
     """The fp64 oracle, as it stands, timed on a bounded sample of the headline workload:
@@ -552,6 +675,8 @@ def main():
                     help="skip the FlashMLA-ETAP decode grid sweep")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the peak-memory comparison at long sequence lengths")
+    ap.add_argument("--no-crossover", action="store_true",
+                    help="skip the dense vs dynamic sparse sweep over sequence length")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the bf16 GEMM / device copy measurement of achievable peaks")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -665,6 +790,16 @@ def main():
         out["memory"] = {"op": "causal prefill B 1, Hq 32, Hkv 8, D 128",
                          "points": bench_memory([4096, 8192, 16384, 32768, 65536, 131072],
                                                 eager_max=16384)}
+    if not args.no_crossover and args.only is None:
+        log("dense vs dynamic sparse crossover ...")
+        out["sparse_crossover"] = {
+            "op": "causal prefill B 1, Hq 32, Hkv 8, D 128: attn_fwd against "
+                  "attn_build_sparse_index + attn_fwd_blocksparse (96 blocks per query block, "
+                  "1000 columns per head at every length)",
+            "points": bench_crossover([4096, 8192, 16384, 32768, 65536, 131072])}
+    if not args.no_memory and args.only is None:
+        log("peak memory of the other entry points ...")
+        out["entry_memory"] = bench_entry_memory()
     if not args.no_cpu_baseline and HEADLINE in res:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(head, args.cpu_seconds)
