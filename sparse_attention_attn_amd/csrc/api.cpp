@@ -53,7 +53,7 @@ void fill_fwd(attn::FwdArgs& a, const attn_tensor_t& q, const attn_tensor_t& k,
   a.blk_ptr = a.blk_idx = a.col_ptr = a.col_idx = nullptr;
   a.nkb = (Lk + 63) / 64;
   a.sl_ptr = a.sl_idx = nullptr;
-  a.sl_bits = a.cl_bits = nullptr;
+  a.sl_bits = a.cl_bits = a.rl_bits = nullptr;
   a.bits_words = 0;
 }
 
@@ -372,6 +372,7 @@ int attn_fwd_vertical_slash(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, a
     uint32_t* bits = static_cast<uint32_t*>(workspace);
     a.sl_bits = bits;
     a.cl_bits = bits + (size_t)B * Hq * a.bits_words;
+    a.rl_bits = bits + 2 * (size_t)B * Hq * a.bits_words;
     return launch_status(fn, attn::launch_fwd_vslash(a, Dqk, static_cast<hipStream_t>(stream)));
   } catch (const std::exception& e) {
     return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());
@@ -382,7 +383,7 @@ int attn_fwd_vertical_slash(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, a
 
 size_t attn_vertical_slash_workspace_bytes(int B, int Hq, int Lk) {
   if (B < 1 || Hq < 1 || Lk < 1) return 0;
-  return 2 * (size_t)B * Hq * attn::vs_bits_words(Lk) * sizeof(uint32_t);
+  return attn::kVslashBitmaps * (size_t)B * Hq * attn::vs_bits_words(Lk) * sizeof(uint32_t);
 }
 
 int attn_vertical_slash_check(const int32_t* slash_ptr, const int32_t* slash_idx, int B, int Hq,

@@ -322,6 +322,101 @@ __device__ __forceinline__ void tile_math_mask(const FwdArgs& a, WaveState<D>& w
   __builtin_amdgcn_s_setprio(0);
 }
 
+// LDS slot of one wave in the window phase: the 32 key rows a wave's 32 query rows meet on one
+// slash line. K rows are stored unpadded with chunk c of row r at position c ^ swz(r), which
+// keeps the MFMA operand read (16 consecutive rows of one chunk per quarter wave) on distinct
+// banks; V rows use the padded row-major layout of the tiles. Two slots fit in a ring stage.
+template <int D>
+struct WinCfg {
+  using T = TileCfg<D>;
+  static constexpr int CPR = T::CPR;
+  static constexpr int KROW = 2 * D;                   // bytes per K row
+  static constexpr int KBYTES = 32 * KROW;
+  static constexpr int KINSTR = KBYTES / 1024;
+  static constexpr int VBYTES = 32 * T::VROW;
+  static constexpr int VINSTR = VBYTES / 1024;
+  static constexpr int BYTES = KBYTES + VBYTES;
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole copy instructions");
+  static_assert(2 * BYTES <= SpCfg<D>::STAGE_BYTES, "two window slots per ring stage");
+  static __device__ __forceinline__ uint32_t swz(uint32_t r) {
+    return D == 128 ? (r & 15u) : ((r >> 1) & 7u);
+  }
+};
+
+// One 32-key unit of the window phase: Sᵀ = K·Qᵀ over the wave's slot, every score but the
+// kept one set to -inf (keep_slot: the accumulator slot j of this lane that holds a visible key,
+// or -1), the weights, then Oᵀ += Vᵀ·Pᵀ.
+template <int D>
+__device__ __forceinline__ void window_unit(const FwdArgs& a, WaveState<D>& ws, uint32_t slot,
+                                            int keep_slot, int l) {
+  using W = WinCfg<D>;
+  using C = SpCfg<D>;
+  const uint32_t i = (uint32_t)(l & 31), h = (uint32_t)(l >> 5);
+  const uint32_t krow = slot + i * (uint32_t)W::KROW;
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int st = 0; st < C::KSTEPS; ++st) {
+    const uint32_t c = 2u * (uint32_t)st + h;
+    s = mfma32(lds_read_b128_at(krow + ((c ^ W::swz(i)) << 4)), ws.qop[st], s);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j != keep_slot) s[j] = -INFINITY;
+  const float sl2 = a.sl2;
+  float sb = ws.lb, sf = ws.lf;
+  uint32_t pk[2][4];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const float e0 = fast_exp2(fmaf(s[2 * g], sl2, -ws.mu));
+    const float e1 = fast_exp2(fmaf(s[2 * g + 1], sl2, -ws.mu));
+    sf += e0;
+    sf += e1;
+    pk[g >> 2][g & 3] = pack_bf16x2(e0, e1);
+    sb = add_bf16_pair(pk[g >> 2][g & 3], sb);
+  }
+  bf16x8 p[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    p[ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]));
+  if (__builtin_expect(__any(!unit_ok(ws.m, sf)), 0)) slow_unit<D>(ws, s, sl2, p, sb, sf);
+  ws.lb = sb;
+  ws.lf = sf;
+  const uint32_t vt = slot + (uint32_t)W::KBYTES + ws.vofs;
+#pragma unroll
+  for (int v = 0; v < 2 * C::DVB; ++v) {
+    const uint32_t o = vt + (16u * (uint32_t)(v / C::DVB)) * C::VROW + 64u * (uint32_t)(v % C::DVB);
+    ws.acc[v % C::DVB] = mfma32(lds_read_tr_pair_at(o, o + 8u * C::VROW), p[v / C::DVB],
+                                ws.acc[v % C::DVB]);
+  }
+}
+
+// Copies into a wave's window slot the K and V rows of keys k0 .. k0 + 31 (clamped into
+// [0, lkm1], so every load is in bounds; the clamped rows are masked by the caller).
+template <int D>
+__device__ __forceinline__ void issue_window(uint32_t slot, const uint16_t* kbase,
+                                             const uint16_t* vbase, uint32_t k_row_bytes,
+                                             uint32_t v_row_bytes, int k0, int lkm1, int l) {
+  using W = WinCfg<D>;
+  using C = SpCfg<D>;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot returned
+#pragma unroll
+  for (int i = 0; i < W::KINSTR; ++i) {
+    const uint32_t q = (uint32_t)i * 64u + (uint32_t)l;
+    const uint32_t r = q / W::CPR, pos = q % W::CPR;
+    const uint32_t c = pos ^ W::swz(r);
+    const int key = min(max(k0 + (int)r, 0), lkm1);
+    dma16_vaddr((const char*)kbase + (int64_t)key * k_row_bytes + c * 16u, slot + (uint32_t)i * 1024u);
+  }
+#pragma unroll
+  for (int i = 0; i < W::VINSTR; ++i) {
+    uint32_t r, c;
+    slot_rc<C::VSPR, C::CPR>((uint32_t)i * 64u + (uint32_t)l, r, c);
+    const int key = min(max(k0 + (int)r, 0), lkm1);
+    dma16_vaddr((const char*)vbase + (int64_t)key * v_row_bytes + c * 16u,
+                slot + (uint32_t)W::KBYTES + (uint32_t)i * 1024u);
+  }
+}
+
 // Key-position form: kidx(local key) gives the key position, or -1 if the slot holds no key;
 // keys beyond the causal limit of `row` are masked too.
 template <int D, class KeyIdx>
@@ -496,7 +591,7 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   const int cstart = a.col_ptr[bh];
   const int ncols = a.col_ptr[bh + 1] - cstart;
   const int* const cidx = a.col_idx + cstart;
-  const uint32_t* const sbits = SLASH ? a.sl_bits + (int64_t)bh * a.bits_words : nullptr;
+  const uint32_t* const sbits = SLASH ? a.rl_bits + (int64_t)bh * a.bits_words : nullptr;
   const uint32_t* const cbits = SLASH ? a.cl_bits + (int64_t)bh * a.bits_words : nullptr;
   const int bits_last = a.bits_words - 1;
   const uint32_t k_row_bytes = (uint32_t)a.k_sl * 2u, v_row_bytes = (uint32_t)a.v_sl * 2u;
@@ -533,12 +628,16 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
     }
   }
   if constexpr (SLASH) {
-    // the line at offset o meets rows q0..qlast at keys q0+off-o .. qlast+off-o (<= klim)
+    // the line at offset o meets rows q0..qlast at keys q0+off-o .. qlast+off-o (<= klim);
+    // only lines inside a run of listed offsets go through the crossed tiles (isolated lines
+    // take the window phase)
     const int s1 = a.sl_ptr[bh + 1];
+    const uint32_t* const rb = a.rl_bits + (int64_t)bh * a.bits_words;
     for (int i = a.sl_ptr[bh] + tid; i < s1; i += NT) {
       const int o = a.sl_idx[i];
       const int hi = qlast + a.off - o;
       if (o < 0 || hi < 0) continue;
+      if (((rb[(o + 128) >> 5] >> ((o + 128) & 31)) & 1u) == 0u) continue;
       const int lo = max(0, q0 + a.off - o);
       if (lo > lkm1) continue;
       for (int kb = lo >> 6; kb <= (min(hi, lkm1) >> 6); ++kb)
@@ -749,30 +848,95 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
             }, l);
           });
     }
+
+    // ---- phase 3b: isolated slash lines (no neighbour offset listed). On the line at offset
+    // o the wave's rows qw0 .. qw0+31 meet the 32 consecutive keys qw0+off-o .. +31, one key
+    // per row (the diagonal of that key range). Each wave copies those keys into its own LDS
+    // slot (two slots per ring stage, free after phase 3a's last barrier), waits for its own
+    // copies only, and runs them as one unit whose mask keeps the diagonal: no workgroup
+    // barrier, and one unit of math per line instead of the two masked 64-key tiles the line
+    // crosses. A key already counted (a listed column, or inside a block the wave's query
+    // block lists) is masked.
+    // The isolated offsets that reach the group's rows are first compacted into kept[] (256
+    // list entries per pass), so each line costs one LDS read before its copy.
+    {
+      using W = WinCfg<D>;
+      const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane(
+          lds_addr(wu < 2 ? st0 : st1) + (uint32_t)(wu & 1) * (uint32_t)W::BYTES);
+      const uint32_t* const rbits = a.rl_bits + (int64_t)bh * a.bits_words;
+      const int* const sidx = a.sl_idx;
+      const int i = l & 31, h = l >> 5;
+      // the accumulator slot that holds local key i (this lane's row) in this lane, or -1
+      const int jdiag = (((i >> 2) & 1) == h) ? 4 * (i >> 3) + (i & 3) : -1;
+      const int s0 = a.sl_ptr[bh], s1 = a.sl_ptr[bh + 1];
+      const int omax = qlast + a.off;  // larger offsets meet no row of the group
+      for (int seg = s0; seg < s1; seg += kSeg) {
+        if (sidx[seg] > omax) break;  // ascending
+        const int cnt = compact(min(kSeg, s1 - seg),
+                                [&](int e) {
+                                  const int o = sidx[seg + e];
+                                  if (o < 0 || o > omax || o >= a.Lk) return false;
+                                  return ((rbits[(o + 128) >> 5] >> ((o + 128) & 31)) & 1u) == 0u;
+                                },
+                                [&](int e) { return sidx[seg + e]; });
+        if (active) {
+          for (int t = 0; t < cnt; ++t) {
+            const int o = kept[t];
+            if (o > qwlast + a.off) break;  // ascending: no row of this wave meets a key
+            const int k0 = qw0 + a.off - o;  // key of the wave's first row on this line
+            issue_window<D>(slot, kbp, vbp, k_row_bytes, v_row_bytes, k0, lkm1, l);
+            const int key = k0 + i;
+            bool keep = jdiag >= 0 && key >= 0 && row < Lq;
+            if (keep) keep = ((cbits[key >> 5] >> (key & 31)) & 1u) == 0u && !listed(myq, key >> 6);
+            wait_dma_all();
+            window_unit<D>(a, ws, slot, keep ? jdiag : -1, l);
+          }
+        }
+        __syncthreads();  // kept[] free for the next pass
+      }
+    }
   }
   store_out<D>(ws, obase, o_sl, lse_row, row, Lq, l);
 }
 
 // Per (b, h): bitmap of the listed slash offsets (bit o + 128, so a lane's window never starts
-// below bit 0) and of the listed columns (bit j), nbw words each; out-of-range entries are
-// ignored.
+// below bit 0), of the listed columns (bit j), and of the listed offsets that have a listed
+// neighbour offset (o - 1 or o + 1: the line lies inside a run of lines), nbw words each;
+// out-of-range entries are ignored. The offsets are first collected in LDS, so the
+// neighbour test reads a complete bitmap.
+constexpr int kVsBitsMaxWords = vs_bits_words(kVslashMaxLk);
+
 __global__ __launch_bounds__(256) void vs_bits_kernel(const FwdArgs a) {
+  __shared__ uint32_t lb[kVsBitsMaxWords];
   const int bh = (int)blockIdx.x;
-  uint32_t* sb = const_cast<uint32_t*>(a.sl_bits) + (int64_t)bh * a.bits_words;
-  uint32_t* cb = const_cast<uint32_t*>(a.cl_bits) + (int64_t)bh * a.bits_words;
-  for (int i = (int)threadIdx.x; i < a.bits_words; i += 256) {
-    sb[i] = 0u;
+  const int nw = a.bits_words;
+  uint32_t* sb = const_cast<uint32_t*>(a.sl_bits) + (int64_t)bh * nw;
+  uint32_t* cb = const_cast<uint32_t*>(a.cl_bits) + (int64_t)bh * nw;
+  uint32_t* rb = const_cast<uint32_t*>(a.rl_bits) + (int64_t)bh * nw;
+  for (int i = (int)threadIdx.x; i < nw; i += 256) {
+    lb[i] = 0u;
     cb[i] = 0u;
+    rb[i] = 0u;
   }
   __threadfence();
   __syncthreads();
-  for (int i = a.sl_ptr[bh] + (int)threadIdx.x; i < a.sl_ptr[bh + 1]; i += 256) {
+  const int s0 = a.sl_ptr[bh], s1 = a.sl_ptr[bh + 1];
+  for (int i = s0 + (int)threadIdx.x; i < s1; i += 256) {
     const int o = a.sl_idx[i];
-    if (o >= 0 && o < a.Lk) atomicOr(&sb[(o + 128) >> 5], 1u << ((o + 128) & 31));
+    if (o >= 0 && o < a.Lk) atomicOr(&lb[(o + 128) >> 5], 1u << ((o + 128) & 31));
   }
   for (int i = a.col_ptr[bh] + (int)threadIdx.x; i < a.col_ptr[bh + 1]; i += 256) {
     const int j = a.col_idx[i];
     if (j >= 0 && j < a.Lk) atomicOr(&cb[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  auto bit = [&](int x) { return (lb[x >> 5] >> (x & 31)) & 1u; };
+  for (int i = (int)threadIdx.x; i < nw; i += 256) sb[i] = lb[i];
+  for (int i = s0 + (int)threadIdx.x; i < s1; i += 256) {
+    const int o = a.sl_idx[i];
+    if (o < 0 || o >= a.Lk) continue;
+    const int x = o + 128;
+    if (bit(x - 1) | bit(x + 1)) atomicOr(&rb[x >> 5], 1u << (x & 31));
   }
 }
 

@@ -35,6 +35,8 @@ struct FwdArgs {
   const int32_t* sl_idx;
   const uint32_t* sl_bits;  // [B*Hq][bits_words]: bit o + 128 set for a listed offset o
   const uint32_t* cl_bits;  // [B*Hq][bits_words]: bit j set for a listed column j
+  const uint32_t* rl_bits;  // [B*Hq][bits_words]: bit o + 128 set for a listed offset o whose
+                            // neighbour o - 1 or o + 1 is listed too (a line inside a run)
   int bits_words;
 };
 
@@ -43,7 +45,9 @@ struct FwdArgs {
 constexpr int kVslashMaxLk = 1 << 19;
 
 // Words per head of each vertical-slash bitmap.
-inline int vs_bits_words(int Lk) { return (Lk + 255) / 32 + 2; }
+constexpr int vs_bits_words(int Lk) { return (Lk + 255) / 32 + 2; }
+// Bitmaps per head in the vertical-slash workspace (offsets, columns, offsets inside runs).
+constexpr int kVslashBitmaps = 3;
 
 // Split-KV partials.
 struct SplitArgs {

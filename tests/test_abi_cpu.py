@@ -201,9 +201,10 @@ def test_vertical_slash_entry_validation(kw, code, frag):
 
 
 def test_vertical_slash_workspace_bytes():
-    # two bitmaps per (b, h) of (Lk + 255) // 32 + 2 words each
-    assert S.attn_vertical_slash_workspace_bytes(1, 32, 131072) == 2 * 32 * (4103 + 2) * 4
-    assert S.attn_vertical_slash_workspace_bytes(2, 3, 1) == 2 * 6 * (8 + 2) * 4
+    # three bitmaps per (b, h) (offsets, columns, offsets inside runs) of (Lk + 255) // 32 + 2
+    # words each
+    assert S.attn_vertical_slash_workspace_bytes(1, 32, 131072) == 3 * 32 * (4103 + 2) * 4
+    assert S.attn_vertical_slash_workspace_bytes(2, 3, 1) == 3 * 6 * (8 + 2) * 4
     assert S.attn_vertical_slash_workspace_bytes(0, 3, 100) == 0
 
 

@@ -112,6 +112,44 @@ def test_bottom_right_alignment_and_d64():
     _compare(q, k, v, bp, bi, cp, ci, sp, si, "alignment d64")
 
 
+@pytest.mark.parametrize("Lq,Lk,D", [(700, 700, 128), (300, 900, 128), (500, 260, 64)],
+                         ids=["square", "lq_lt_lk", "lq_gt_lk_d64"])
+def test_isolated_lines_planted(Lq, Lk, D):
+    """Isolated slash lines (no neighbour offset listed: the per-wave window phase) beside a run
+    of offsets (the tile phase). Keys on two isolated lines are planted so that each carries
+    about half of its rows' weight (K row parallel to the row's Q, large V): a line missed, a
+    pair counted twice, or a wrong key moves O by far more than the tolerance. Some planted keys
+    are also listed columns or inside listed blocks (counted once), and with Lq > Lk the lines
+    start at negative keys for the first rows. The planted keys dominate their rows (scores
+    near 20 against about 1), so O there is close to 1; one row in three is planted, which keeps
+    the mean |O| (and with it the mean-abs error of bf16 weights) near that of plain inputs."""
+    import torch
+    B, Hq, Hkv = 1, 4, 2
+    say(f"vslash isolated lines Lq={Lq} Lk={Lk} D={D}")
+    q, k, v = _qkv(B, Lq, Lk, Hq, Hkv, D, 7700 + Lq)
+    off = Lk - Lq
+    lines = [37, 211]                      # isolated offsets for every head
+    run = list(range(0, 6))                # a run: tile phase
+    kf, vf = k.float(), v.float()
+    for h in range(Hkv):
+        hq = h * (Hq // Hkv)               # plant for the first query head of each group
+        for n, o in enumerate(lines):
+            for i in range(3 * n, Lq, 6):  # rows 0 mod 6 on one line, 3 mod 6 on the other
+                j = i + off - o
+                if 0 <= j < Lk:
+                    qi = q[0, i, hq].float()
+                    kf[0, j, h] = 6.0 * qi / qi.norm() * (D ** 0.25)
+                    vf[0, j, h] = 1.0
+    k, v = kf.to(torch.bfloat16), vf.to(torch.bfloat16)
+    nqb = -(-Lq // 64)
+    bp, bi = _csr([[qb % max(1, -(-Lk // 64))] for _ in range(B * Hq) for qb in range(nqb)])
+    cols = [[j for j in (5 + off - 37, 90 + off - 211, 301 + off - 37) if 0 <= j < Lk]
+            for _ in range(B * Hq)]
+    cp, ci = _csr(cols)
+    sp, si = _csr([run + lines for _ in range(B * Hq)])
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, f"isolated lines {Lq}x{Lk}")
+
+
 def test_noncausal_blocks_above_diagonal():
     B, Hq, Hkv, L, D = 1, 2, 2, 400, 128
     say("vslash: non-causal")
