@@ -228,7 +228,7 @@ def bench_decode(w, steps, warmup):
             "num_splits": nsp, "kv_copies": ncopies, **STEP_TIMES}
 
 
-def bench_blocksparse(w, steps, warmup):
+def bench_blocksparse(w, steps, warmup, dynamic=True):
     import numpy as np
     import torch
     import sparse_attention_attn_amd as S
@@ -245,6 +245,8 @@ def bench_blocksparse(w, steps, warmup):
     dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
     res = {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
            "density_vs_causal": pairs / dense, **STEP_TIMES}
+    if not dynamic:
+        return res
     # The same attention with lists built from Q and K at run time (attn_build_sparse_index:
     # 96 blocks per query block, 1000 columns per head, about the synthetic lists' density).
     topk, ncols = 96, 1000
@@ -274,7 +276,7 @@ def bench_blocksparse(w, steps, warmup):
     return res
 
 
-def bench_vslash(w, steps, warmup):
+def bench_vslash(w, steps, warmup, dynamic=True):
     import numpy as np
     import torch
     import sparse_attention_attn_amd as S
@@ -297,6 +299,8 @@ def bench_vslash(w, steps, warmup):
     dense = w.B * w.Hq * dense_causal_pairs(w.Lq, w.Lk, True)
     res = {"ms": ms, "wall_s": wall, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
            "density_vs_causal": pairs / dense, **STEP_TIMES}
+    if not dynamic:
+        return res
     # Lists built from Q and K at run time (attn_build_vslash_index), as many columns and lines
     # as the synthetic lists. Random inputs have no diagonal structure, so the chosen lines
     # scatter over all offsets and the forward then visits nearly every causal block.
@@ -675,6 +679,9 @@ def main():
                     help="skip the FlashMLA-ETAP decode grid sweep")
     ap.add_argument("--no-memory", action="store_true",
                     help="skip the peak-memory comparison at long sequence lengths")
+    ap.add_argument("--no-dynamic", action="store_true",
+                    help="block-sparse and vertical-slash: skip the built-list (index builder) "
+                         "measurements, so a profile of the run holds the static-list launches only")
     ap.add_argument("--no-crossover", action="store_true",
                     help="skip the dense vs dynamic sparse sweep over sequence length")
     ap.add_argument("--no-achievable", action="store_true",
@@ -721,9 +728,11 @@ def main():
         elif w.kind in ("decode", "mla_decode"):
             res[name] = bench_decode(w, args.steps * 5, args.warmup)
         elif w.kind == "blocksparse":
-            res[name] = bench_blocksparse(w, max(3, args.steps // 4), min(args.warmup, 2))
+            res[name] = bench_blocksparse(w, max(3, args.steps // 4), min(args.warmup, 2),
+                                          dynamic=not args.no_dynamic)
         elif w.kind == "vslash":
-            res[name] = bench_vslash(w, max(3, args.steps // 4), min(args.warmup, 2))
+            res[name] = bench_vslash(w, max(3, args.steps // 4), min(args.warmup, 2),
+                                     dynamic=not args.no_dynamic)
         log(f"  -> {res[name]}")
 
     head = WORKLOADS[HEADLINE]

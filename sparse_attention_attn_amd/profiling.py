@@ -152,6 +152,25 @@ def per_dispatch(dispatches, kernel):
     return sum(vals) / len(vals), len(vals)
 
 
+def step_rate(stats, kernels, work, unit, peak):
+    """Per-step rate from the kernel trace: `kernels` run once per step each; their average
+    durations add up to the step time. work: algorithmic flops (unit TFLOP/s) or bytes (unit
+    GB/s) of one step; peak in the same unit."""
+    ns = 0.0
+    parts = []
+    for k in kernels:
+        mine = [s for s in stats if k in s["name"]]
+        if not mine:
+            raise ValueError(f"kernel {k!r} not in the trace")
+        ns += mine[0]["avg_ns"]
+        parts.append({"kernel": k, "avg_us": round(mine[0]["avg_ns"] / 1e3, 2),
+                      "calls": mine[0]["calls"]})
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    rate = work / (ns * 1e-9) / scale
+    return {"kernels": parts, "step_us": round(ns / 1e3, 2), "work": work, "unit": unit,
+            "achieved": round(rate, 3), "peak": peak, "frac": round(rate / peak, 4)}
+
+
 def summary(stats_dir, fetch_dir, write_dir, calib_mib, kernel, workload, command,
             algorithmic_bytes=None):
     stats = read_kernel_stats(stats_dir)
@@ -180,6 +199,13 @@ def render_md(rec, stats, stats_cmd, fetch_cmd, write_cmd):
     lines = [f"# {rec['kernel']} — {rec['workload']}", ""]
     lines += ["Kernel-trace statistics command (run from the repository root):", "",
               "```", stats_cmd, "```", ""]
+    if "rate" in rec:
+        r = rec["rate"]
+        names = " + ".join(f"`{p['kernel']}` {p['avg_us']} µs" for p in r["kernels"])
+        lines += [f"- step time from the trace: {names} = {r['step_us']} µs",
+                  f"- algorithmic work per step: {r['work']:,} ({'flop' if r['unit'] == 'TFLOP/s' else 'B'})",
+                  f"- rate: {r['achieved']} {r['unit']} = {r['frac']:.4f} of the {r['peak']} "
+                  f"{r['unit']} peak", ""]
     lines += ["| kernel | calls | avg µs | min µs | max µs | % of GPU time |",
               "|---|---|---|---|---|---|"]
     for s in stats:
@@ -219,6 +245,12 @@ def main(argv=None):
                    help="comma list of csrc files whose hash tags the traffic record")
     s.add_argument("--out", required=True)
     s.add_argument("--traffic-json")
+    s.add_argument("--step-kernel", action="append", default=[],
+                   help="kernel run once per step (repeat for several); with --work, --unit "
+                        "and --peak the summary states the step's rate and fraction of peak")
+    s.add_argument("--work", type=float, default=None)
+    s.add_argument("--unit", default="TFLOP/s")
+    s.add_argument("--peak", type=float, default=None)
     m = sub.add_parser("mfma")
     m.add_argument("--dir", required=True)
     m.add_argument("--kernel", required=True)
@@ -235,6 +267,8 @@ def main(argv=None):
         return
     rec, stats = summary(a.stats, a.fetch, a.write, a.calib_mib, a.kernel, a.workload,
                          a.stats_command, a.algorithmic_bytes)
+    if a.work is not None and a.peak is not None:
+        rec["rate"] = step_rate(stats, a.step_kernel or [a.kernel], int(a.work), a.unit, a.peak)
     with open(a.out, "w") as fh:
         fh.write(render_md(rec, stats, a.stats_command, a.fetch_command, a.write_command))
     if a.traffic_json:
