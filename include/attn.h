@@ -74,6 +74,10 @@ typedef enum attn_status {
 
 /*
  * attn_fwd — dense attention forward (prefill; any Lq, Lk).
+ * Passage: "Resumen Técnico: FlashMLA-ETAP", section "Mecanismo Central" (S = Q·Kᵀ,
+ * P = softmax(S), O = P·V), computed tile by tile as in "Activar Flash Attention con
+ * llama.cpp para optimizar la inferencia", section "¿Qué es Flash Attention y por qué es
+ * crucial para llama.cpp?"; causal GQA as in that page's FAQ entry on Grouped Query Attention.
  * Supported head dims: (Dqk, Dv) = (64, 64) or (128, 128).
  * Errors: INVALID_ARG if any of B, Hq, Hkv, Lq, Lk < 1, Hq % Hkv != 0, scale not finite, a
  * NULL q/k/v/o pointer, misalignment; UNSUPPORTED for other head dims; LAUNCH on HIP failure.
@@ -84,6 +88,12 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
 
 /*
  * Split-KV decode: attn_fwd_splitkv writes per-split partials, attn_combine_lse merges them.
+ * Passage: "Resumen Técnico: FlashMLA-ETAP", section "Planteamiento del Problema" (one or two
+ * query tokens against a KV context of up to 64K, bound by the bandwidth of reading it) and
+ * section "Mecanismo Central" (the attention each split computes over its keys). The pages do
+ * not describe splitting the keys; the split and the log-sum-exp merge are this library's way
+ * of spreading one decode step over the whole GPU, and the merge is exact: it equals attention
+ * over all keys up to rounding.
  * Split s covers keys [s·C, min((s+1)·C, Lk)) with C = 64·ceil(ceil(Lk / S) / 64); a split
  * with no visible key writes O_s = 0 and LSE_s = -inf (weight 0 in the merge). The merge is
  * M = max_s LSE_s, w_s = exp(LSE_s - M), LSE = M + ln Σ w_s, O = Σ w_s O_s / Σ w_s.
@@ -100,15 +110,17 @@ int attn_splitkv_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int
 /* Bytes of o_part plus lse_part for these sizes (0 on invalid sizes). */
 size_t attn_splitkv_workspace_bytes(int B, int Hq, int Lq, int Dv, int num_splits);
 
-/* Errors: as attn_fwd, plus INVALID_ARG for num_splits out of range and WORKSPACE when
+/* attn_fwd_splitkv — the partials of every split (passages as above).
+ * Errors: as attn_fwd, plus INVALID_ARG for num_splits out of range and WORKSPACE when
  * o_part or lse_part is NULL or not 16-byte aligned. */
 int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v,
                      float* o_part, float* lse_part, int num_splits,
                      int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal,
                      float scale, void* stream);
 
-/* Merges the partials into O (bf16, strided like attn_fwd's O) and LSE (fp32 [B, Hq, Lq] or
- * NULL). Errors: INVALID_ARG for sizes < 1, NULL or misaligned pointers, Dv not in
+/* attn_combine_lse — merges the partials into O (bf16, strided like attn_fwd's O) and LSE
+ * (fp32 [B, Hq, Lq] or NULL) with the formula above: the softmax over all keys of
+ * "Mecanismo Central", rebuilt from per-split maxima and sums. Errors: INVALID_ARG for sizes < 1, NULL or misaligned pointers, Dv not in
  * {64, 128, 512}; WORKSPACE when o_part or lse_part is NULL. */
 int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits,
                      attn_tensor_t o, float* lse, int B, int Hq, int Lq, int Dv, void* stream);
@@ -163,6 +175,9 @@ int attn_fwd_decode_noalloc(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, a
  * vertical key columns (the block-sparse / A-shape / vertical-slash index lists), with the
  * causal mask applied on top when `causal` is set. Each key is counted once even when it is
  * both inside a listed block and listed as a column.
+ * Passage: MInference article (7minutos.es), paragraphs on the A-shape, vertical-slash and
+ * block-sparse patterns and on the sparse indices the kernels consume; "SparseAccelerate:
+ * Acelerando Modelos de Lenguaje", section "Patrones de Atención Dispersa Dinámicos".
  *
  *   blk_ptr [B·Hq·nqb + 1], blk_idx — CSR over (b, h, qb) row-major, nqb = ceil(Lq / 64):
  *       blk_idx[blk_ptr[r] .. blk_ptr[r+1]) are the key-block ids (key block kb = keys
