@@ -337,18 +337,21 @@ struct WinCfg {
   static constexpr int VINSTR = VBYTES / 1024;
   static constexpr int BYTES = KBYTES + VBYTES;
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole copy instructions");
-  static_assert(2 * BYTES <= SpCfg<D>::STAGE_BYTES, "two window slots per ring stage");
+  static_assert(2 * BYTES + 512 <= SpCfg<D>::STAGE_BYTES,
+                "two window slots and their column words per ring stage");
   static __device__ __forceinline__ uint32_t swz(uint32_t r) {
     return D == 128 ? (r & 15u) : ((r >> 1) & 7u);
   }
 };
 
-// One 32-key unit of the window phase: Sᵀ = K·Qᵀ over the wave's slot, every score but the
-// kept one set to -inf (keep_slot: the accumulator slot j of this lane that holds a visible key,
-// or -1), the weights, then Oᵀ += Vᵀ·Pᵀ.
+// One 32-key unit of the window phase, in two halves so that the copies of the next line's K
+// and of this line's V can overlap them. window_scores: Sᵀ = K·Qᵀ over the wave's slot, every
+// score but the kept one set to -inf (keep_slot: the accumulator slot j of this lane that
+// holds a visible key, or -1), and the weights (Pᵀ operands p, running sums updated).
+// window_pv: Oᵀ += Vᵀ·Pᵀ.
 template <int D>
-__device__ __forceinline__ void window_unit(const FwdArgs& a, WaveState<D>& ws, uint32_t slot,
-                                            int keep_slot, int l) {
+__device__ __forceinline__ void window_scores(const FwdArgs& a, WaveState<D>& ws, uint32_t slot,
+                                              int keep_slot, int l, bf16x8 (&p)[2]) {
   using W = WinCfg<D>;
   using C = SpCfg<D>;
   const uint32_t i = (uint32_t)(l & 31), h = (uint32_t)(l >> 5);
@@ -374,13 +377,18 @@ __device__ __forceinline__ void window_unit(const FwdArgs& a, WaveState<D>& ws, 
     pk[g >> 2][g & 3] = pack_bf16x2(e0, e1);
     sb = add_bf16_pair(pk[g >> 2][g & 3], sb);
   }
-  bf16x8 p[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
     p[ks] = __builtin_bit_cast(bf16x8, make_uint4(pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]));
   if (__builtin_expect(__any(!unit_ok(ws.m, sf)), 0)) slow_unit<D>(ws, s, sl2, p, sb, sf);
   ws.lb = sb;
   ws.lf = sf;
+}
+
+template <int D>
+__device__ __forceinline__ void window_pv(WaveState<D>& ws, uint32_t slot, const bf16x8 (&p)[2]) {
+  using W = WinCfg<D>;
+  using C = SpCfg<D>;
   const uint32_t vt = slot + (uint32_t)W::KBYTES + ws.vofs;
 #pragma unroll
   for (int v = 0; v < 2 * C::DVB; ++v) {
@@ -390,15 +398,21 @@ __device__ __forceinline__ void window_unit(const FwdArgs& a, WaveState<D>& ws, 
   }
 }
 
-// Copies into a wave's window slot the K and V rows of keys k0 .. k0 + 31 (clamped into
-// [0, lkm1], so every load is in bounds; the clamped rows are masked by the caller).
+// Copies into a wave's window slot the K rows (issue_window_k, with the two words of the
+// column bitmap that cover those keys, to LDS address cw) or the V rows (issue_window_v) of keys
+// k0 .. k0 + 31, clamped into [0, lkm1] so that every load is in bounds (the clamped rows are
+// masked by the caller). Each first waits for the wave's earlier reads of the slot.
 template <int D>
-__device__ __forceinline__ void issue_window(uint32_t slot, const uint16_t* kbase,
-                                             const uint16_t* vbase, uint32_t k_row_bytes,
-                                             uint32_t v_row_bytes, int k0, int lkm1, int l) {
+constexpr int kWinKCopies = WinCfg<D>::KINSTR + 1;  // copy instructions of issue_window_k
+template <int D>
+constexpr int kWinVCopies = WinCfg<D>::VINSTR;      // copy instructions of issue_window_v
+
+template <int D>
+__device__ __forceinline__ void issue_window_k(uint32_t slot, uint32_t cw, const uint16_t* kbase,
+                                               uint32_t k_row_bytes, const uint32_t* cbits,
+                                               int k0, int lkm1, int l) {
   using W = WinCfg<D>;
-  using C = SpCfg<D>;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // earlier reads of the slot returned
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int i = 0; i < W::KINSTR; ++i) {
     const uint32_t q = (uint32_t)i * 64u + (uint32_t)l;
@@ -407,6 +421,17 @@ __device__ __forceinline__ void issue_window(uint32_t slot, const uint16_t* kbas
     const int key = min(max(k0 + (int)r, 0), lkm1);
     dma16_vaddr((const char*)kbase + (int64_t)key * k_row_bytes + c * 16u, slot + (uint32_t)i * 1024u);
   }
+  // words max(k0, 0)/32 and the next one (lanes beyond 1 re-read them; the bitmap has two
+  // spare words past the last key)
+  dma4_vaddr(cbits + (max(k0, 0) >> 5) + (l & 1), cw);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_window_v(uint32_t slot, const uint16_t* vbase,
+                                               uint32_t v_row_bytes, int k0, int lkm1, int l) {
+  using W = WinCfg<D>;
+  using C = SpCfg<D>;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int i = 0; i < W::VINSTR; ++i) {
     uint32_t r, c;
@@ -415,6 +440,12 @@ __device__ __forceinline__ void issue_window(uint32_t slot, const uint16_t* kbas
     dma16_vaddr((const char*)vbase + (int64_t)key * v_row_bytes + c * 16u,
                 slot + (uint32_t)W::KBYTES + (uint32_t)i * 1024u);
   }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Key-position form: kidx(local key) gives the key position, or -1 if the slot holds no key;
@@ -863,6 +894,9 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
       using W = WinCfg<D>;
       const uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane(
           lds_addr(wu < 2 ? st0 : st1) + (uint32_t)(wu & 1) * (uint32_t)W::BYTES);
+      // the wave's two column-bitmap words, past both slots of its stage
+      const uint32_t cw = (uint32_t)__builtin_amdgcn_readfirstlane(
+          lds_addr(wu < 2 ? st0 : st1) + 2u * (uint32_t)W::BYTES + 256u * (uint32_t)(wu & 1));
       const uint32_t* const rbits = a.rl_bits + (int64_t)bh * a.bits_words;
       const int* const sidx = a.sl_idx;
       const int i = l & 31, h = l >> 5;
@@ -880,16 +914,36 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
                                 },
                                 [&](int e) { return sidx[seg + e]; });
         if (active) {
-          for (int t = 0; t < cnt; ++t) {
-            const int o = kept[t];
-            if (o > qwlast + a.off) break;  // ascending: no row of this wave meets a key
-            const int k0 = qw0 + a.off - o;  // key of the wave's first row on this line
-            issue_window<D>(slot, kbp, vbp, k_row_bytes, v_row_bytes, k0, lkm1, l);
+          // lines 0 .. n-1 of this pass reach the wave's rows (ascending offsets)
+          int n = 0;
+          while (n < cnt && kept[n] <= qwlast + a.off) ++n;
+          n = __builtin_amdgcn_readfirstlane(n);  // wave-uniform: scalar loop control
+          // Software pipeline over the wave's lines: K (with its column words) of line t+1 is
+          // copied during the softmax and P·V of line t, V of line t+1 during the scores of
+          // line t+1; the counted waits leave the other half's copies in flight.
+          auto k0_of = [&](int t) { return qw0 + a.off - kept[t]; };
+          if (n > 0) {
+            issue_window_k<D>(slot, cw, kbp, k_row_bytes, cbits, k0_of(0), lkm1, l);
+            issue_window_v<D>(slot, vbp, v_row_bytes, k0_of(0), lkm1, l);
+          }
+          for (int t = 0; t < n; ++t) {
+            const int k0 = k0_of(t);
+            wait_vmcnt_le<kWinVCopies<D>>();  // K and column words of line t landed
             const int key = k0 + i;
             bool keep = jdiag >= 0 && key >= 0 && row < Lq;
-            if (keep) keep = ((cbits[key >> 5] >> (key & 31)) & 1u) == 0u && !listed(myq, key >> 6);
-            wait_dma_all();
-            window_unit<D>(a, ws, slot, keep ? jdiag : -1, l);
+            if (keep) {
+              const uint32_t cwd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+                  cw + 4u * (uint32_t)((key >> 5) - (max(k0, 0) >> 5)));
+              keep = ((cwd >> (key & 31)) & 1u) == 0u && !listed(myq, key >> 6);
+            }
+            bf16x8 p[2];
+            window_scores<D>(a, ws, slot, keep ? jdiag : -1, l, p);
+            const bool more = t + 1 < n;
+            if (more) issue_window_k<D>(slot, cw, kbp, k_row_bytes, cbits, k0_of(t + 1), lkm1, l);
+            if (more) wait_vmcnt_le<kWinKCopies<D>>();  // V of line t landed
+            else wait_dma_all();
+            window_pv<D>(ws, slot, p);
+            if (more) issue_window_v<D>(slot, vbp, v_row_bytes, k0_of(t + 1), lkm1, l);
           }
         }
         __syncthreads();  // kept[] free for the next pass
