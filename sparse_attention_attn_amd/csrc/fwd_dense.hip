@@ -362,7 +362,11 @@ __global__ __launch_bounds__(kDenseWaves * 64, kDenseWgPerCu) void fwd_dense_ker
   const int hq = hkv * a.g + hg;
 
   const int q0 = qt * BM;
-  const int qw0 = q0 + 32 * NR * w;           // first row of this wave
+  // Row block of this wave. Waves w and w + NW/2 share a SIMD; they take row blocks w and
+  // NW-1-w, so near the causal diagonal (where a wave skips the units past its last row) every
+  // SIMD skips the same number of units.
+  const int rblk = w < NW / 2 ? w : (3 * NW / 2 - 1) - w;
+  const int qw0 = q0 + 32 * NR * rblk;        // first row of this wave
   const int qlast = min(q0 + BM, a.Lq) - 1;   // last row of the workgroup
   int klimit = a.Lk;                          // keys [0, klimit) can be visible
   if (a.causal) klimit = max(0, min(a.Lk, qlast + a.off + 1));
@@ -388,6 +392,14 @@ __global__ __launch_bounds__(kDenseWaves * 64, kDenseWgPerCu) void fwd_dense_ker
   int nfull = a.Lk / 32;
   if (a.causal) nfull = min(nfull, max(0, qw0 + a.off + 1) / 32);
   nfull = __builtin_amdgcn_readfirstlane(nfull);
+  // Last step with work for this wave: the P·V of the last unit holding a key visible to one of
+  // its rows (with causal masking the workgroup streams later units for its other waves only).
+  int jlast = 2 * ntiles;
+  if (a.causal) {
+    const int lastkey = min(a.Lk - 1, min(qw0 + 32 * NR - 1, a.Lq - 1) + a.off);
+    jlast = min(jlast, (lastkey + 32) / 32);  // last unit + 1 (0 when no key is visible)
+  }
+  jlast = __builtin_amdgcn_readfirstlane(jlast);
 
   auto stage_addr = [&](int t) -> uint32_t { return lds0 + (uint32_t)(t & 1) * C::STAGE_BYTES; };
   // Copies pair t (issued in increasing order of t <= ntiles) into its stage: K of tile t when
@@ -443,6 +455,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, kDenseWgPerCu) void fwd_dense_ker
       barrier_lds();   // ... for every wave, and every wave is done with step 2t
       if (t + 2 <= ntiles) issue(t + 2);
     }
+    if (j > jlast) return;  // every later unit is masked for all rows of this wave
     float sb[NR], sf[NR];
     bool ok;
     if (j >= nfull) mask_unit<NR>(sc[H], j, qw0, a.Lk, a.causal, a.off, l);
