@@ -161,8 +161,65 @@ def achievable_peaks():
     copy = 2.0 * x.numel() / (ms_c * 1e-3) / 1e9
     del x, y
     torch.cuda.empty_cache()
-    return {"bf16_gemm_tflops": round(gemm, 1), "hbm_copy_gbs": round(copy, 1),
-            "gemm": "torch.matmul bf16 8192^3", "copy": "1 GiB device copy, read + write"}
+    out = {"bf16_gemm_tflops": round(gemm, 1), "hbm_copy_gbs": round(copy, 1),
+           "gemm": "torch.matmul bf16 8192^3", "copy": "1 GiB device copy, read + write"}
+    out["read_ceilings"] = read_ceilings()
+    return out
+
+
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_attn_amd", "libattn_probes.so"))
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.probe_read_tiles.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    lib.probe_read_tiles.restype = i32
+    return lib
+
+
+def read_ceilings():
+    """Read rates of this GPU measured with the library's own probe kernel (libattn_probes.so):
+    whole 32 KiB tiles (the K and V bytes of one 64-key tile at D = 128), read in order
+    (a stream: each XCD reads distinct tiles) or at seeded random tile positions, from a 2 GiB
+    region (HBM) and from a 128 MiB region re-read launch after launch (two KV heads' K and V
+    at 128K keys: larger than the eight 4 MiB L2s, inside the 256 MiB Infinity Cache). 2048 workgroups of 256 lanes, each
+    reading 16 tiles one after another."""
+    import torch
+    lib = _probe_lib()
+    grid, per_wg, tile = 2048, 16, 32 << 10
+    ntile = grid * per_wg
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda:0")
+    g = torch.Generator().manual_seed(11)
+    res = {}
+    for region_name, region, steps in (("hbm", 2 << 30, 20), ("infinity_cache", 128 << 20, 50)):
+        buf = torch.empty(region, dtype=torch.uint8, device="cuda:0")
+        nreg = region // tile
+        for kind in ("stream", "tile_gather"):
+            if kind == "stream":
+                # workgroup g (XCD g % 8) reads 16 consecutive tiles; the XCDs start 1/8 of the
+                # region apart, so no XCD reads a tile twice in a launch (its L2 never hits)
+                g_ = torch.arange(grid, dtype=torch.int64).repeat_interleave(per_wg)
+                t_ = torch.arange(per_wg, dtype=torch.int64).repeat(grid)
+                ids = (((g_ // 8) * per_wg + t_ + (g_ % 8) * (nreg // 8)) % nreg).to(torch.int32)
+            else:
+                ids = torch.randint(0, nreg, (ntile,), generator=g, dtype=torch.int32)
+            ids = ids.to("cuda:0")
+
+            def step():
+                rc = lib.probe_read_tiles(buf.data_ptr(), ids.data_ptr(), per_wg, grid, tile,
+                                          sink.data_ptr(), stream)
+                if rc != 0:
+                    raise RuntimeError(f"read probe launch failed: hipError {rc}")
+
+            ms, _ = time_steps(step, steps, 10)
+            res[f"{region_name}_{kind}_read_gbs"] = round(ntile * tile / (ms * 1e-3) / 1e9, 1)
+            del ids
+        del buf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    res["probe"] = ("libattn_probes.so: 2048 x 256 lanes, 16 tiles of 32 KiB each, 16-byte "
+                    "loads, 8 in flight per lane")
+    return res
 
 
 def kernel_source_hash(files):

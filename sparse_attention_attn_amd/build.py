@@ -1,7 +1,8 @@
-"""Build libattn.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+"""Build libattn.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc, and beside it
+libattn_probes.so (the benchmark's read-rate probes; no attention entry point uses them).
 
 Usage: python -m sparse_attention_attn_amd.build [--verbose]
-The library lands next to this file; object files go to sparse_attention_attn_amd/_build/.
+The libraries land next to this file; object files go to sparse_attention_attn_amd/_build/.
 """
 
 from __future__ import annotations
@@ -17,9 +18,11 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libattn_probes.so")
 
 SOURCES = ["fwd_dense.hip", "fwd_blocksparse.hip", "fwd_splitkv.hip", "sparse_index.hip", "api.cpp",
            "validate.cpp"]
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 # Per-source extra flags for the dense kernel:
 #  * no IEEE mode and no NaN semantics: its row maxima then lower to plain v_max3_f32 with no
@@ -68,19 +71,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libattn.so. Always rebuilds. Returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libattn.so failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"linking {os.path.basename(path)} failed:\n{res.stderr}")
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libattn.so and libattn_probes.so. Always rebuilds.
+    Returns the path of libattn.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

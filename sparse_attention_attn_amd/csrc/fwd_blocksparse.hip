@@ -703,6 +703,17 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
     return cnt;
   };
 
+  // Key blocks 0 .. nvis-1 can hold a key visible to a row of the group. A segment of block ids
+  // whose candidate bits (word_fn of its words) are all clear is skipped without a compaction
+  // pass; every thread reads the same LDS words, so the decision is uniform.
+  const int nvis = (klim >> 6) + 1;
+  auto seg_empty = [&](int c0, auto word_fn) -> bool {
+    uint32_t v = 0u;
+    const int w1 = min((c0 + kSeg) >> 5, nwords);
+    for (int wd = c0 >> 5; wd < w1; ++wd) v |= word_fn(wd);
+    return v == 0u;
+  };
+
   WaveState<D> ws;
   load_q<D>(a, ws, b, hq, row, l);
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -730,9 +741,12 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   // the other stage, whose readers (the math of tile t-1) all passed the barrier, and runs the
   // math of tile t. The copies are invisible to the compiler, so it adds no waits of its own
   // before the LDS reads; the barrier carries no memory fence (nothing else needs ordering).
+  // An empty pass returns at once: the compaction that produced it ended with a barrier, and it
+  // issues no copies.
   auto run = [&](int ntl, auto issue_fn, auto math_fn) {
+    if (ntl == 0) return;
     wait_vmcnt_visible0();  // the Q operands (and any earlier load) are in registers
-    if (ntl > 0) issue_fn(ic<0>{}, 0);
+    issue_fn(ic<0>{}, 0);
     auto step = [&](auto S, int t) {
       constexpr int s = decltype(S)::value;
       wait_dma_all();
@@ -747,9 +761,10 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
     __syncthreads();  // stages and kept[] free for the next pass
   };
 
-  // ---- phase 1: the union of the group's listed key blocks, 512 block ids per pass
-  for (int c0 = 0; c0 < nwords * 32; c0 += kSeg) {
-    const int cnt = compact(min(kSeg, nwords * 32 - c0),
+  // ---- phase 1: the union of the group's listed key blocks, kSeg block ids per pass
+  for (int c0 = 0; c0 < nvis; c0 += kSeg) {
+    if (seg_empty(c0, any_word)) continue;
+    const int cnt = compact(min(kSeg, nvis - c0),
                             [&](int i) {
                               const int kb = c0 + i;
                               return ((any_word(kb >> 5) >> (kb & 31)) & 1u) != 0u;
@@ -806,7 +821,12 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
           if (!active) return;
           // columns are ascending: skip if even the first one is beyond this wave's horizon
           if (a.causal && (kept[cb] & kColMask) > qwlast + a.off) return;
-          tile_math<D>(a, ws, stage(S), row, true,
+          // no mask when every slot holds a column that every row of the wave sees and that
+          // no block the wave's block lists contains (lane l checks entry cb + l)
+          const int el = kept[min(cb + l, cnt - 1)];
+          const bool hidden = cb + l >= cnt || ((el >> (kFlagShift + myq)) & 1) ||
+                              (a.causal && (el & kColMask) > qw0 + a.off);
+          tile_math<D>(a, ws, stage(S), row, __any(hidden),
                        [&](int kl) {
                          if (cb + kl >= cnt) return -1;
                          const int e = kept[cb + kl];
@@ -823,8 +843,9 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
     const int rw0 = q0 + a.off + 65;  // smallest rw of the group (row q0, h = 1)
     // first offset word of the group's window for the tile at `base`
     auto win0 = [&](int base) { return max(rw0 - base, 0) >> 5; };
-    for (int c0 = 0; c0 < nwords * 32; c0 += kSeg) {
-      const int cnt = compact(min(kSeg, nwords * 32 - c0),
+    for (int c0 = 0; c0 < nvis; c0 += kSeg) {
+      if (seg_empty(c0, [&](int wd) { return tbits[wd] & ~all_word(wd); })) continue;
+      const int cnt = compact(min(kSeg, nvis - c0),
                               [&](int i) {
                                 const int kb = c0 + i;
                                 const uint32_t all = all_word(kb >> 5);
@@ -871,7 +892,10 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
             const uint32_t vis1 = (r1 >> 4) & ~c1w;
             // a line crossing the tile within the pair's rows may miss this wave's rows
             if (!__any((vis0 | vis1) != 0u)) return;
-            tile_math_mask<D>(a, ws, stage(S), true, [&](auto U, f32x16& sc) {
+            // no mask when every slot of both units is visible in every lane
+            constexpr uint32_t kSlots = 0x0F0F0F0Fu;
+            const bool full = __all((vis0 & vis1 & kSlots) == kSlots);
+            tile_math_mask<D>(a, ws, stage(S), !full, [&](auto U, f32x16& sc) {
               const uint32_t vis = decltype(U)::value == 0 ? vis0 : vis1;
 #pragma unroll
               for (int jj = 0; jj < 16; ++jj)
@@ -904,8 +928,17 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
       const int jdiag = (((i >> 2) & 1) == h) ? 4 * (i >> 3) + (i & 3) : -1;
       const int s0 = a.sl_ptr[bh], s1 = a.sl_ptr[bh + 1];
       const int omax = qlast + a.off;  // larger offsets meet no row of the group
+      static_assert(kSeg == NT, "one list entry per thread in the emptiness test");
       for (int seg = s0; seg < s1; seg += kSeg) {
         if (sidx[seg] > omax) break;  // ascending
+        // a pass with no isolated offset in reach is skipped after one barrier
+        bool any_iso = false;
+        if (seg + tid < s1) {
+          const int o = sidx[seg + tid];
+          any_iso = o >= 0 && o <= omax && o < a.Lk &&
+                    ((rbits[(o + 128) >> 5] >> ((o + 128) & 31)) & 1u) == 0u;
+        }
+        if (!__syncthreads_or(any_iso)) continue;
         const int cnt = compact(min(kSeg, s1 - seg),
                                 [&](int e) {
                                   const int o = sidx[seg + e];

@@ -36,6 +36,17 @@ def test_library_exports_symbol(name):
     assert hasattr(_lib(), name), f"libattn.so does not export {name}"
 
 
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The benchmark's read-rate probe sits in their own library; argument errors return
+    hipErrorInvalidValue (1) before any launch."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_attn_amd", "libattn_probes.so"))
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.probe_read_tiles.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    assert lib.probe_read_tiles(None, 1, 4, 8, 4096, 1, None) == 1
+    assert lib.probe_read_tiles(1, 1, 4, 8, 100, 1, None) == 1    # tile not a multiple of 16
+    assert lib.probe_read_tiles(1, 1, 0, 8, 4096, 1, None) == 1
+
+
 def test_status_strings():
     assert S.attn_status_string(0) == "ATTN_OK"
     assert S.attn_status_string(-1) == "ATTN_ERR_INVALID_ARG"
