@@ -101,6 +101,24 @@ def test_slashes_columns_blocks_overlap():
     _compare(q, k, v, bp, bi, cp, ci, sp, si, "union overlap")
 
 
+def test_wide_band_full_and_masked_tiles():
+    """A band of 300 offsets: run tiles wholly inside it take the unmasked tile math, those that
+    hold a listed column or cross the band's edges keep their masks; listed blocks inside the
+    band and columns below every row (gathered tiles without a mask) are counted once."""
+    B, Hq, Hkv, L, D = 1, 4, 2, 1500, 128
+    say("vslash: wide band, full and masked tiles")
+    q, k, v = _qkv(B, L, L, Hq, Hkv, D, 7150)
+    rng = np.random.default_rng(5)
+    nqb = -(-L // 64)
+    bp, bi = _csr([[max(qb - 2, 0)] + ([1] if qb % 3 == 0 else []) for _ in range(B * Hq)
+                   for qb in range(nqb)])
+    cp, ci = _csr([list(range(0, 64)) + [130, 500, 501, 900, 1400] + rng.choice(L, 12, False).tolist()
+                   for _ in range(B * Hq)])
+    sp, si = _csr([list(range(0, 300)) + rng.choice(np.arange(300, L), 8, False).tolist()
+                   for _ in range(B * Hq)])
+    _compare(q, k, v, bp, bi, cp, ci, sp, si, "wide band")
+
+
 def test_bottom_right_alignment_and_d64():
     B, Hq, Hkv, Lq, Lk, D = 1, 2, 1, 333, 1000, 64
     say("vslash: Lq < Lk, D 64")
