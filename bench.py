@@ -30,6 +30,10 @@ HEADLINE = "gqa_prefill_8k"
 # The headline's kernel (as rocprofv3 names it) and the sources its machine code comes from.
 DENSE_KERNEL = "fwd_dense_kernel<128, 1>"
 DENSE_SOURCES = ["fwd_dense.hip", "tile_io.hpp", "common.hpp", "kernels.hpp"]
+# The sparse prefill kernels (block-sparse and vertical-slash) and their sources: their figure of
+# merit beside the MFMA fraction is the rate of their L2-miss traffic against the read ceiling.
+SPARSE_SOURCES = ["fwd_blocksparse.hip", "tile_io.hpp", "common.hpp", "kernels.hpp"]
+SPARSE_WORKLOADS = ("blocksparse_128k", "vslash_128k")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -181,8 +185,8 @@ def read_ceilings():
     whole 32 KiB tiles (the K and V bytes of one 64-key tile at D = 128), read in order
     (a stream: each XCD reads distinct tiles) or at seeded random tile positions, from a 2 GiB
     region (HBM) and from a 128 MiB region re-read launch after launch (two KV heads' K and V
-    at 128K keys: larger than the eight 4 MiB L2s, inside the 256 MiB Infinity Cache). 2048 workgroups of 256 lanes, each
-    reading 16 tiles one after another."""
+    at 128K keys: larger than the eight 4 MiB L2s, inside the 256 MiB Infinity Cache).
+    2048 workgroups of 256 lanes, each reading 16 tiles one after another."""
     import torch
     lib = _probe_lib()
     grid, per_wg, tile = 2048, 16, 32 << 10
@@ -845,6 +849,19 @@ def main():
                 wl[name]["density_vs_causal"] = round(r["density_vs_causal"], 4)
             if "dynamic" in r:
                 wl[name]["dynamic_index"] = r["dynamic"]
+        if name in SPARSE_WORKLOADS:
+            # L2-miss traffic (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated, taken on the
+            # current kernel source) over this run's step time, against the read ceiling
+            sparse_hash = kernel_source_hash(SPARSE_SOURCES)
+            tb = load_traffic(name, sparse_hash)
+            entry = {"bytes_per_launch": tb, "kernel_source_sha256_16": sparse_hash}
+            if tb is not None:
+                entry["rate_gbs"] = round(tb / (r["ms"] * 1e-3) / 1e9, 1)
+                ceil = (ach or {}).get("read_ceilings", {}).get("infinity_cache_tile_gather_read_gbs")
+                if ceil:
+                    entry["read_ceiling_gbs"] = ceil
+                    entry["frac_of_read_ceiling"] = round(entry["rate_gbs"] / ceil, 4)
+            wl[name]["l2_miss_traffic"] = entry
     out["workloads"] = wl
     if not args.no_etap_grid and args.only is None:
         log("FlashMLA-ETAP decode grid ...")
