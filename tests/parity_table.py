@@ -1,8 +1,8 @@
 """Per-workload numerical-error table from the parity log the GPU tests write.
 
 Usage:
-    ATTN_PARITY_LOG=gpurun_out/parity.jsonl python -m pytest tests -m gpu
-    python tests/parity_table.py gpurun_out/parity.jsonl
+    ATTN_PARITY_LOG=/tmp/parity.jsonl python -m pytest tests -m gpu
+    python tests/parity_table.py /tmp/parity.jsonl
 
 Each line of the log is one check_parity call (tests/helpers.py) that named a workload: the GPU
 output against the fp64 oracle on the same seeded inputs. Calls of one workload (the 128K
