@@ -662,23 +662,42 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
     // the line at offset o meets rows q0..qlast at keys q0+off-o .. qlast+off-o (<= klim);
     // only lines inside a run of listed offsets go through the crossed tiles (isolated lines
     // take the window phase)
-    const int s1 = a.sl_ptr[bh + 1];
+    // The list entries of a chunk of kSetupJ * NT are loaded first, then their run bits, so a
+    // chunk costs two memory round trips rather than two per entry of each thread.
+    constexpr int kSetupJ = 8;
+    const int s0 = a.sl_ptr[bh], s1 = a.sl_ptr[bh + 1];
     const uint32_t* const rb = a.rl_bits + (int64_t)bh * a.bits_words;
-    for (int i = a.sl_ptr[bh] + tid; i < s1; i += NT) {
-      const int o = a.sl_idx[i];
-      const int hi = qlast + a.off - o;
-      if (o < 0 || hi < 0) continue;
-      if (((rb[(o + 128) >> 5] >> ((o + 128) & 31)) & 1u) == 0u) continue;
-      const int lo = max(0, q0 + a.off - o);
-      if (lo > lkm1) continue;
-      for (int kb = lo >> 6; kb <= (min(hi, lkm1) >> 6); ++kb)
-        atomicOr(&tbits[kb >> 5], 1u << (kb & 31));
+    for (int c = s0; c < s1; c += kSetupJ * NT) {
+      int o[kSetupJ];
+      uint32_t rw[kSetupJ];
+#pragma unroll
+      for (int j = 0; j < kSetupJ; ++j) {
+        const int i = c + j * NT + tid;
+        o[j] = i < s1 ? a.sl_idx[i] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kSetupJ; ++j) {
+        const bool in = o[j] >= 0 && o[j] <= qlast + a.off;
+        rw[j] = in ? rb[(o[j] + 128) >> 5] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kSetupJ; ++j) {
+        if (((rw[j] >> ((o[j] + 128) & 31)) & 1u) == 0u) continue;  // not in reach or isolated
+        const int hi = qlast + a.off - o[j];
+        const int lo = max(0, q0 + a.off - o[j]);
+        if (lo > lkm1) continue;
+        for (int kb = lo >> 6; kb <= (min(hi, lkm1) >> 6); ++kb)
+          atomicOr(&tbits[kb >> 5], 1u << (kb & 31));
+      }
     }
   }
   __syncthreads();
 
   // Ordered compaction: for the items i < n whose keep(i) holds, value(i) goes to kept[] in
   // the order of i; returns their count (the same in every wave).
+  // Passes over list entries hold one entry per thread (phases 2 and 3b read it once into a
+  // register and pass it to compact, which then evaluates entry tid in thread tid).
+  static_assert(kSeg == NT, "one list entry per thread in a pass");
   auto compact = [&](int n, auto keep_fn, auto value_fn) -> int {
     int cnt = 0;
     for (int rr = 0; rr < n; rr += NT) {
@@ -794,14 +813,16 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
   for (int seg = 0; seg < ncols; seg += kSeg) {
     if (cidx[seg] > klim) break;  // sorted: nothing further is visible
     const int n = min(kSeg, ncols - seg);
+    // thread tid's column of the pass, read once (compact evaluates entry tid in thread tid)
+    const int my_col = tid < n ? cidx[seg + tid] : -1;
     const int cnt = compact(n,
-                            [&](int i) {
-                              const int col = cidx[seg + i];
+                            [&](int) {
+                              const int col = my_col;
                               if (col < 0 || col > klim) return false;
                               return ((all_word(col >> 11) >> ((col >> 6) & 31)) & 1u) == 0u;
                             },
-                            [&](int i) {
-                              const int col = cidx[seg + i];
+                            [&](int) {
+                              const int col = my_col;
                               int e = col;
 #pragma unroll
                               for (int q = 0; q < QB; ++q)
@@ -928,28 +949,29 @@ __global__ __launch_bounds__(2 * QB * 64, 2) void fwd_sparse_kernel(const FwdArg
       const int jdiag = (((i >> 2) & 1) == h) ? 4 * (i >> 3) + (i & 3) : -1;
       const int s0 = a.sl_ptr[bh], s1 = a.sl_ptr[bh + 1];
       const int omax = qlast + a.off;  // larger offsets meet no row of the group
-      static_assert(kSeg == NT, "one list entry per thread in the emptiness test");
       for (int seg = s0; seg < s1; seg += kSeg) {
         if (sidx[seg] > omax) break;  // ascending
-        // a pass with no isolated offset in reach is skipped after one barrier
-        bool any_iso = false;
+        // Thread tid holds entry seg + tid of the pass: its offset, read once, and whether it is
+        // an isolated line in reach. A pass without one is skipped after one barrier.
+        int my_o = -1;
+        bool my_iso = false;
         if (seg + tid < s1) {
-          const int o = sidx[seg + tid];
-          any_iso = o >= 0 && o <= omax && o < a.Lk &&
-                    ((rbits[(o + 128) >> 5] >> ((o + 128) & 31)) & 1u) == 0u;
+          my_o = sidx[seg + tid];
+          my_iso = my_o >= 0 && my_o <= omax && my_o < a.Lk &&
+                   ((rbits[(my_o + 128) >> 5] >> ((my_o + 128) & 31)) & 1u) == 0u;
         }
-        if (!__syncthreads_or(any_iso)) continue;
-        const int cnt = compact(min(kSeg, s1 - seg),
-                                [&](int e) {
-                                  const int o = sidx[seg + e];
-                                  if (o < 0 || o > omax || o >= a.Lk) return false;
-                                  return ((rbits[(o + 128) >> 5] >> ((o + 128) & 31)) & 1u) == 0u;
-                                },
-                                [&](int e) { return sidx[seg + e]; });
+        if (!__syncthreads_or(my_iso)) continue;
+        // with kSeg == NT, compact evaluates entry e = tid in thread tid
+        const int cnt = compact(min(kSeg, s1 - seg), [&](int) { return my_iso; },
+                                [&](int) { return my_o; });
         if (active) {
-          // lines 0 .. n-1 of this pass reach the wave's rows (ascending offsets)
+          // lines 0 .. n-1 of this pass reach the wave's rows: kept[] ascends, so they are the
+          // entries at or below the wave's last row's offset limit, counted by ballots
           int n = 0;
-          while (n < cnt && kept[n] <= qwlast + a.off) ++n;
+          for (int i0 = 0; i0 < cnt; i0 += 64) {
+            const int i = i0 + l;
+            n += __popcll(__ballot(i < cnt && kept[i] <= qwlast + a.off));
+          }
           n = __builtin_amdgcn_readfirstlane(n);  // wave-uniform: scalar loop control
           // Software pipeline over the wave's lines: K (with its column words) of line t+1 is
           // copied during the softmax and P·V of line t, V of line t+1 during the scores of
