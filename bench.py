@@ -180,6 +180,8 @@ def _probe_lib():
     vp, i32 = ctypes.c_void_p, ctypes.c_int
     lib.probe_read_tiles.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.probe_read_tiles.restype = i32
+    lib.probe_read_rows.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp, vp]
+    lib.probe_read_rows.restype = i32
     return lib
 
 
@@ -287,9 +289,53 @@ def bench_decode(w, steps, warmup):
         S.attn_fwd_decode(qd, ks[i], vs[i], o, lse, causal=w.causal, scale=w.scale, workspace=ws)
 
     ms, wall = time_steps(step, steps, warmup)
+    times = dict(STEP_TIMES)
     nbytes = kv_bytes + q.numel() * 2 + o.numel() * 2 + lse.numel() * 4
+    try:
+        floor = decode_read_floor(w, nsp, ks, None if w.mla else vs, kv_bytes, steps, warmup)
+    except OSError as e:  # the probe library was not built: report it, keep the rest
+        floor = {"error": f"libattn_probes.so not loaded ({e})"}
     return {"ms": ms, "wall_s": wall, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
-            "num_splits": nsp, "kv_copies": ncopies, **STEP_TIMES}
+            "num_splits": nsp, "kv_copies": ncopies, "read_floor": floor, **times}
+
+
+def decode_read_floor(w, nsp, ks, vs, kv_bytes, steps, warmup):
+    """The time a plain read of exactly the cache rows the split kernel reads takes
+    (libattn_probes.so `probe_read_rows`): one workgroup per (batch, split, KV head) in the split
+    kernel's order (KV head fastest), each reading its split's K rows (and V rows, unless V is
+    the latent itself) with 16-byte loads, over the same KV copies in the same rotation. It has
+    no softmax, no MFMA, no LDS and no combine, so the decode step's time over it is what the
+    kernels add to moving the bytes. Only for shapes whose workgroups each take one column block
+    and a whole split of visible keys (None otherwise)."""
+    import torch
+    g = w.Hq // w.Hkv
+    chunk = 64 * -(-(-(-w.Lk // nsp)) // 64)
+    if g * w.Lq > 16 or w.Lk % chunk or (w.causal and w.Lq > 1) or (vs and w.Dv != w.Dqk):
+        return None
+    lib = _probe_lib()
+    lid = torch.arange(w.B * nsp * w.Hkv, dtype=torch.int64)
+    hkv, sp, b = lid % w.Hkv, (lid // w.Hkv) % nsp, lid // (w.Hkv * nsp)
+    row_bytes, stride = w.Dqk * 2, w.Hkv * w.Dqk * 2
+    base = (((b * w.Lk + sp * chunk) * w.Hkv + hkv) * row_bytes).to("cuda:0")
+    sink = torch.zeros(lid.numel() * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in ks + (vs or []):
+        assert t.is_contiguous() and t.shape == (w.B, w.Lk, w.Hkv, w.Dqk)
+    it = [0]
+
+    def step():
+        i = it[0] % len(ks)
+        it[0] += 1
+        rc = lib.probe_read_rows(ks[i].data_ptr(), vs[i].data_ptr() if vs else None,
+                                 base.data_ptr(), lid.numel(), chunk, row_bytes, stride,
+                                 sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"read probe launch failed: hipError {rc}")
+
+    ms, _ = time_steps(step, steps, warmup)
+    return {"ms": round(ms, 4), "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+            "probe": (f"probe_read_rows: {lid.numel()} workgroups x {chunk} rows of {row_bytes} B "
+                      f"at stride {stride} B" + (", K and V" if vs else ", latent only"))}
 
 
 def bench_blocksparse(w, steps, warmup, dynamic=True):
@@ -845,6 +891,11 @@ def main():
                         "num_splits": r["num_splits"], "bytes": r["bytes"]}
             if ach:
                 wl[name]["frac_of_achievable"] = round(r["gbs"] / ach["hbm_copy_gbs"], 4)
+            fl = r.get("read_floor")
+            if fl is not None:
+                wl[name]["read_floor"] = fl
+                if "ms" in fl:
+                    wl[name]["frac_of_read_floor"] = round(fl["ms"] / r["ms"], 4)
         else:
             wl[name] = {"value": round(r["tflops"], 3), "unit": "TFLOP/s", "ms": round(r["ms"], 4),
                         **pct, "frac_of_mfma_peak": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -10,6 +10,9 @@
 // eight L2s together (8 x 4 MiB) but well inside the 256 MiB Infinity Cache, launches after the
 // first measure the Infinity Cache.
 //
+// probe_read_rows: every workgroup reads strided rows of one or two buffers, as one split-KV
+// workgroup reads its keys' K and V rows; the decode kernels' step time is compared with it.
+//
 // Each lane folds what it reads into one word and writes it only if it equals a value no input
 // produces in practice, so the loads cannot be dropped and the probe writes (almost) nothing.
 
@@ -25,6 +28,9 @@ constexpr int kUnroll = 8;
 constexpr uint32_t kNever = 0x9e3779b9u;
 
 __device__ inline uint32_t fold(uint4 v) { return v.x ^ (v.y * 3u) ^ (v.z * 5u) ^ (v.w * 7u); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a register-operand type for asm
+__device__ inline uint32_t fold(u32x4 v) { return v.x ^ (v.y * 3u) ^ (v.z * 5u) ^ (v.w * 7u); }
 
 // Tiles of tile16 16-byte chunks; workgroup g reads tiles ids[g * per_wg + t], t < per_wg.
 __global__ __launch_bounds__(kThreads) void read_tiles_kernel(const uint4* __restrict__ buf,
@@ -48,6 +54,51 @@ __global__ __launch_bounds__(kThreads) void read_tiles_kernel(const uint4* __res
   if (acc == kNever) sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// Rows of row16 16-byte chunks at a byte stride: workgroup g reads rows [0, nrows) from byte
+// base[g] of `a`, and of `b` unless it is null, 64 rows at a time (the tile's chunks of `a`, then
+// those of `b`). The chunks are numbered in that order and dealt out over the lanes, kRowsUnroll
+// loads in flight per lane (a split-KV workgroup keeps up to four 36 KiB tiles in flight, so
+// eight per lane, 32 KiB per workgroup, would understate what one workgroup per CU can read).
+// The index is clamped rather than the load made conditional, so the loads stay independent.
+constexpr int kRowsUnroll = 32;
+
+__global__ __launch_bounds__(kThreads) void read_rows_kernel(const char* __restrict__ a,
+                                                             const char* __restrict__ b,
+                                                             const int64_t* __restrict__ base,
+                                                             int nrows, int row16, int64_t stride,
+                                                             uint32_t* __restrict__ sink) {
+  const int64_t b0 = base[blockIdx.x];
+  const int per_t = 64 * row16;                 // chunks of one buffer in a 64-row tile
+  const int per_tile = b ? 2 * per_t : per_t;
+  const int n = (nrows / 64) * per_tile;
+  uint32_t acc = 0;
+  for (int j0 = 0; j0 < n; j0 += kRowsUnroll * kThreads) {
+    u32x4 v[kRowsUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowsUnroll; ++u) {
+      const int j = min(j0 + u * kThreads + (int)threadIdx.x, n - 1);
+      const int t = j / per_tile;
+      const int rem = j - t * per_tile;
+      const bool second = rem >= per_t;
+      const int jj = second ? rem - per_t : rem;
+      const int r = jj / row16, c = jj - r * row16;
+      const char* src = second ? b : a;
+      v[u] = *reinterpret_cast<const u32x4*>(src + b0 + (int64_t)(t * 64 + r) * stride +
+                                             (int64_t)c * 16);
+    }
+    // Every load of the batch is issued before the first fold waits for one: the empty asm
+    // statements take the loaded registers as operands after a scheduling barrier, so the folds
+    // (which the compiler would otherwise interleave with the loads) cannot move above them.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kRowsUnroll; u += 4)
+      asm volatile("" : "+v"(v[u]), "+v"(v[u + 1]), "+v"(v[u + 2]), "+v"(v[u + 3]));
+#pragma unroll
+    for (int u = 0; u < kRowsUnroll; ++u) acc += fold(v[u]);
+  }
+  if (acc == kNever) sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +114,23 @@ int probe_read_tiles(const void* buf, const int32_t* ids, int per_wg, int grid, 
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_tiles_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                      (const uint4*)buf, ids, per_wg, tile_bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// Reads, in each of `grid` workgroups g, the rows r < nrows (a multiple of 64) of `row_bytes`
+// bytes (a multiple of 16) that start at byte base[g] + r * stride of `a`, and of `b` at the same
+// offsets unless `b` is null: the access pattern of one split-KV workgroup over a [B, L, H, D]
+// cache. `base` is
+// device memory of `grid` byte offsets; the caller keeps every row inside both buffers. `sink`
+// is device memory of grid * 256 words that the kernel may write. Returns a hipError_t value
+// (0 on success).
+int probe_read_rows(const void* a, const void* b, const int64_t* base, int grid, int nrows,
+                    int row_bytes, int64_t stride, uint32_t* sink, void* stream) {
+  if (!a || !base || !sink || grid <= 0 || nrows <= 0 || nrows % 64 || row_bytes <= 0 ||
+      row_bytes % 16 || stride < row_bytes)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_rows_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const char*)a, (const char*)b, base, nrows, row_bytes / 16, stride, sink);
   return (int)hipGetLastError();
 }
 

@@ -45,6 +45,13 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.probe_read_tiles(None, 1, 4, 8, 4096, 1, None) == 1
     assert lib.probe_read_tiles(1, 1, 4, 8, 100, 1, None) == 1    # tile not a multiple of 16
     assert lib.probe_read_tiles(1, 1, 0, 8, 4096, 1, None) == 1
+    lib.probe_read_rows.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp, vp]
+    assert lib.probe_read_rows(None, None, 1, 8, 64, 256, 2048, 1, None) == 1
+    assert lib.probe_read_rows(1, None, None, 8, 64, 256, 2048, 1, None) == 1
+    assert lib.probe_read_rows(1, 1, 1, 8, 64, 250, 2048, 1, None) == 1  # row not 16-byte whole
+    assert lib.probe_read_rows(1, 1, 1, 8, 64, 256, 128, 1, None) == 1   # rows would overlap
+    assert lib.probe_read_rows(1, 1, 1, 8, 0, 256, 2048, 1, None) == 1
+    assert lib.probe_read_rows(1, 1, 1, 8, 100, 256, 2048, 1, None) == 1  # not whole 64-row tiles
 
 
 def test_status_strings():
