@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import numpy as np
@@ -148,40 +149,53 @@ def _check(fn: str, status: int):
 
 
 # ------------------------------------------------------------------------------------ helpers
+# The helpers below run on every call, so they keep Python work small: torch is looked up once,
+# each tensor's strides are read in one call, and the stream comes from torch's raw-stream query
+# (the one its own generated kernels use) instead of building a Stream object.
+_TORCH = None
+_RAW_STREAM = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _TORCH, _RAW_STREAM
+    if _TORCH is None:
+        import torch
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _TORCH = torch
+    return _TORCH
 
 
 def _tensor_desc(t, name):
-    torch = _torch()
-    if t.dtype != torch.bfloat16:
+    if t.dtype != _torch().bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
-    if t.dim() != 4:
+    st = t.stride()
+    if len(st) != 4:
         raise ValueError(f"{name} must be [B, L, H, D], got shape {tuple(t.shape)}")
-    if t.stride(3) != 1:
+    if st[3] != 1:
         raise ValueError(f"{name} must have a contiguous head dimension")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    return AttnTensorC(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+    return AttnTensorC(t.data_ptr(), st[0], st[1], st[2])
 
 
 def _opt_ptr(t, name, dtype_name="float32"):
     if t is None:
         return None
-    torch = _torch()
-    if t.dtype != getattr(torch, dtype_name):
+    if t.dtype != getattr(_torch(), dtype_name):
         raise TypeError(f"{name} must be {dtype_name}")
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous GPU tensor")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _stream(stream, device):
+    """The HIP stream to launch on: the caller's, else torch's current stream on `device`."""
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return int(stream)
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _RAW_STREAM is not None and device.index is not None:
+        return _RAW_STREAM(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 # Shape checks. The C ABI receives raw pointers and cannot see buffer sizes, so every wrapper
@@ -217,10 +231,11 @@ def _numel(t, name, n):
 
 
 def _one_device(named):
-    devs = {str(t.device) for _, t in named if t is not None}
-    if len(devs) > 1:
-        names = ", ".join(f"{n}: {t.device}" for n, t in named if t is not None)
-        raise ValueError(f"all tensors must be on one device ({names})")
+    d0 = named[0][1].device
+    for _, t in named:
+        if t is not None and t.device != d0:
+            names = ", ".join(f"{n}: {t.device}" for n, t in named if t is not None)
+            raise ValueError(f"all tensors must be on one device ({names})")
 
 
 def _qkv_sizes(q, k, v):
@@ -331,6 +346,7 @@ def splitkv_decode(q, k, v, o, lse=None, causal=False, scale=None, num_splits=No
     return o
 
 
+@functools.lru_cache(maxsize=256)
 def attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv) -> int:
     return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, Dqk, Dv))
 
