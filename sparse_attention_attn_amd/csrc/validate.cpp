@@ -103,27 +103,28 @@ int check_num_splits(const char* fn, int num_splits, int Lk) {
 int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   (void)Dv;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
-  constexpr int kCUs = 256;  // MI355X
   const int g = Hq / Hkv;
   const int cols = split_cols(Dqk, g * Lq);
   const int64_t colblk = ((int64_t)g * Lq + cols - 1) / cols;
   const int64_t units = (int64_t)B * Hkv * colblk;
-  // resident workgroups per CU (LDS ring: 64 KiB for D = 64 and 128, 128-144 KiB for the
-  // latent shape); D = 128 also asks for two rounds of them, the measured best on the batched
-  // 4K GQA decode (8 splits: 49.7 us, 4 splits: 50.8 us)
-  const int wg_per_cu = (Dqk == 576) ? 1 : 2;
-  const int rounds = (Dqk == 128) ? 2 : 1;
-  int64_t s = ((int64_t)kCUs * wg_per_cu * rounds + units - 1) / units;
-  // at least 256 keys per split, 128 for the latent shape: its 1152-byte rows make a 128-key
-  // split 144 KiB, and short latent caches gain from the extra workgroups (B 16, 512 keys:
-  // 18.5 -> 15.5 us), while for D = 128 more, shorter splits lose (B 16, 1K keys: 16.5 -> 19.1)
-  const int min_keys = (Dqk == 576) ? 128 : 256;
+  // Grid size and keys per split, measured over B 1..64, 512..131072 keys and the three head
+  // shapes (GPU time per call, splits forced from 1 to 512): the best grids hold one round of
+  // two D = 128 workgroups per CU (512), one D = 64 or latent workgroup per CU (256); a split
+  // keeps at least one 64-key tile (two for the latent, whose 1152-byte rows make short splits
+  // pay for their partials), and more than 256 splits only adds combine work (B 1, one KV head,
+  // 131072 keys: 24.4 us at 256 splits, 26.1 at 512).
+  const int64_t grid = (Dqk == 128) ? 512 : 256;
+  const int min_keys = (Dqk == 576) ? 128 : 64;
+  int64_t s = (grid + units - 1) / units;
   const int64_t max_by_len = std::max<int64_t>(1, Lk / min_keys);
   const int64_t max_s = (Lk + 63) / 64;
   s = std::min(s, max_by_len);
   s = std::min(s, max_s);
+  s = std::min<int64_t>(s, 256);
   s = std::max<int64_t>(s, 1);
-  return (int)s;
+  // splits are whole 64-key tiles: drop those the rounding of the split length leaves empty
+  const int chunk = split_chunk(Lk, (int)s);
+  return (int)((Lk + chunk - 1) / chunk);
 }
 
 int split_chunk(int Lk, int num_splits) {

@@ -141,8 +141,10 @@ def test_blocksparse_entry_validation():
 def test_decode_entry_validation_and_workspace():
     lib = _lib()
     need = S.attn_decode_workspace_bytes(16, 32, 8, 1, 4096, 128, 128)
-    # the two partial buffers of attn_fwd_splitkv (2 splits), each 256-byte aligned
-    part = S.attn_splitkv_workspace_bytes(16, 32, 1, 128, 8)
+    # the two partial buffers of attn_fwd_splitkv at the picked split count, each 256-byte
+    # aligned
+    nsp = S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128)
+    part = S.attn_splitkv_workspace_bytes(16, 32, 1, 128, nsp)
     assert part <= need <= part + 2 * 256
     assert S.attn_decode_workspace_bytes(0, 32, 8, 1, 4096, 128, 128) == 0
     f = lambda ws=FAKE, nb=need: lib.attn_fwd_decode(
@@ -155,9 +157,9 @@ def test_decode_entry_validation_and_workspace():
 
 
 def test_num_splits_heuristic_is_pure_and_in_range():
-    # the decode workloads: 128 (b, kv-head) units -> 8 splits (two rounds of two workgroups
+    # the decode workloads: 128 (b, kv-head) units -> 4 splits (one round of two workgroups
     # per CU); 8 units of MLA -> 32 splits
-    assert S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128) == 8
+    assert S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128) == 4
     assert S.attn_splitkv_num_splits(8, 16, 1, 1, 65536, 576, 512) == 32
     for args in [(1, 1, 1, 1, 1, 64, 64), (1, 8, 1, 1, 100, 128, 128), (64, 64, 8, 1, 30, 64, 64),
                  (1, 16, 1, 2, 1 << 20, 576, 512)]:

@@ -58,7 +58,7 @@ def test_decode_one_call_mla_workload():
 
 
 @pytest.mark.parametrize("shape", [(1, 16, 1, 2, 200, 576, 512, True),
-                                   (2, 8, 2, 1, 300, 64, 64, False)],
+                                   (64, 8, 4, 1, 300, 64, 64, False)],
                          ids=["mla_lq2_two_colblocks", "d64"])
 def test_decode_one_call_direct_path(shape):
     """One split: the split kernel writes O and LSE itself. The MLA shape with two query tokens
@@ -80,7 +80,8 @@ SHAPES = [
     (2, 16, 4, 2, 3000, 128, True),     # two query tokens, bottom-right causal
     (5, 8, 8, 1, 777, 64, False),
     (2, 6, 2, 3, 2049, 64, True),
-    (2, 16, 4, 2, 300, 128, True),      # one split (under 512 keys): O and LSE written directly
+    (2, 16, 4, 2, 300, 128, True),      # short splits: 128, 128 and 44 keys
+    (2, 16, 4, 2, 100, 128, True),      # one split (under 128 keys): O and LSE written directly
     (128, 32, 8, 1, 1024, 128, False),  # one split (1024 units fill the GPU): direct too
 ]
 
@@ -149,7 +150,7 @@ def test_decode_one_split_equals_partials_path():
     followed by attn_combine_lse, bit for bit."""
     import torch
     import sparse_attention_attn_amd as S
-    B, Hq, Hkv, Lq, Lk, D = 2, 16, 4, 2, 300, 128
+    B, Hq, Hkv, Lq, Lk, D = 128, 16, 4, 2, 300, 128   # 512 (b, KV head) units: one split
     say("one split: direct outputs vs partials + combine")
     q = randn_bf16((B, Lq, Hq, D), 8710).to(DEV)
     k = randn_bf16((B, Lk, Hkv, D), 8711).to(DEV)
