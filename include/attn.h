@@ -102,9 +102,10 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
  * Supported head dims: (64, 64), (128, 128) and the MLA latent (576, 512).
  */
 
-/* Split count the library would pick for MI355X (256 CUs): enough workgroups to fill the chip
- * while each split keeps at least a few 64-key tiles. Pure function of its arguments; returns
- * a value in [1, ceil(Lk/64)], or ATTN_ERR_INVALID_ARG for sizes < 1. */
+/* Split count the library would pick for MI355X (256 CUs): one round of workgroups over the
+ * chip (two per CU for D = 128, one otherwise), each split at least one 64-key tile (two for the
+ * latent shape), at most 256 splits, none empty. Pure function of its arguments; returns a
+ * value in [1, ceil(Lk/64)], or ATTN_ERR_INVALID_ARG for sizes < 1. */
 int attn_splitkv_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
 /* Bytes of o_part plus lse_part for these sizes (0 on invalid sizes). */
