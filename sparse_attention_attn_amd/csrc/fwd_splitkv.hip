@@ -67,7 +67,7 @@ using ic = std::integral_constant<int, N>;
 template <int DQK, int DV, int BNK, int NST, int NCB>
 __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   using C = SplitCfg<DQK, DV, BNK, NST>;
-  static_assert(NCB == 1 || C::MLA, "two column blocks per workgroup only for the MLA shape");
+  static_assert(NCB == 1 || NCB == 2, "one or two 16-column blocks per workgroup");
   static_assert(NST >= 2 && NST <= 6, "2..6 stages");
   // One array per ring stage: with the stage fixed at compile time the compiler can tell the
   // stage being read from the stages still being filled, and does not wait for those copies.
@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
         constexpr int s = decltype(SI)::value;
 #pragma unroll
         for (int k = 0; k < C::KBLK; ++k)
-          st[0][k] = mfma16(kr[s % (RA + 1)][k], qop[0][s], st[0][k]);
+#pragma unroll
+          for (int c = 0; c < NCB; ++c)
+            st[c][k] = mfma16(kr[s % (RA + 1)][k], qop[c][s], st[c][k]);
         // refill the slot consumed one step earlier
         if constexpr (s + RA < C::QSTEPS) {
 #pragma unroll
@@ -604,8 +606,12 @@ hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t strea
   }
   // D = 128: a 2-stage ring (64 KiB of LDS) so that two workgroups share a CU; measured on
   // B 16, Hq 32, Hkv 8, Lk 4096 against 4 stages at one workgroup per CU: 49.7 vs 52.5 us.
-  if (dqk == 128) return launch_split_t<128, 128, 64, 2, 1>(a, stream);
-  return launch_split_t<64, 64, 64, 4, 1>(a, stream);
+  const bool two = split_cols(dqk, a.g * a.Lq) == 32;
+  if (dqk == 128)
+    return two ? launch_split_t<128, 128, 64, 2, 2>(a, stream)
+               : launch_split_t<128, 128, 64, 2, 1>(a, stream);
+  return two ? launch_split_t<64, 64, 64, 4, 2>(a, stream)
+             : launch_split_t<64, 64, 64, 4, 1>(a, stream);
 }
 
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream) {

@@ -1,7 +1,9 @@
 """GPU parity at GQA ratios beyond the sweeps' 1..8: 16, 32 and 64 query heads per KV head
-(multi-query attention at the far end). Decode then spreads one KV head's query columns over
-several 16-column blocks (g * Lq up to 128 columns), and prefill and block-sparse map many
-query heads onto one K/V stream. Compared element by element with the fp64 oracle."""
+(multi-query attention at the far end), and decode shapes with more than 16 query columns per
+KV head (heads of the group times query tokens). Decode then runs one workgroup over two
+16-column blocks, up to four such workgroups per KV head (g * Lq up to 128 columns), and
+prefill and block-sparse map many query heads onto one K/V stream. Compared element by element
+with the fp64 oracle."""
 
 import numpy as np
 import pytest
@@ -38,7 +40,11 @@ def test_prefill_wide_groups(shape):
 
 
 @pytest.mark.parametrize("shape", [(4, 16, 1, 1, 3000, 128), (2, 32, 1, 2, 1500, 128),
-                                   (3, 64, 1, 2, 777, 64), (2, 64, 2, 1, 4100, 128)],
+                                   (3, 64, 1, 2, 777, 64), (2, 64, 2, 1, 4100, 128),
+                                   # 17..32 columns per KV head: one workgroup takes both
+                                   # 16-column blocks, the second one partly filled
+                                   (3, 24, 2, 2, 999, 128), (2, 8, 1, 3, 2000, 128),
+                                   (1, 32, 4, 4, 513, 64), (2, 40, 2, 1, 1000, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_decode_wide_groups(shape):
     import torch
