@@ -13,6 +13,9 @@
 // probe_read_rows: every workgroup reads strided rows of one or two buffers, as one split-KV
 // workgroup reads its keys' K and V rows; the decode kernels' step time is compared with it.
 //
+// probe_mfma_stream: back-to-back bf16 MFMAs on random operands, the rate the matrix cores
+// sustain at the power limit (the prefill kernels' compute ceiling in practice).
+//
 // Each lane folds what it reads into one word and writes it only if it equals a value no input
 // produces in practice, so the loads cannot be dropped and the probe writes (almost) nothing.
 
@@ -99,6 +102,44 @@ __global__ __launch_bounds__(kThreads) void read_rows_kernel(const char* __restr
   if (acc == kNever) sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
 
+// MFMA stream: every wave runs `iters` rounds of 32x32x16 bf16 MFMAs, eight operand pairs
+// (loaded once from `in`) against four independent accumulator chains, so nothing but the
+// matrix core bounds the issue rate. The operands are the caller's random bits: on this part
+// the MFMA rate follows the clock, and the clock follows the power the operand data draws
+// (zero operands run faster than any real input).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kMfmaThreads = 512;
+constexpr int kMfmaPairs = 8;
+constexpr int kMfmaChains = 4;
+
+__global__ __launch_bounds__(kMfmaThreads) void mfma_stream_kernel(const u32x4* __restrict__ in,
+                                                                   int iters,
+                                                                   uint32_t* __restrict__ sink) {
+  const int l = threadIdx.x & 63;
+  bf16x8_t a[kMfmaPairs], b[kMfmaPairs];
+#pragma unroll
+  for (int j = 0; j < kMfmaPairs; ++j) {
+    a[j] = __builtin_bit_cast(bf16x8_t, in[(2 * j) * 64 + l]);
+    b[j] = __builtin_bit_cast(bf16x8_t, in[(2 * j + 1) * 64 + l]);
+  }
+  f32x16_t acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = f32x16_t{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kMfmaPairs; ++j)
+#pragma unroll
+      for (int c = 0; c < kMfmaChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[c], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) r += acc[c][l & 15];
+  if (__builtin_bit_cast(uint32_t, r) == kNever)
+    sink[(size_t)blockIdx.x * kMfmaThreads + threadIdx.x] = kNever;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +172,17 @@ int probe_read_rows(const void* a, const void* b, const int64_t* base, int grid,
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_rows_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                      (const char*)a, (const char*)b, base, nrows, row_bytes / 16, stride, sink);
+  return (int)hipGetLastError();
+}
+
+// Runs `grid` workgroups of 512 lanes (8 waves), each wave doing iters * 32 MFMAs of
+// 32x32x16 bf16 (32768 flops each) on operands read from `in`: device memory of 16 * 64
+// 16-byte words (random bf16 bits). `sink` is device memory of grid * 512 words that the kernel
+// may write. Flops per launch: grid * 8 * iters * 32 * 32768. Returns a hipError_t value.
+int probe_mfma_stream(const void* in, int grid, int iters, uint32_t* sink, void* stream) {
+  if (!in || !sink || grid <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_stream_kernel, dim3(grid), dim3(kMfmaThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)in, iters, sink);
   return (int)hipGetLastError();
 }
 

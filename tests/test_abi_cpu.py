@@ -52,6 +52,10 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.probe_read_rows(1, 1, 1, 8, 64, 256, 128, 1, None) == 1   # rows would overlap
     assert lib.probe_read_rows(1, 1, 1, 8, 0, 256, 2048, 1, None) == 1
     assert lib.probe_read_rows(1, 1, 1, 8, 100, 256, 2048, 1, None) == 1  # not whole 64-row tiles
+    lib.probe_mfma_stream.argtypes = [vp, i32, i32, vp, vp]
+    assert lib.probe_mfma_stream(None, 8, 10, 1, None) == 1
+    assert lib.probe_mfma_stream(1, 0, 10, 1, None) == 1
+    assert lib.probe_mfma_stream(1, 8, 0, 1, None) == 1
 
 
 def test_status_strings():
