@@ -394,7 +394,10 @@ def bench_blocksparse(w, steps, warmup, dynamic=True):
     if not dynamic:
         return res
     # The same attention with lists built from Q and K at run time (attn_build_sparse_index:
-    # 96 blocks per query block, 1000 columns per head, about the synthetic lists' density).
+    # 96 blocks per query block, 1000 columns per head, about the synthetic lists' density),
+    # on the workload's noise inputs (nothing for the builder to find) and on inputs with a
+    # planted band and planted columns (make_structured_qk).
+    from workloads import make_structured_qk
     topk, ncols = 96, 1000
     nb, nc = S.attn_sparse_index_sizes(w.B, w.Hq, w.Lq, topk, ncols)
     nqb = -(-w.Lq // 64)
@@ -404,21 +407,31 @@ def bench_blocksparse(w, steps, warmup, dynamic=True):
             torch.empty(nc, dtype=torch.int32, device="cuda:0"))
     ws = torch.empty(S.attn_sparse_index_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Dqk),
                      dtype=torch.uint8, device="cuda:0")
-    build = lambda: S.attn_build_sparse_index(q, k, topk, ncols, scale=w.scale, outputs=outs,
-                                              workspace=ws)
-    ms_b, _ = time_steps(build, steps, warmup)
-    built = build()
-    torch.cuda.synchronize()
-    step_d = lambda: (build(), S.attn_fwd_blocksparse(q, k, v, o, *built, lse=lse, causal=True,
-                                                      scale=w.scale))
-    ms_d, _ = time_steps(step_d, steps, warmup)
-    hl = [t.cpu().numpy() for t in built]
-    pairs_d = blocksparse_pairs(hl, w.B, w.Hq, w.Lq)
-    flops_d = 2 * (w.Dqk + w.Dv) * pairs_d
-    res["dynamic"] = {"index_build_ms": round(ms_b, 4), "build_plus_attention_ms": round(ms_d, 4),
-                      "topk_blocks": topk, "n_cols": ncols,
-                      "density_vs_causal": round(pairs_d / dense, 4),
-                      "tflops_incl_build": round(flops_d / (ms_d * 1e-3) / 1e12, 3)}
+
+    def dynamic(qd, kd, inputs):
+        build = lambda: S.attn_build_sparse_index(qd, kd, topk, ncols, scale=w.scale,
+                                                  outputs=outs, workspace=ws)
+        ms_b, _ = time_steps(build, steps, warmup)
+        built = build()
+        torch.cuda.synchronize()
+        step_d = lambda: (build(), S.attn_fwd_blocksparse(qd, kd, v, o, *built, lse=lse,
+                                                          causal=True, scale=w.scale))
+        ms_d, _ = time_steps(step_d, steps, warmup)
+        hl = [t.cpu().numpy() for t in built]
+        pairs_d = blocksparse_pairs(hl, w.B, w.Hq, w.Lq)
+        flops_d = 2 * (w.Dqk + w.Dv) * pairs_d
+        return {"inputs": inputs, "index_build_ms": round(ms_b, 4),
+                "build_plus_attention_ms": round(ms_d, 4), "topk_blocks": topk, "n_cols": ncols,
+                "density_vs_causal": round(pairs_d / dense, 4),
+                "tflops_incl_build": round(flops_d / (ms_d * 1e-3) / 1e12, 3)}
+
+    res["dynamic"] = dynamic(q, k, "the workload's Q and K (N(0, 1) noise: no structure)")
+    qs, kst = make_structured_qk(w.B, w.Lq, w.Hq, w.Hkv, w.Dqk, 1000 * w.index + 5, window=6144,
+                                 scale=w.scale)
+    res["dynamic_structured"] = dynamic(
+        qs, kst, "make_structured_qk: noise plus a planted band (window 6144, rise 6) and 1000 "
+                 "planted columns per KV head (rise 8)")
+    del qs, kst
     return res
 
 
@@ -448,8 +461,10 @@ def bench_vslash(w, steps, warmup, dynamic=True):
     if not dynamic:
         return res
     # Lists built from Q and K at run time (attn_build_vslash_index), as many columns and lines
-    # as the synthetic lists. Random inputs have no diagonal structure, so the chosen lines
-    # scatter over all offsets and the forward then visits nearly every causal block.
+    # as the synthetic lists. On the workload's noise inputs the chosen lines scatter over all
+    # offsets (the forward then reads a K/V window per line and row block); on inputs with a
+    # planted band and planted columns (make_structured_qk) they gather in the band.
+    from workloads import make_structured_qk
     ncols, nslash = 1000, int(sp[1] - sp[0])
     nc, ns = w.B * w.Hq * min(ncols, w.Lk), w.B * w.Hq * min(nslash, w.Lk)
     outs = (torch.empty(w.B * w.Hq + 1, dtype=torch.int32, device="cuda:0"),
@@ -458,21 +473,37 @@ def bench_vslash(w, steps, warmup, dynamic=True):
             torch.empty(ns, dtype=torch.int32, device="cuda:0"))
     iws = torch.empty(S.attn_sparse_index_workspace_bytes(w.B, w.Hq, w.Hkv, w.Lq, w.Dqk),
                       dtype=torch.uint8, device="cuda:0")
-    build = lambda: S.attn_build_vslash_index(q, k, ncols, nslash, scale=w.scale, outputs=outs,
-                                              workspace=iws)
-    ms_b, _ = time_steps(build, steps, warmup)
-    bcp, bci, bsp, bsi = build()
-    step_d = lambda: (build(), S.attn_fwd_vertical_slash(q, k, v, o, bp, bi, bcp, bci, bsp, bsi,
-                                                         lse=lse, causal=True, scale=w.scale,
-                                                         workspace=ws))
-    ms_d, _ = time_steps(step_d, 2, 1)
-    hl = [t.cpu().numpy() for t in (bsp, bsi, bcp, bci)]
-    pairs_d = vslash_pairs(*hl, w.B, w.Hq, w.Lq)
-    res["dynamic"] = {"index_build_ms": round(ms_b, 4), "build_plus_attention_ms": round(ms_d, 4),
-                      "n_cols": ncols, "n_slash": nslash,
-                      "density_vs_causal": round(pairs_d / dense, 4),
-                      "tflops_incl_build": round(2 * (w.Dqk + w.Dv) * pairs_d / (ms_d * 1e-3)
-                                                 / 1e12, 3)}
+
+    def dynamic(qd, kd, inputs, steps_d):
+        build = lambda: S.attn_build_vslash_index(qd, kd, ncols, nslash, scale=w.scale,
+                                                  outputs=outs, workspace=iws)
+        ms_b, _ = time_steps(build, steps, warmup)
+        bcp, bci, bsp, bsi = build()
+        step_d = lambda: (build(), S.attn_fwd_vertical_slash(qd, kd, v, o, bp, bi, bcp, bci, bsp,
+                                                             bsi, lse=lse, causal=True,
+                                                             scale=w.scale, workspace=ws))
+        ms_d, _ = time_steps(step_d, steps_d, 1)
+        hl = [t.cpu().numpy() for t in (bsp, bsi, bcp, bci)]
+        pairs_d = vslash_pairs(*hl, w.B, w.Hq, w.Lq)
+        return {"inputs": inputs, "index_build_ms": round(ms_b, 4),
+                "build_plus_attention_ms": round(ms_d, 4), "n_cols": ncols, "n_slash": nslash,
+                "density_vs_causal": round(pairs_d / dense, 4),
+                "tflops_incl_build": round(2 * (w.Dqk + w.Dv) * pairs_d / (ms_d * 1e-3) / 1e12,
+                                           3)}
+
+    res["dynamic"] = dynamic(q, k, "the workload's Q and K (N(0, 1) noise: no structure)", 2)
+    # A band rise of 12 that stays above 10 over the first ~1100 offsets (window 4096), over
+    # scores whose noise has a standard deviation near 1.8: the probe's diagonal sums then rank
+    # those offsets above nearly every offset that only a noise extreme or a planted column
+    # crosses, as in the static lists' 1024-offset band (at 32K keys, checked with the oracle's
+    # builder: 1079 of the 1088 lines below offset 1500). With a band that halves by offset
+    # 1024 (window 2048), a few hundred such offsets enter the lines and run as windows.
+    qs, kst = make_structured_qk(w.B, w.Lq, w.Hq, w.Hkv, w.Dqk, 1000 * w.index + 5, window=4096,
+                                 band_logit=12.0, col_logit=5.0, scale=w.scale)
+    res["dynamic_structured"] = dynamic(
+        qs, kst, "make_structured_qk: noise plus a planted band (window 4096, rise 12) and 1000 "
+                 "planted columns per KV head (rise 5)", steps)
+    del qs, kst
     return res
 
 
@@ -943,6 +974,8 @@ def main():
                 wl[name]["density_vs_causal"] = round(r["density_vs_causal"], 4)
             if "dynamic" in r:
                 wl[name]["dynamic_index"] = r["dynamic"]
+            if "dynamic_structured" in r:
+                wl[name]["dynamic_index_structured"] = r["dynamic_structured"]
         if name in SPARSE_WORKLOADS:
             # L2-miss traffic (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated, taken on the
             # current kernel source) over this run's step time, against the read ceiling

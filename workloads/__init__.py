@@ -17,6 +17,15 @@ Recipe:
   offsets 0..1023 (a band of 1024 diagonals below the causal one) plus 64 offsets drawn
   uniformly from [1024, L), and 1000 vertical columns: keys 0..63 plus 936 keys drawn
   uniformly from [64, L). No key blocks.
+* Structured Q/K for the dynamic index builders (`make_structured_qk`): the noise above plus a
+  planted local band (a rotary code in 64 of the dims with random frequencies, so scores fall
+  with the offset |i - j| like a Gaussian, to half at half a window) and planted vertical
+  columns (a per-KV-head direction in the other dims, added to 1000 keys and to every query
+  row). The block-sparse pipeline uses a 6144-key
+  window (half height at 3072 keys, so the 96 listed blocks are about the nearest 96), a band
+  rise of 6 and a column rise of 8 after the softmax scale; the vertical-slash pipeline a
+  4096-key window (the rise stays above 10 over the first ~1100 offsets, the static lists'
+  1024-offset band), a band rise of 12 and a column rise of 5.
 * The MLA decode grid of the FlashMLA-ETAP page (section on experiments: DeepSeek-R1's 16
   heads of dimension 576, batch sizes 16 and 32, KV lengths 512 to 64K; one or two query
   tokens per the problem statement) uses the MLA recipe above with bottom-right causal
@@ -44,6 +53,7 @@ __all__ = [
     "sampled_rows",
     "dense_causal_lists",
     "make_vslash_lists",
+    "make_structured_qk",
 ]
 
 
@@ -193,6 +203,51 @@ def make_vslash_lists(B, Hq, Lk, seed, band=1024, n_far=64, n_cols=1000, sink=64
         cp.append(cp[-1] + cols.size)
     cat = lambda parts: np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
     return (np.asarray(sp, np.int32), cat(sparts), np.asarray(cp, np.int32), cat(cparts))
+
+
+def make_structured_qk(B, L, Hq, Hkv, D, seed, window=2048, n_cols=1000, band_logit=6.0,
+                       col_logit=8.0, n_pairs=32, scale=None, device="cuda:0"):
+    """Q [B, L, Hq, D] and K [B, L, Hkv, D] (bf16 on `device`) carrying the two structures the
+    MInference article describes in long-context attention, planted on N(0, 1) noise: a local
+    band and vertical columns. Inputs for the dynamic index builders, which find nothing in
+    pure noise.
+
+    Band: dims 0 .. 2*n_pairs-1 of every query row i and key j add a rotary code,
+    a * (cos(w_m p), sin(w_m p)) at position p, for n_pairs frequencies w_m = |N(0, sigma)|
+    drawn from the seeded generator with sigma = 2.355 / window. The scores then rise by
+    a^2 * sum_m cos(w_m (i - j)), which averages to `band_logit` * exp(-(sigma (i - j))^2 / 2):
+    the full rise at offset 0, half of it at offset window / 2, and beyond about one window
+    only a random remainder of about band_logit / sqrt(2 n_pairs) (random frequencies, so no
+    offset far from the diagonal is favoured twice). Columns: every KV head draws `n_cols` key positions and a unit vector u
+    over the remaining dims; those keys and every query row of the group add c * u, so those
+    columns' scores rise by `col_logit`. The rises are after the softmax scale (1/sqrt(D)
+    unless given). Batch entries share the structure, not the noise."""
+    scale = D ** -0.5 if scale is None else scale
+    assert 2 * n_pairs < D
+    a = math.sqrt(band_logit / (n_pairs * scale))
+    c = math.sqrt(col_logit / scale)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    pos = torch.arange(L, device=device, dtype=torch.float64)
+    sigma = 2.355 / window
+    w = sigma * torch.randn(n_pairs, generator=g, device=device).double().abs()
+    ph = pos[:, None] * w[None, :]                                      # [L, n_pairs]
+    rot = torch.zeros((L, D), device=device)
+    rot[:, 0:2 * n_pairs:2] = (a * torch.cos(ph)).float()
+    rot[:, 1:2 * n_pairs:2] = (a * torch.sin(ph)).float()
+    u = torch.zeros((Hkv, D), device=device)
+    u[:, 2 * n_pairs:] = torch.randn((Hkv, D - 2 * n_pairs), generator=g, device=device)
+    u = c * u / u.norm(dim=-1, keepdim=True)
+    grp = Hq // Hkv
+    q = torch.randn((B, L, Hq, D), generator=g, device=device)
+    q += rot[None, :, None, :]
+    q += u.repeat_interleave(grp, dim=0)[None, None]
+    k = torch.randn((B, L, Hkv, D), generator=g, device=device)
+    k += rot[None, :, None, :]
+    for h in range(Hkv):
+        cols = torch.randperm(L, generator=g, device=device)[:min(n_cols, L)]
+        k[:, cols, h, :] += u[h]
+    return q.to(torch.bfloat16), k.to(torch.bfloat16)
 
 
 def dense_causal_lists(B, Hq, Lq, Lk, block=64):
