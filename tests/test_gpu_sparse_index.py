@@ -312,3 +312,25 @@ def test_build_vslash_index_deterministic():
     a = _build_vs(q, k, 100, 200, 0.09)
     b = _build_vs(q, k, 100, 200, 0.09)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_builders_on_structured_inputs():
+    """Both builders on the structured inputs the bench uses for its dynamic pipelines
+    (workloads.make_structured_qk: a planted band and planted columns), at 4096 tokens: the
+    lists match the oracle's, and the planted band is what they find (the diagonal's
+    neighbourhood among the blocks, the first offsets among the slash lines)."""
+    from workloads import make_structured_qk
+    B, Hq, Hkv, L, D = 1, 4, 2, 4096, 128
+    say("index builders on structured inputs")
+    q, k = make_structured_qk(B, L, Hq, Hkv, D, 9400, window=1024, n_cols=40, band_logit=12.0,
+                              col_logit=5.0, device="cpu")
+    bp, bi, cp, ci = _compare(q, k, 8, 60, D ** -0.5, "structured blocks")
+    nqb = L // 64
+    for h in range(Hq):
+        for qb in range(8, nqb):
+            row = bi[bp[h * nqb + qb]:bp[h * nqb + qb + 1]]
+            assert np.all(row >= qb - 12), f"head {h} query block {qb}: {row}"
+    cp, ci, sp, si = _compare_vs(q, k, 60, 300, D ** -0.5, "structured lines")
+    for h in range(Hq):
+        offs = si[sp[h]:sp[h + 1]]
+        assert np.count_nonzero(offs < 400) >= 280, f"head {h}: {offs}"
