@@ -162,3 +162,28 @@ def test_decode_one_split_equals_partials_path():
     S.splitkv_decode(q, k, v, o2, l2, causal=True, scale=D ** -0.5, num_splits=1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, Lq, Lk, Dqk, causal
+    (2, 8, 2, 2, 1, 128, True),      # Lq > Lk, bottom-right causal: query row 0 sees no key
+    (2, 8, 2, 3, 2, 64, True),       # rows see 0, 1 and 2 keys
+    (1, 16, 1, 2, 1, 576, True),     # the latent shape with an empty row
+    (3, 8, 8, 1, 63, 128, False),    # one key short of a tile
+    (3, 8, 8, 1, 64, 128, False),    # exactly one tile
+    (3, 8, 8, 1, 65, 128, False),    # one key into a second tile
+    (1, 16, 1, 1, 127, 576, False),  # the latent shape's split minimum, one key short
+    (1, 16, 1, 1, 129, 576, False),  # one key past it
+    (1, 8, 1, 1, 130, 128, False),   # two splits, the second of 2 keys
+    (1, 16, 1, 2, 257, 576, True),   # latent, two splits (192 + 65 keys), two tokens
+], ids=lambda s: "x".join(map(str, s)))
+def test_decode_edge_lengths(shape):
+    """Cache lengths at tile edges and query rows with no visible key (O = 0, LSE = -inf in
+    both the kernel and the oracle)."""
+    B, Hq, Hkv, Lq, Lk, Dqk, causal = shape
+    mla = Dqk == 576
+    say(f"decode edge {shape}")
+    q = randn_bf16((B, Lq, Hq, Dqk), 8500 + Lk + Lq)
+    k = randn_bf16((B, Lk, Hkv, Dqk), 8501 + Lk + Lq)
+    v = None if mla else randn_bf16((B, Lk, Hkv, Dqk), 8502 + Lk + Lq)
+    _check(q, k, v, causal, (192 if mla else Dqk) ** -0.5, f"decode edge {shape}", mla=mla)
