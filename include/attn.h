@@ -103,8 +103,9 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
  */
 
 /* Split count the library would pick for MI355X (256 CUs): one round of workgroups over the
- * chip (two per CU for D = 128, one otherwise), each split at least one 64-key tile (two for the
- * latent shape), at most 256 splits, none empty. Pure function of its arguments; returns a
+ * chip (two per CU for D = 128, one otherwise), or whole rounds when one round cannot be filled
+ * exactly, each split at least one 64-key tile (two for the latent shape), at most 256 splits,
+ * none empty. Pure function of its arguments; returns a
  * value in [1, ceil(Lk/64)], or ATTN_ERR_INVALID_ARG for sizes < 1. */
 int attn_splitkv_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 

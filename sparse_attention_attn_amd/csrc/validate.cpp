@@ -116,6 +116,21 @@ int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   const int64_t grid = (Dqk == 128) ? 512 : 256;
   const int min_keys = (Dqk == 576) ? 128 : 64;
   int64_t s = (grid + units - 1) / units;
+  // A grid just past a whole number of rounds leaves a short last round (B 24 at D = 128:
+  // 3 splits, 576 workgroups, 36.1 / 97.5 / 353.2 us at 1K / 4K / 16K keys). Take instead the
+  // smallest split count that fills whole rounds with splits of at least 512 keys (8 splits:
+  // 29.9 / 84.3 / 283.3 us), else the largest that stays within one round (2 splits: 26.9 /
+  // 86.8 / 306.5 us); at B 48, 4 splits (147.8 / 549.5 us at 4K / 16K) or 1 (42.7 us at 1K)
+  // against 2 (165.2 / 585.7 / 48.3 us).
+  if ((units * s) % grid != 0) {
+    int64_t fill = 0;
+    for (int64_t t = s; t <= 8 * s && t <= 256; ++t)
+      if ((units * t) % grid == 0 && Lk / t >= 512) {
+        fill = t;
+        break;
+      }
+    s = fill ? fill : std::max<int64_t>(1, grid / units);
+  }
   const int64_t max_by_len = std::max<int64_t>(1, Lk / min_keys);
   const int64_t max_s = (Lk + 63) / 64;
   s = std::min(s, max_by_len);
