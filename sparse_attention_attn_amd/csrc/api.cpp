@@ -161,7 +161,6 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
     if (st != ATTN_OK) return st;
     attn::FwdArgs a;
     fill_fwd(a, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, causal, scale);
-    a.n_qtiles = (Lq + attn::kDenseBlockM - 1) / attn::kDenseBlockM;
     return launch_status(fn, attn::launch_fwd_dense(a, Dqk, static_cast<hipStream_t>(stream)));
   } catch (const std::exception& e) {
     return attn::fail(ATTN_ERR_LAUNCH, fn, e.what());

@@ -45,9 +45,9 @@ namespace attn {
 namespace {
 
 constexpr int kStages = 2;
-// Waves per workgroup (each owns 32 query rows) and workgroups resident per CU.
-constexpr int kDenseWaves = kDenseBlockM / 32;
-constexpr int kDenseWgPerCu = kDenseWaves == 4 ? 2 : 1;
+// Waves per workgroup (each owns 32 query rows): 8 (256 rows, one workgroup per CU) or 4 (128
+// rows, two per CU); launch_dense_t picks one per launch.
+constexpr int wg_per_cu(int nw) { return nw == 4 ? 2 : 1; }
 // MFMA slots between an operand's LDS read and its use.
 #ifndef ATTN_DENSE_READ_AHEAD
 #define ATTN_DENSE_READ_AHEAD 2
@@ -338,12 +338,11 @@ __device__ __forceinline__ int logical_block_xcd(int xcd_remap) {
 // t and V of tile t-1: together they form the LDS pair t, held in stage t%2. Step 2t+1 (second
 // half of tile t) opens with the wait for pair t+1, the workgroup barrier, and the copy of pair
 // t+2 into the stage of pair t, whose last reader was step 2t.
-template <int D, int NR>
-__global__ __launch_bounds__(kDenseWaves * 64, kDenseWgPerCu) void fwd_dense_kernel(const FwdArgs a) {
+template <int D, int NR, int NW>
+__global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
-  constexpr int NW = kDenseWaves;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   constexpr int BM = 32 * NR * NW;
-  static_assert(BM == kDenseBlockM, "rows per workgroup");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * C::STAGE_BYTES];
   const uint32_t lds0 = lds_addr(smem);
 
@@ -488,15 +487,28 @@ __global__ __launch_bounds__(kDenseWaves * 64, kDenseWgPerCu) void fwd_dense_ker
   store_rows<D, NR>(a, ws, b, hq, qw0, l);
 }
 
-template <int D>
-hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = kDenseWaves;
-  const int64_t nwg = (int64_t)a.B * a.Hq * a.n_qtiles;
+template <int D, int NW>
+hipError_t launch_dense_nw(const FwdArgs& a, hipStream_t stream) {
+  constexpr int BM = 32 * kDenseNR * NW;
   FwdArgs aa = a;
+  aa.n_qtiles = (a.Lq + BM - 1) / BM;
+  const int64_t nwg = (int64_t)a.B * a.Hq * aa.n_qtiles;
   aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, aa);
   return hipGetLastError();
+}
+
+// 256-row workgroups (8 waves, one per CU) unless that grid is a single round or less: then
+// 128-row workgroups (4 waves, two per CU) put twice as many on the chip. Measured per call:
+// B 1, Hq 8, Hkv 2 at 2K / 4K / 8K tokens 60.4 / 113.6 / 222.4 -> 43.4 / 81.3 / 213.1 us,
+// Hq 32 at 2K 60.1 -> 52.3 us; with two rounds or more the 256-row form is ahead (Hq 32 at 4K:
+// 142.1 against 153.1 us, at 8K 515.0 against 532.3 us).
+template <int D>
+hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
+  const int64_t nwg256 = (int64_t)a.B * a.Hq * ((a.Lq + 255) / 256);
+  if (nwg256 <= kCUs) return launch_dense_nw<D, 4>(a, stream);
+  return launch_dense_nw<D, 8>(a, stream);
 }
 
 }  // namespace

@@ -126,11 +126,8 @@ hipError_t launch_fwd_blocksparse(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int dv, hipStream_t stream);
 
-// Query rows per workgroup of the dense forward kernel.
-#ifndef ATTN_DENSE_BLOCK_M
-#define ATTN_DENSE_BLOCK_M 256
-#endif
-constexpr int kDenseBlockM = ATTN_DENSE_BLOCK_M;
+// Compute units of an MI355X (the launchers size their grids against it).
+constexpr int kCUs = 256;
 // Query rows per workgroup of the block-sparse kernel (one 64-row query block).
 constexpr int kSparseBlockM = 64;
 // Query columns per 16-column block of a split-KV workgroup (see split_cols in validate.hpp).
