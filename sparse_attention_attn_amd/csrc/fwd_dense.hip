@@ -322,10 +322,23 @@ __device__ __forceinline__ void store_rows(const FwdArgs& a, const WaveRows<D, N
 
 // Maps blockIdx.x to a logical tile id so that consecutive logical ids run on one XCD (the
 // hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
+// The hardware deals workgroups round-robin over the 8 XCDs: workgroup bid runs on XCD bid % 8
+// as its (bid / 8)-th. xcd_remap (set by the launcher, grid a multiple of 8):
+//  0  no remap (logical id = bid);
+//  1  the (b, kv head) groups are a multiple of 8: XCD x takes the x-th eighth of the logical
+//     order, i.e. whole groups;
+//  X  (2, 4 or 8) there are 8 / X groups: each group's logical ids are dealt round-robin over
+//     X XCDs, so every XCD keeps one KV head and an equal share of its longest-first tiles.
+//     (Cutting a group's tiles into contiguous ranges gave one XCD the longest tiles and another
+//     the shortest: B 1, Hq 8, Hkv 2 at 32K tokens ran at 676 TFLOP/s.)
 __device__ __forceinline__ int logical_block_xcd(int xcd_remap) {
   const int bid = (int)blockIdx.x;
   const int n = (int)gridDim.x;
-  return xcd_remap ? ((bid & 7) * (n >> 3) + (bid >> 3)) : bid;
+  if (xcd_remap == 0) return bid;
+  const int x = bid & 7, k = bid >> 3;
+  if (xcd_remap == 1) return x * (n >> 3) + k;
+  const int X = xcd_remap;
+  return (x / X) * ((n >> 3) * X) + k * X + (x % X);
 }
 
 // Logical order: (b, kv head) major so one XCD keeps one KV head's K/V in its L2, then query
@@ -493,7 +506,11 @@ hipError_t launch_dense_nw(const FwdArgs& a, hipStream_t stream) {
   FwdArgs aa = a;
   aa.n_qtiles = (a.Lq + BM - 1) / BM;
   const int64_t nwg = (int64_t)a.B * a.Hq * aa.n_qtiles;
-  aa.xcd_remap = (nwg % 8 == 0) ? 1 : 0;
+  const int64_t groups = (int64_t)a.B * a.Hkv;
+  aa.xcd_remap = (nwg % 8 != 0)    ? 0
+                 : (groups % 8 == 0) ? 1
+                 : (8 % groups == 0) ? (int)(8 / groups)
+                                     : 0;
   hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
                      stream, aa);
   return hipGetLastError();

@@ -23,7 +23,7 @@ struct FwdArgs {
   float sl2;      // |scale| * log2(e), > 0 (see exp2_scale)
   uint32_t qsign; // 0x80008000 when scale < 0: the kernels negate Q as they load it
   int n_qtiles;   // query tiles per (b, hq)
-  int xcd_remap;  // grid size divisible by 8: group consecutive logical tiles per XCD
+  int xcd_remap;  // how logical tiles map to XCDs (0: none; see the kernels' launchers)
   // block-sparse lists (device pointers), unused by the dense kernel
   const int32_t* blk_ptr;
   const int32_t* blk_idx;
