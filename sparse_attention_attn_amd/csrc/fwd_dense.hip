@@ -516,15 +516,18 @@ hipError_t launch_dense_nw(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// 256-row workgroups (8 waves, one per CU) unless that grid is a single round or less: then
-// 128-row workgroups (4 waves, two per CU) put twice as many on the chip. Measured per call:
-// B 1, Hq 8, Hkv 2 at 2K / 4K / 8K tokens 60.4 / 113.6 / 222.4 -> 43.4 / 81.3 / 213.1 us,
-// Hq 32 at 2K 60.1 -> 52.3 us; with two rounds or more the 256-row form is ahead (Hq 32 at 4K:
-// 142.1 against 153.1 us, at 8K 515.0 against 532.3 us).
+// 256-row workgroups (8 waves, one per CU) unless that grid is a single round or less, or the
+// keys are few: then 128-row workgroups (4 waves, two per CU). Measured per call: B 1, Hq 8,
+// Hkv 2 at 2K / 4K / 8K tokens 60.4 / 113.6 / 222.4 -> 43.4 / 81.3 / 213.1 us, Hq 32 at 2K
+// 60.1 -> 52.3 us; with at most 1024 keys a workgroup's start and drain weigh more than its
+// tiles, and two per CU hide each other's (B 8, Hq 32 at 1K tokens 112.0 -> 104.2 us; B 16 at
+// 512 78.9 -> 70.3 us; D = 64, B 4 at 1K 41.7 -> 37.3 us). Otherwise the 256-row form is
+// ahead, each K/V tile feeding twice the rows (Hq 32 at 4K: 141.4 against 152.9 us; B 2 at
+// 2K 82.2 against 86.5 us; at 8K 515.0 against 532.3 us).
 template <int D>
 hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
   const int64_t nwg256 = (int64_t)a.B * a.Hq * ((a.Lq + 255) / 256);
-  if (nwg256 <= kCUs) return launch_dense_nw<D, 4>(a, stream);
+  if (nwg256 <= kCUs || a.Lk <= 1024) return launch_dense_nw<D, 4>(a, stream);
   return launch_dense_nw<D, 8>(a, stream);
 }
 
