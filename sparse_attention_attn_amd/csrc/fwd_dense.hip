@@ -320,10 +320,9 @@ __device__ __forceinline__ void store_rows(const FwdArgs& a, const WaveRows<D, N
   }
 }
 
-// Maps blockIdx.x to a logical tile id so that consecutive logical ids run on one XCD (the
-// hardware deals workgroups round-robin over the 8 XCDs, each with its own L2).
-// The hardware deals workgroups round-robin over the 8 XCDs: workgroup bid runs on XCD bid % 8
-// as its (bid / 8)-th. xcd_remap (set by the launcher, grid a multiple of 8):
+// Maps blockIdx.x to a logical tile id. The hardware deals workgroups round-robin over the 8
+// XCDs: workgroup bid runs on XCD bid % 8 as its (bid / 8)-th. xcd_remap (set by the launcher,
+// grid a multiple of 8):
 //  0  no remap (logical id = bid);
 //  1  the (b, kv head) groups are a multiple of 8: XCD x takes the x-th eighth of the logical
 //     order, i.e. whole groups;
