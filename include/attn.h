@@ -100,13 +100,18 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
  * Sizes: o_part is fp32 [S, B, Hq, Lq, Dv], lse_part is fp32 [S, B, Hq, Lq], both contiguous
  * DEVICE buffers owned by the caller. num_splits must lie in [1, ceil(Lk / 64)].
  * Supported head dims: (64, 64), (128, 128) and the MLA latent (576, 512).
+ * Any Lq is accepted. With at least 128 query rows and D = 64 or 128 (a query chunk against a
+ * longer cache: chunked prefill) the partials come from the prefill kernel run over each
+ * split's keys; otherwise from the decode kernel (up to 32 query columns of a KV head per
+ * workgroup). Both write the same partials.
  */
 
 /* Split count the library would pick for MI355X (256 CUs): one round of workgroups over the
  * chip (two per CU for D = 128, one otherwise), or whole rounds when one round cannot be filled
  * exactly, each split at least one 64-key tile (two for the latent shape), at most 256 splits,
- * none empty. Pure function of its arguments; returns a
- * value in [1, ceil(Lk/64)], or ATTN_ERR_INVALID_ARG for sizes < 1. */
+ * none empty; for query chunks of at least 128 rows, one round of two 128-row prefill
+ * workgroups per CU with splits of at least 1024 keys. Pure function of its arguments; returns
+ * a value in [1, ceil(Lk/64)], or ATTN_ERR_INVALID_ARG for sizes < 1. */
 int attn_splitkv_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
 /* Bytes of o_part plus lse_part for these sizes (0 on invalid sizes). */
@@ -131,8 +136,9 @@ int attn_combine_lse(const float* o_part, const float* lse_part, int num_splits,
  * attn_fwd_decode — split-KV decode and its LSE combine in one call: attn_fwd_splitkv with
  * num_splits = attn_splitkv_num_splits(...) followed by attn_combine_lse, on one stream, with
  * the partials in the caller's workspace. When that count is 1, the split kernel writes O and
- * LSE itself and no combine is launched (same values bit for bit). Arguments as attn_fwd; o is bf16 strided like
- * attn_fwd's, lse fp32 [B, Hq, Lq] or NULL.
+ * LSE itself and no combine is launched (same values bit for bit; for a query chunk of at least
+ * 128 rows that kernel is attn_fwd's). Arguments as attn_fwd; o is bf16 strided like attn_fwd's,
+ * lse fp32 [B, Hq, Lq] or NULL.
  * workspace: DEVICE buffer of at least attn_decode_workspace_bytes(...) bytes, 256-byte
  * aligned, owned by the caller; its contents on entry do not matter. Calls that overlap on
  * one workspace race.

@@ -55,6 +55,25 @@ void fill_fwd(attn::FwdArgs& a, const attn_tensor_t& q, const attn_tensor_t& k,
   a.sl_ptr = a.sl_idx = nullptr;
   a.sl_bits = a.cl_bits = a.rl_bits = nullptr;
   a.bits_words = 0;
+  a.o_part = a.lse_part = nullptr;
+  a.num_splits = 1;
+  a.chunk = 0;
+}
+
+// Split-KV partials of a prefill-shaped query block (attn::dense_split_shape) by the dense
+// kernel's split form: same partial layout and split bounds as the decode kernel's.
+int dense_split_launch(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k,
+                       const attn_tensor_t& v, float* o_part, float* lse_part, int num_splits,
+                       int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int causal, float scale,
+                       hipStream_t sm) {
+  attn_tensor_t none{};
+  attn::FwdArgs a;
+  fill_fwd(a, q, k, v, none, nullptr, B, Hq, Hkv, Lq, Lk, causal, scale);
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.num_splits = num_splits;
+  a.chunk = attn::split_chunk(Lk, num_splits);
+  return launch_status(fn, attn::launch_fwd_dense_split(a, Dqk, sm));
 }
 
 // Split-KV decode into a checked workspace `wb` laid out by `ws`: the split kernel, then the
@@ -63,6 +82,27 @@ int decode_launch(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k
                   const attn_tensor_t& v, const attn_tensor_t& o, float* lse, int B, int Hq,
                   int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal, float scale, char* wb,
                   const attn::DecodeWorkspace& ws, hipStream_t sm) {
+  if (attn::dense_split_shape(Dqk, Dv, Lq)) {
+    // a prefill-shaped query block: the dense kernel, whole (one split) or in splits + combine
+    if (ws.num_splits == 1) {
+      attn::FwdArgs f;
+      fill_fwd(f, q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, causal, scale);
+      return launch_status(fn, attn::launch_fwd_dense(f, Dqk, sm));
+    }
+    float* op = reinterpret_cast<float*>(wb + ws.o_part);
+    float* lp = reinterpret_cast<float*>(wb + ws.lse_part);
+    int st = dense_split_launch(fn, q, k, v, op, lp, ws.num_splits, B, Hq, Hkv, Lq, Lk, Dqk,
+                                causal, scale, sm);
+    if (st != ATTN_OK) return st;
+    attn::CombineArgs c;
+    c.o_part = op;
+    c.lse_part = lp;
+    c.o = static_cast<uint16_t*>(o.data);
+    c.lse = lse;
+    c.o_sb = o.stride_b; c.o_sl = o.stride_l; c.o_sh = o.stride_h;
+    c.B = B; c.Hq = Hq; c.Lq = Lq; c.S = ws.num_splits;
+    return launch_status(fn, attn::launch_combine(c, Dv, sm));
+  }
   attn::SplitArgs a;
   a.q = static_cast<const uint16_t*>(q.data);
   a.k = static_cast<const uint16_t*>(k.data);
@@ -191,6 +231,9 @@ int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o
       return attn::fail(ATTN_ERR_WORKSPACE, fn, "o_part / lse_part is NULL");
     if ((reinterpret_cast<uintptr_t>(o_part) & 15u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u))
       return attn::fail(ATTN_ERR_WORKSPACE, fn, "o_part must be 16-byte and lse_part 4-byte aligned");
+    if (attn::dense_split_shape(Dqk, Dv, Lq))
+      return dense_split_launch(fn, q, k, v, o_part, lse_part, num_splits, B, Hq, Hkv, Lq, Lk,
+                                Dqk, causal, scale, static_cast<hipStream_t>(stream));
     attn::SplitArgs a;
     a.q = static_cast<const uint16_t*>(q.data);
     a.k = static_cast<const uint16_t*>(k.data);

@@ -320,6 +320,37 @@ __device__ __forceinline__ void store_rows(const FwdArgs& a, const WaveRows<D, N
   }
 }
 
+// Split form: the rows' normalised partial output O_s (fp32) and LSE_s over this workgroup's key
+// range go to the split-KV partials, row (s, b, hq, row) of [S, B, Hq, Lq] (a row that sees no
+// key of the range writes O_s = 0 and LSE_s = -inf).
+template <int D, int NR>
+__device__ __forceinline__ void store_part(const FwdArgs& a, const WaveRows<D, NR>& ws, int b,
+                                           int hq, int qw0, int l, int sp) {
+  using C = TileCfg<D>;
+  const int h = l >> 5;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float tb = ws.lb[r] + other_half(ws.lb[r]);
+    const float tf = ws.lf[r] + other_half(ws.lf[r]);
+    const int row = qw0 + 32 * r + (l & 31);
+    if (row >= a.Lq) continue;
+    const float inv = tb > 0.f ? 1.0f / tb : 0.f;
+    const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq) * a.Lq + row;
+    float* orow = a.o_part + prow * D;
+#pragma unroll
+    for (int bb = 0; bb < C::DVB; ++bb) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dv = 32 * bb + 8 * u + 4 * h;
+        *reinterpret_cast<float4*>(orow + dv) =
+            make_float4(ws.acc[r][bb][4 * u + 0] * inv, ws.acc[r][bb][4 * u + 1] * inv,
+                        ws.acc[r][bb][4 * u + 2] * inv, ws.acc[r][bb][4 * u + 3] * inv);
+      }
+    }
+    if (h == 0) a.lse_part[prow] = tf > 0.f ? ws.m[r] * kLn2 + logf(tf) : -INFINITY;
+  }
+}
+
 // Maps blockIdx.x to a logical tile id. The hardware deals workgroups round-robin over the 8
 // XCDs: workgroup bid runs on XCD bid % 8 as its (bid / 8)-th. xcd_remap (set by the launcher,
 // grid a multiple of 8):
@@ -350,7 +381,7 @@ __device__ __forceinline__ int logical_block_xcd(int xcd_remap) {
 // t and V of tile t-1: together they form the LDS pair t, held in stage t%2. Step 2t+1 (second
 // half of tile t) opens with the wait for pair t+1, the workgroup barrier, and the copy of pair
 // t+2 into the stage of pair t, whose last reader was step 2t.
-template <int D, int NR, int NW>
+template <int D, int NR, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
@@ -366,6 +397,11 @@ __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const
   int lid = logical_block_xcd(a.xcd_remap);
   const int hg = lid % a.g;
   lid /= a.g;
+  int sp = 0;  // split form: the key range [sp * chunk, (sp + 1) * chunk) of this workgroup
+  if constexpr (SPLIT) {
+    sp = lid % a.num_splits;
+    lid /= a.num_splits;
+  }
   const int qt = a.n_qtiles - 1 - (lid % a.n_qtiles);
   lid /= a.n_qtiles;
   const int hkv = lid % a.Hkv;
@@ -379,35 +415,42 @@ __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const
   const int rblk = w < NW / 2 ? w : (3 * NW / 2 - 1) - w;
   const int qw0 = q0 + 32 * NR * rblk;        // first row of this wave
   const int qlast = min(q0 + BM, a.Lq) - 1;   // last row of the workgroup
-  int klimit = a.Lk;                          // keys [0, klimit) can be visible
-  if (a.causal) klimit = max(0, min(a.Lk, qlast + a.off + 1));
+  // Key positions below are relative to the workgroup's range [kbeg, kbeg + rlk): all keys in
+  // one launch, one split's keys in the split form; roff is the causal offset relative to it.
+  const int kbeg = SPLIT ? sp * a.chunk : 0;
+  const int rlk = SPLIT ? min(a.Lk, kbeg + a.chunk) - kbeg : a.Lk;
+  const int roff = a.off - kbeg;
+  int klimit = rlk;                           // keys [0, klimit) of the range can be visible
+  if (a.causal) klimit = max(0, min(rlk, qlast + roff + 1));
   const int ntiles = __builtin_amdgcn_readfirstlane((klimit + BN - 1) / BN);
 
   WaveRows<D, NR> ws;
   load_q_rows<D, NR>(a, ws, b, hq, qw0, l);
 
-  if (ntiles == 0) {  // no row of the workgroup sees any key (causal with Lq > Lk)
-    store_rows<D, NR>(a, ws, b, hq, qw0, l);
+  if (ntiles == 0) {  // no row of the workgroup sees any key (causal with Lq > Lk, or a split
+                      // past the rows' horizon)
+    if constexpr (SPLIT) store_part<D, NR>(a, ws, b, hq, qw0, l, sp);
+    else store_rows<D, NR>(a, ws, b, hq, qw0, l);
     return;
   }
 
   TileByteOffsets<D, NW> off;
   off.init_k(a, w, l);
   off.init_v(a, w, l);
-  const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-  const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+  const uint16_t* kb = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh + (int64_t)kbeg * a.k_sl;
+  const uint16_t* vb = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh + (int64_t)kbeg * a.v_sl;
 
   // Units [0, nfull) are complete and visible to every row of this wave; later units are
   // masked (the causal diagonal, the ragged end, and the units past this wave's horizon that
   // the workgroup still streams for its other waves).
-  int nfull = a.Lk / 32;
-  if (a.causal) nfull = min(nfull, max(0, qw0 + a.off + 1) / 32);
+  int nfull = rlk / 32;
+  if (a.causal) nfull = min(nfull, max(0, qw0 + roff + 1) / 32);
   nfull = __builtin_amdgcn_readfirstlane(nfull);
   // Last step with work for this wave: the P·V of the last unit holding a key visible to one of
   // its rows (with causal masking the workgroup streams later units for its other waves only).
   int jlast = 2 * ntiles;
   if (a.causal) {
-    const int lastkey = min(a.Lk - 1, min(qw0 + 32 * NR - 1, a.Lq - 1) + a.off);
+    const int lastkey = min(rlk - 1, min(qw0 + 32 * NR - 1, a.Lq - 1) + roff);
     jlast = min(jlast, (lastkey + 32) / 32);  // last unit + 1 (0 when no key is visible)
   }
   jlast = __builtin_amdgcn_readfirstlane(jlast);
@@ -421,12 +464,12 @@ __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const
     const uint32_t st = __builtin_amdgcn_readfirstlane(stage_addr(t));
     if (t < ntiles) {
       const int base = t * BN;
-      if (base + BN > a.Lk) off.init_k(a, w, l, a.Lk - 1 - base);
+      if (base + BN > rlk) off.init_k(a, w, l, rlk - 1 - base);
       issue_k_sbase<D, NW>(st, kb + (int64_t)base * a.k_sl, off, wu);
     }
     if (t >= 1) {
       const int base = (t - 1) * BN;
-      if (base + BN > a.Lk) off.init_v(a, w, l, a.Lk - 1 - base);
+      if (base + BN > rlk) off.init_v(a, w, l, rlk - 1 - base);
       issue_v_sbase<D, NW>(st + C::KT_BYTES, vb + (int64_t)base * a.v_sl, off, wu);
     }
   };
@@ -469,7 +512,7 @@ __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const
     if (j > jlast) return;  // every later unit is masked for all rows of this wave
     float sb[NR], sf[NR];
     bool ok;
-    if (j >= nfull) mask_unit<NR>(sc[H], j, qw0, a.Lk, a.causal, a.off, l);
+    if (j >= nfull) mask_unit<NR>(sc[H], j, qw0, rlk, a.causal, roff, l);
     // Sᵀ(j+1): H = 0 -> second half of tile t; H = 1 -> first half of tile t+1.
     // P·V of unit j-1: H = 0 -> second half of tile t-1; H = 1 -> first half of tile t.
     const uint32_t st = stage_addr(t + H);
@@ -496,22 +539,24 @@ __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const
   }
   step(icn<0>{}, ntiles);
   wait_dma_all();
-  store_rows<D, NR>(a, ws, b, hq, qw0, l);
+  if constexpr (SPLIT) store_part<D, NR>(a, ws, b, hq, qw0, l, sp);
+  else store_rows<D, NR>(a, ws, b, hq, qw0, l);
 }
 
-template <int D, int NW>
+template <int D, int NW, bool SPLIT = false>
 hipError_t launch_dense_nw(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * kDenseNR * NW;
   FwdArgs aa = a;
   aa.n_qtiles = (a.Lq + BM - 1) / BM;
-  const int64_t nwg = (int64_t)a.B * a.Hq * aa.n_qtiles;
+  const int64_t nwg = (int64_t)a.B * a.Hq * aa.n_qtiles * (SPLIT ? a.num_splits : 1);
+  if (nwg > 0x7fffffff) return hipErrorInvalidConfiguration;  // beyond one grid dimension
   const int64_t groups = (int64_t)a.B * a.Hkv;
   aa.xcd_remap = (nwg % 8 != 0)    ? 0
                  : (groups % 8 == 0) ? 1
                  : (8 % groups == 0) ? (int)(8 / groups)
                                      : 0;
-  hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR, NW>), dim3((unsigned)nwg), dim3(NW * 64), 0,
-                     stream, aa);
+  hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR, NW, SPLIT>), dim3((unsigned)nwg),
+                     dim3(NW * 64), 0, stream, aa);
   return hipGetLastError();
 }
 
@@ -535,6 +580,13 @@ hipError_t launch_dense_t(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream) {
   if (d == 128) return launch_dense_t<128>(a, stream);
   return launch_dense_t<64>(a, stream);
+}
+
+// Split form (split-KV partials of a prefill-shaped query block): 128-row workgroups, one per
+// (b, query head, row tile, split); the split count sets the grid.
+hipError_t launch_fwd_dense_split(const FwdArgs& a, int d, hipStream_t stream) {
+  if (d == 128) return launch_dense_nw<128, 4, true>(a, stream);
+  return launch_dense_nw<64, 4, true>(a, stream);
 }
 
 }  // namespace attn

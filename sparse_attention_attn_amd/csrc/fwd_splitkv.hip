@@ -529,6 +529,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
 template <int DQK, int DV, int BNK, int NST, int NCB>
 hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.B * a.Hkv * a.ncolblk * a.num_splits;
+  if (nwg > 0x7fffffff) return hipErrorInvalidConfiguration;  // beyond one grid dimension
   hipLaunchKernelGGL((splitkv_kernel<DQK, DV, BNK, NST, NCB>), dim3((unsigned)nwg), dim3(256), 0,
                      stream, a);
   return hipGetLastError();

@@ -24,6 +24,12 @@ struct FwdArgs {
   uint32_t qsign; // 0x80008000 when scale < 0: the kernels negate Q as they load it
   int n_qtiles;   // query tiles per (b, hq)
   int xcd_remap;  // how logical tiles map to XCDs (0: none; see the kernels' launchers)
+  // split form of the dense kernel (launch_fwd_dense_split): split s covers keys
+  // [s * chunk, min((s + 1) * chunk, Lk)) and writes its normalised partials here
+  float* o_part;    // [S, B, Hq, Lq, Dv]
+  float* lse_part;  // [S, B, Hq, Lq]
+  int num_splits;
+  int chunk;        // keys per split (multiple of 64)
   // block-sparse lists (device pointers), unused by the dense kernel
   const int32_t* blk_ptr;
   const int32_t* blk_idx;
@@ -119,6 +125,7 @@ constexpr int kProbeRows = 64;
 constexpr int kProbeChunk = 1024;
 
 hipError_t launch_fwd_dense(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_dense_split(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_build_index(const IndexArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_vslash(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_build_vslash_index(const IndexArgs& a, int d, hipStream_t stream);

@@ -103,6 +103,16 @@ int check_num_splits(const char* fn, int num_splits, int Lk) {
 int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   (void)Dv;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (dense_split_shape(Dqk, Dv, Lq)) {
+    // the dense kernel's split form: one round of two 128-row workgroups per CU, splits of at
+    // least 1024 keys, none empty
+    const int64_t units = (int64_t)B * Hq * ((Lq + 127) / 128);
+    int64_t s = std::max<int64_t>(1, 512 / units);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, Lk / 1024));
+    s = std::min<int64_t>(s, 256);
+    const int chunk = split_chunk(Lk, (int)s);
+    return (int)((Lk + chunk - 1) / chunk);
+  }
   const int g = Hq / Hkv;
   const int cols = split_cols(Dqk, g * Lq);
   const int64_t colblk = ((int64_t)g * Lq + cols - 1) / cols;

@@ -34,6 +34,13 @@ int check_num_splits(const char* fn, int num_splits, int Lk);
 // heads, 8 heads with 4 query tokens, the latent shape with 2 tokens), 16 otherwise.
 inline int split_cols(int dqk, int ncols) { (void)dqk; return ncols > 16 ? 32 : 16; }
 
+// Split-KV of a prefill-shaped query block (at least 128 query rows, D = 64 or 128): the dense
+// kernel's split form computes the partials (128-row workgroups per key range) instead of the
+// decode kernel, whose workgroups take at most 32 query columns of a KV head.
+inline bool dense_split_shape(int dqk, int dv, int lq) {
+  return dqk == dv && (dqk == 64 || dqk == 128) && lq >= 128;
+}
+
 int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv);
 
 // Keys per split: 64 * ceil(ceil(Lk / S) / 64).
