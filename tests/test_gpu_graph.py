@@ -38,8 +38,9 @@ def _replays_match(run, outs, label):
 
 
 @pytest.mark.parametrize("shape", [(16, 32, 8, 1, 4096, 128, 128), (4, 16, 1, 2, 3000, 576, 512),
-                                   (128, 16, 4, 2, 300, 128, 128)],
-                         ids=["gqa", "mla", "one_split_direct"])
+                                   (128, 16, 4, 2, 300, 128, 128),
+                                   (1, 16, 4, 384, 3000, 128, 128)],
+                         ids=["gqa", "mla", "one_split_direct", "chunked_prefill"])
 def test_decode_graph_replays_equal_eager(shape):
     import torch
     import sparse_attention_attn_amd as S
