@@ -614,6 +614,63 @@ def bench_memory(lengths, eager_max):
     return out
 
 
+def bench_prefill_sweep(shapes, steps=10, warmup=3):
+    """Causal GQA prefill (attn_fwd, D 128) over batch, head counts and lengths other than the
+    headline's, including grids of one round or less (where the launcher takes the 128-row
+    workgroup form). Inputs: seeded device N(0, 1) in bf16."""
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import randn_bf16_device
+    out = []
+    for (B, Hq, Hkv, L) in shapes:
+        D = 128
+        q = randn_bf16_device((B, L, Hq, D), 7100 + L)
+        k = randn_bf16_device((B, L, Hkv, D), 7101 + L)
+        v = randn_bf16_device((B, L, Hkv, D), 7102 + L)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda:0")
+        ms, _ = time_steps(lambda: S.attn_fwd(q, k, v, o, lse, causal=True, scale=D ** -0.5),
+                           steps, warmup)
+        flops = 2 * 2 * D * B * Hq * dense_causal_pairs(L, L, True)
+        out.append({"B": B, "Hq": Hq, "Hkv": Hkv, "L": L, "ms": round(ms, 4),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "workgroups_256_rows": B * Hq * (-(-L // 256))})
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_chunked_prefill(shapes, steps=10, warmup=3):
+    """A query chunk against a longer cache (bottom-right causal, D 128): attn_fwd (one
+    workgroup per 128 or 256 rows of a head) against the one-call split-KV path
+    (attn_fwd_decode, which runs the prefill kernel over split key ranges and the LSE combine).
+    Inputs: seeded device N(0, 1) in bf16."""
+    import torch
+    import sparse_attention_attn_amd as S
+    from workloads import randn_bf16_device
+    out = []
+    for (B, Hq, Hkv, Lq, Lk) in shapes:
+        D = 128
+        q = randn_bf16_device((B, Lq, Hq, D), 7200 + Lq)
+        k = randn_bf16_device((B, Lk, Hkv, D), 7201 + Lk)
+        v = randn_bf16_device((B, Lk, Hkv, D), 7202 + Lk)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(max(256, S.attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, D, D)),
+                         dtype=torch.uint8, device="cuda:0")
+        ms_f, _ = time_steps(lambda: S.attn_fwd(q, k, v, o, lse, causal=True), steps, warmup)
+        ms_s, _ = time_steps(lambda: S.attn_fwd_decode(q, k, v, o, lse, causal=True,
+                                                       workspace=ws), steps, warmup)
+        flops = 2 * 2 * D * B * Hq * dense_causal_pairs(Lq, Lk, True)
+        out.append({"B": B, "Hq": Hq, "Hkv": Hkv, "Lq": Lq, "Lk": Lk,
+                    "num_splits": S.attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, D, D),
+                    "attn_fwd_ms": round(ms_f, 4), "split_ms": round(ms_s, 4),
+                    "split_tflops": round(flops / (ms_s * 1e-3) / 1e12, 1)})
+        del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_crossover(lengths, topk=96, n_cols=1000, steps=3, warmup=2):
     """Dense causal attention (attn_fwd) against the dynamic sparse path (attn_build_sparse_index
     then attn_fwd_blocksparse on the built lists) as the sequence grows, at B 1, Hq 32, Hkv 8,
@@ -995,6 +1052,19 @@ def main():
         out["etap_grid"] = {"unit": "one attn_fwd_decode per step; TFLOP/s = 2*(576+512) per "
                                     "visible (query, key) pair; GB/s = latent cache + Q + O + LSE",
                             "points": bench_etap_grid(max(5, args.steps // 2), 3)}
+    if not args.no_crossover and args.only is None:
+        log("prefill shapes ...")
+        out["prefill_sweep"] = {
+            "op": "causal GQA prefill, D 128; TFLOP/s over the visible (query, key) pairs",
+            "points": bench_prefill_sweep([(1, 8, 2, 2048), (1, 8, 2, 8192), (1, 8, 2, 32768),
+                                           (1, 32, 8, 2048), (1, 32, 8, 4096), (4, 32, 8, 4096),
+                                           (1, 64, 8, 16384), (2, 32, 8, 32768)])}
+    if not args.no_crossover and args.only is None:
+        log("chunked prefill ...")
+        out["chunked_prefill"] = {
+            "op": "causal GQA prefill of a query chunk against a longer cache, D 128",
+            "points": bench_chunked_prefill([(1, 32, 8, 512, 32768), (1, 32, 8, 1024, 16384),
+                                             (4, 32, 8, 256, 16384)])}
     if not args.no_memory and args.only is None:
         log("peak memory at long sequence lengths ...")
         out["memory"] = {"op": "causal prefill B 1, Hq 32, Hkv 8, D 128",
