@@ -100,10 +100,10 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
  * Sizes: o_part is fp32 [S, B, Hq, Lq, Dv], lse_part is fp32 [S, B, Hq, Lq], both contiguous
  * DEVICE buffers owned by the caller. num_splits must lie in [1, ceil(Lk / 64)].
  * Supported head dims: (64, 64), (128, 128) and the MLA latent (576, 512).
- * Any Lq is accepted. With at least 128 query rows and D = 64 or 128 (a query chunk against a
- * longer cache: chunked prefill) the partials come from the prefill kernel run over each
- * split's keys; otherwise from the decode kernel (up to 32 query columns of a KV head per
- * workgroup). Both write the same partials.
+ * Any Lq is accepted. With D = 64 or 128 and at least 128 query rows, or 64 over at least 8192
+ * keys (a query chunk against a longer cache: chunked prefill), the partials come from the
+ * prefill kernel run over each split's keys; otherwise from the decode kernel (up to 32 query
+ * columns of a KV head per workgroup). Both write the same partials.
  */
 
 /* Split count the library would pick for MI355X (256 CUs): one round of workgroups over the

@@ -82,7 +82,7 @@ int decode_launch(const char* fn, const attn_tensor_t& q, const attn_tensor_t& k
                   const attn_tensor_t& v, const attn_tensor_t& o, float* lse, int B, int Hq,
                   int Hkv, int Lq, int Lk, int Dqk, int Dv, int causal, float scale, char* wb,
                   const attn::DecodeWorkspace& ws, hipStream_t sm) {
-  if (attn::dense_split_shape(Dqk, Dv, Lq)) {
+  if (attn::dense_split_shape(Dqk, Dv, Lq, Lk)) {
     // a prefill-shaped query block: the dense kernel, whole (one split) or in splits + combine
     if (ws.num_splits == 1) {
       attn::FwdArgs f;
@@ -231,7 +231,7 @@ int attn_fwd_splitkv(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, float* o
       return attn::fail(ATTN_ERR_WORKSPACE, fn, "o_part / lse_part is NULL");
     if ((reinterpret_cast<uintptr_t>(o_part) & 15u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u))
       return attn::fail(ATTN_ERR_WORKSPACE, fn, "o_part must be 16-byte and lse_part 4-byte aligned");
-    if (attn::dense_split_shape(Dqk, Dv, Lq))
+    if (attn::dense_split_shape(Dqk, Dv, Lq, Lk))
       return dense_split_launch(fn, q, k, v, o_part, lse_part, num_splits, B, Hq, Hkv, Lq, Lk,
                                 Dqk, causal, scale, static_cast<hipStream_t>(stream));
     attn::SplitArgs a;

@@ -103,7 +103,7 @@ int check_num_splits(const char* fn, int num_splits, int Lk) {
 int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   (void)Dv;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
-  if (dense_split_shape(Dqk, Dv, Lq)) {
+  if (dense_split_shape(Dqk, Dv, Lq, Lk)) {
     // the dense kernel's split form: one round of two 128-row workgroups per CU, splits of at
     // least 1024 keys, none empty
     const int64_t units = (int64_t)B * Hq * ((Lq + 127) / 128);

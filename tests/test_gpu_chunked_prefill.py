@@ -1,8 +1,9 @@
-"""GPU parity of split-KV over prefill-shaped query blocks (at least 128 query rows, D = 64 or
-128), which the library computes with the dense prefill kernel's split form: a short query
-chunk against a longer cache (chunked prefill, bottom-right causal), through attn_fwd_splitkv
-(the per-split partials, compared with the oracle's partials) and through the one-call
-attn_fwd_decode (split partials plus the LSE combine, or one split written directly)."""
+"""GPU parity of split-KV over prefill-shaped query blocks (D = 64 or 128; at least 128 query
+rows, or 64 over at least 8192 keys), which the library computes with the dense prefill
+kernel's split form: a short query chunk against a longer cache (chunked prefill, bottom-right
+causal), through attn_fwd_splitkv (the per-split partials, compared with the oracle's
+partials) and through the one-call attn_fwd_decode (split partials plus the LSE combine, or one
+split written directly)."""
 
 import numpy as np
 import pytest
@@ -28,6 +29,7 @@ def _qkv(B, Hq, Hkv, Lq, Lk, D, seed):
     (1, 4, 4, 129, 700, 128, True, 11),     # 64-key splits, the last one of 60 keys
     (1, 4, 2, 200, 256, 128, True, 3),      # 128-key splits: the third is empty
     (1, 8, 2, 400, 300, 128, True, 2),      # Lq > Lk: the first rows see no key at all
+    (1, 4, 1, 64, 8192, 64, False, 5),      # 64 rows over 8K keys: a half-filled row tile
 ], ids=lambda s: "x".join(map(str, s)))
 def test_dense_split_partials_match_oracle(shape):
     import torch
@@ -50,6 +52,7 @@ def test_dense_split_partials_match_oracle(shape):
     (2, 8, 2, 200, 3000, 64, True),
     (1, 16, 4, 1000, 1000, 128, True),      # square: one split, the prefill kernel directly
     (1, 8, 8, 150, 2500, 128, False),
+    (1, 8, 2, 100, 9000, 128, True),        # under 128 rows, over 8K keys: the split form too
 ], ids=lambda s: "x".join(map(str, s)))
 def test_chunked_prefill_one_call(shape):
     import torch
