@@ -28,7 +28,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 
 HEADLINE = "gqa_prefill_8k"
 # The headline's kernel (as rocprofv3 names it) and the sources its machine code comes from.
-DENSE_KERNEL = "fwd_dense_kernel<128, 1, 8>"
+DENSE_KERNEL = "fwd_dense_kernel<128, 1, 8, false>"
 DENSE_SOURCES = ["fwd_dense.hip", "tile_io.hpp", "common.hpp", "kernels.hpp"]
 # The sparse prefill kernels (block-sparse and vertical-slash) and their sources: their figure of
 # merit beside the MFMA fraction is the rate of their L2-miss traffic against the read ceiling.

@@ -13,7 +13,7 @@ factor = bytes the copy must move / bytes the counter reports for it.
 Usage (after the three rocprofv3 runs, see the header of each summary for the commands):
 
     python -m sparse_attention_attn_amd.profiling summary --stats DIR --fetch DIR --write DIR \
-        --calib-mib 1024 --kernel "fwd_dense_kernel<128, 1, 8>" --workload gqa_prefill_8k \
+        --calib-mib 1024 --kernel "fwd_dense_kernel<128, 1, 8, false>" --workload gqa_prefill_8k \
         --command "..." --out profiles/fwd_dense_kernel_gqa_prefill_8k.md [--traffic-json F]
 
 MFMA work and clock. One `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE
