@@ -1,7 +1,8 @@
 """Seeded sweep of random shapes through every forward entry point, each checked against the
 fp64 oracle element by element: dense prefill (attn_fwd), decode (attn_fwd_decode, GQA and the
-MLA latent shape), block-sparse (attn_fwd_blocksparse) and vertical-slash
-(attn_fwd_vertical_slash) over random lists. The shapes mix batch sizes, GQA ratios, ragged
+MLA latent shape), chunked prefill (attn_fwd_decode over query chunks of 64 to 700 rows),
+block-sparse (attn_fwd_blocksparse) and vertical-slash (attn_fwd_vertical_slash) over random
+lists. The shapes mix batch sizes, GQA ratios, ragged
 and tile-aligned lengths, Lq above and below Lk, D = 64 and 128, causal and not, so that the
 combinations the hand-picked cases do not list are covered too. Sizes stay small enough for
 the oracle to finish each case in well under a second."""
@@ -169,3 +170,30 @@ def test_random_vertical_slash(case):
     o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
                                  True, allowed_fn=fn)
     check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"random vertical-slash {case}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_chunked_prefill(case):
+    """A random query chunk against a longer cache through the one-call split path
+    (attn_fwd_decode): 64 to 700 query rows over up to 12000 keys, so both the prefill kernel's
+    split form and, for the shorter chunks over short caches, the decode kernel are drawn."""
+    import torch
+    import sparse_attention_attn_amd as S
+    rng = np.random.default_rng(500 + case)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    Lq = int(rng.integers(64, 701))
+    Lk = int(rng.integers(Lq, 12001))
+    causal = bool(rng.random() < 0.7)
+    nsp = S.attn_splitkv_num_splits(B, Hq, Hkv, Lq, Lk, D, D)
+    say(f"random chunked prefill {case}: B{B} Hq{Hq} Hkv{Hkv} Lq{Lq} Lk{Lk} D{D} "
+        f"causal={causal}, {nsp} splits")
+    q, k, v = _qkv(B, Hq, Hkv, Lq, Lk, D, 24000 + 10 * case)
+    o, lse = _outs(B, Lq, Hq, D)
+    S.attn_fwd_decode(q.to(DEV), k.to(DEV), v.to(DEV), o, lse, causal=causal, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
+                                 causal)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"random chunked prefill {case}")
