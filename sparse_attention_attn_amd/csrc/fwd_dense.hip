@@ -352,35 +352,24 @@ __device__ __forceinline__ void store_part(const FwdArgs& a, const WaveRows<D, N
 }
 
 // Maps blockIdx.x to a logical tile id. The hardware deals workgroups round-robin over the 8
-// XCDs: workgroup bid runs on XCD bid % 8 as its (bid / 8)-th. xcd_remap (set by the launcher,
-// grid a multiple of 8):
-//  0  no remap (logical id = bid);
-//  1  the (b, kv head) groups are a multiple of 8: XCD x takes the x-th eighth of the logical
-//     order, i.e. whole groups;
-//  X  (2, 4 or 8) there are 8 / X groups: each group's logical ids are dealt round-robin over
-//     X XCDs, so every XCD keeps one KV head and an equal share of its longest-first tiles.
-//     (Cutting a group's tiles into contiguous ranges gave one XCD the longest tiles and another
-//     the shortest: B 1, Hq 8, Hkv 2 at 32K tokens ran at 676 TFLOP/s.)
+// XCDs: workgroup bid runs on XCD bid % 8 as its (bid / 8)-th. The logical order is (b, KV head)
+// groups, each a run of longest-first tiles. xcd_remap = c (set by the launcher for grids that
+// are a multiple of 8; 0: no remap) splits the XCDs into clusters of c = 8 / gcd(groups, 8):
+// cluster i takes the i-th (c / 8) of the logical order, i.e. whole groups, and deals it
+// round-robin over its c XCDs. With 8, 16, ... groups every XCD holds whole groups (c = 1); with
+// 1, 2 or 4 each group spreads over 8, 4 or 2 XCDs; with 12 two XCDs share three groups. Every
+// XCD so gets the same mix of long and short tiles and as few KV heads as the counts allow.
+// (Cutting a group's tiles into contiguous ranges gave one XCD only the longest tiles and
+// another only the shortest: B 1, Hq 8, Hkv 2 at 32K tokens ran at 676 TFLOP/s.)
 __device__ __forceinline__ int logical_block_xcd(int xcd_remap) {
   const int bid = (int)blockIdx.x;
   const int n = (int)gridDim.x;
   if (xcd_remap == 0) return bid;
   const int x = bid & 7, k = bid >> 3;
-  if (xcd_remap == 1) return x * (n >> 3) + k;
-  const int X = xcd_remap;
-  return (x / X) * ((n >> 3) * X) + k * X + (x % X);
+  const int c = xcd_remap;
+  return (x / c) * ((n >> 3) * c) + k * c + (x % c);
 }
 
-// Logical order: (b, kv head) major so one XCD keeps one KV head's K/V in its L2, then query
-// tiles longest-first (causal work grows with the tile index), then the query heads of the
-// group.
-//
-// Pipeline. Keys are processed in 32-key units u (unit u = half u%2 of tile u/2). Step j issues
-// the MFMAs of Sᵀ(u = j+1) and of Oᵀ += Vᵀ(j-1)·Pᵀ(j-1), and the softmax of unit j. Score and
-// weight registers alternate between two sets by unit parity. Steps 2t-1 and 2t read K of tile
-// t and V of tile t-1: together they form the LDS pair t, held in stage t%2. Step 2t+1 (second
-// half of tile t) opens with the wait for pair t+1, the workgroup barrier, and the copy of pair
-// t+2 into the stage of pair t, whose last reader was step 2t.
 template <int D, int NR, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, wg_per_cu(NW)) void fwd_dense_kernel(const FwdArgs a) {
   using C = TileCfg<D>;
@@ -551,10 +540,9 @@ hipError_t launch_dense_nw(const FwdArgs& a, hipStream_t stream) {
   const int64_t nwg = (int64_t)a.B * a.Hq * aa.n_qtiles * (SPLIT ? a.num_splits : 1);
   if (nwg > 0x7fffffff) return hipErrorInvalidConfiguration;  // beyond one grid dimension
   const int64_t groups = (int64_t)a.B * a.Hkv;
-  aa.xcd_remap = (nwg % 8 != 0)    ? 0
-                 : (groups % 8 == 0) ? 1
-                 : (8 % groups == 0) ? (int)(8 / groups)
-                                     : 0;
+  int gcd8 = 8;
+  while (groups % gcd8 != 0) gcd8 >>= 1;  // gcd(groups, 8)
+  aa.xcd_remap = (nwg % 8 != 0) ? 0 : 8 / gcd8;
   hipLaunchKernelGGL((fwd_dense_kernel<D, kDenseNR, NW, SPLIT>), dim3((unsigned)nwg),
                      dim3(NW * 64), 0, stream, aa);
   return hipGetLastError();
