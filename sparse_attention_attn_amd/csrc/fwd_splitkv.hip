@@ -128,6 +128,23 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   // branches stay scalar
   kend = __builtin_amdgcn_readfirstlane(kend);
   const int ntiles = __builtin_amdgcn_readfirstlane(kend > kstart ? (kend - kstart + BNK - 1) / BNK : 0);
+  // Tile order. Workgroup (b, split) starts its walk at tile rot = ntiles * r / (B * S) of its
+  // split, r = b * S + split, and wraps around, so the workgroups running together read at
+  // positions spread evenly over their key ranges instead of all at the same offset of
+  // ranges that lie a fixed power-of-two apart. The result does not depend on the order (the
+  // masks and the ragged tail follow each tile's key position; the softmax takes no running
+  // maximum). Measured per call (rotating KV copies): 1 to 13% faster for D = 64 and for
+  // D = 128 with 8 or more KV heads. It was 2 to 8% slower for D = 128 with 2 or 4 KV heads
+  // and for the latent shape: those keep the plain order.
+  const bool spread = !C::MLA && (DQK == 64 || a.Hkv >= 8);
+  const int rot = __builtin_amdgcn_readfirstlane(
+      spread && ntiles > 0
+          ? (int)((((int64_t)b * a.num_splits + sp) * ntiles) / ((int64_t)a.B * a.num_splits))
+          : 0);
+  auto phys = [&](int t) {  // tile t of the walk -> tile index within the split
+    const int p = t + rot;
+    return p >= ntiles ? p - ntiles : p;
+  };
 
   // Qᵀ operand: lane l holds column l%16, head-dim elements 32*s + 8*(l/16) .. +7
   // With KSPLIT, wave w holds the reduction steps [qs0, qs1) only (4 or 5 of 18 for MLA).
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   // waits and barriers.
   auto issue = [&](auto S, int t) {
     const uint32_t st = lds_addr(stage(S));
-    const int base = kstart + t * BNK;
+    const int base = kstart + phys(t) * BNK;
     const bool tail = base + BNK - 1 > kmax;
     const uint16_t* kt = kb + (int64_t)base * a.k_sl;
     const uint16_t* vt = vb + (int64_t)base * a.v_sl;
@@ -218,7 +235,7 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
   auto compute = [&](auto S, int t) {
     const char* kt = stage(S);
     const char* vt = C::MLA ? kt : kt + C::KT_BYTES;
-    const int base = kstart + t * BNK;
+    const int base = kstart + phys(t) * BNK;
 
     // ---- Sᵀ: per column block, KBLK blocks of 16 keys x 16 columns
     f32x4 st[NCB][C::KBLK];

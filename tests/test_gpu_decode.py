@@ -80,6 +80,39 @@ def test_splitkv_partials_match_oracle_partials():
     assert bool(torch.isneginf(lp[2]).all()) and float(op[2].abs().max()) == 0.0
 
 
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, Lq, Lk, D, causal, splits
+    (3, 16, 8, 2, 2389, 128, True, 5),    # 8 KV heads: the walk starts mid-split; the ragged
+                                          # last tile (341 keys in the last split) and the
+                                          # causal edge come first or in the middle
+    (2, 8, 2, 3, 1000, 64, True, 4),      # D = 64 (any KV head count)
+    (4, 32, 8, 1, 4096 + 64 * 3 + 5, 128, False, 7),
+], ids=lambda s: "x".join(map(str, s)))
+def test_splitkv_partials_rotated_walk(shape):
+    """Workgroups of these shapes start their walk over the split's tiles at a tile that
+    depends on (batch, split) and wrap around; each split's partials still equal the oracle's
+    for that split's key range."""
+    import torch
+    import sparse_attention_attn_amd as S
+    B, Hq, Hkv, Lq, Lk, D, causal, splits = shape
+    say(f"partials, rotated walk {shape}")
+    seed = 8150 + Lk
+    q = randn_bf16((B, Lq, Hq, D), seed)
+    k = randn_bf16((B, Lk, Hkv, D), seed + 1)
+    v = randn_bf16((B, Lk, Hkv, D), seed + 2)
+    op = torch.full((splits, B, Hq, Lq, D), float("nan"), dtype=torch.float32, device=DEV)
+    lp = torch.full((splits, B, Hq, Lq), float("nan"), dtype=torch.float32, device=DEV)
+    S.attn_fwd_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), op, lp, causal=causal, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    op_ref, lp_ref = A.splitkv_partials(to_f64(q), to_f64(k), to_f64(v),
+                                        A.effective_scale(D ** -0.5), causal, splits)
+    check_parity(to_f64(op), op_ref, to_f64(lp), lp_ref, f"rotated walk {shape}")
+    o, lse = _decode(q.to(DEV), k.to(DEV), v.to(DEV), causal, D ** -0.5, num_splits=splits)
+    o_ref, lse_ref = A.attention(to_f64(q), to_f64(k), to_f64(v), A.effective_scale(D ** -0.5),
+                                 causal)
+    check_parity(to_f64(o), o_ref, to_f64(lse), lse_ref, f"rotated walk, combined {shape}")
+
+
 DECODE_SHAPES = [
     # B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal
     (2, 8, 8, 1, 1000, 128, 128, False),    # MHA, ragged Lk
