@@ -443,11 +443,15 @@ __global__ __launch_bounds__(256) void splitkv_kernel(const SplitArgs a) {
     }
     const int64_t prow = (((int64_t)sp * a.B + b) * a.Hq + hq[c]) * a.Lq + pos[c];
     float* op = a.o_part + prow * DV;
+    // Non-temporal stores: the partials are read once, by the combine launch, so they stream
+    // out instead of sitting dirty in this XCD's L2 until the end-of-kernel write-back (MLA
+    // 64K decode, 8 MB of partials: 112.6-113.0 -> 111.3-111.4 us per step; GQA unchanged).
 #pragma unroll
     for (int i = 0; i < C::DVB; ++i) {
       const int dv = w * C::DVW + 16 * i + 4 * G;
-      *reinterpret_cast<float4*>(op + dv) = make_float4(acc[c][i][0] * inv, acc[c][i][1] * inv,
-                                                        acc[c][i][2] * inv, acc[c][i][3] * inv);
+      const f32x4 val = {acc[c][i][0] * inv, acc[c][i][1] * inv, acc[c][i][2] * inv,
+                         acc[c][i][3] * inv};
+      __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(op + dv));
     }
     if (w == 0 && G == 0) a.lse_part[prow] = tf > 0.f ? m[c] * kLn2 + logf(tf) : -INFINITY;
   }
