@@ -179,7 +179,8 @@ def achievable_peaks():
     ms_ = out.get("mfma_stream", {}).get("tflops")
     out["achievable_mfma_tflops"] = max(gemm, ms_) if ms_ else round(gemm, 1)
     rc = out["read_ceilings"]
-    reads = [rc[k] for k in ("hbm_stream_read_gbs", "hbm_tile_gather_read_gbs") if k in rc]
+    reads = [rc[k] for k in ("hbm_stream_read_gbs", "hbm_tile_gather_read_gbs",
+                             "hbm_stream_nt_read_gbs", "hbm_tile_gather_nt_read_gbs") if k in rc]
     out["achievable_hbm_read_gbs"] = max(reads) if reads else round(copy, 1)
     return out
 
@@ -216,6 +217,10 @@ def _probe_lib():
     lib.probe_read_tiles.restype = i32
     lib.probe_read_rows.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp, vp]
     lib.probe_read_rows.restype = i32
+    lib.probe_read_tiles_nt.argtypes = lib.probe_read_tiles.argtypes
+    lib.probe_read_tiles_nt.restype = i32
+    lib.probe_read_rows_nt.argtypes = lib.probe_read_rows.argtypes
+    lib.probe_read_rows_nt.restype = i32
     lib.probe_mfma_stream.argtypes = [vp, i32, i32, vp, vp]
     lib.probe_mfma_stream.restype = i32
     return lib
@@ -227,7 +232,8 @@ def read_ceilings():
     (a stream: each XCD reads distinct tiles) or at seeded random tile positions, from a 2 GiB
     region (HBM) and from a 128 MiB region re-read launch after launch (two KV heads' K and V
     at 128K keys: larger than the eight 4 MiB L2s, inside the 256 MiB Infinity Cache).
-    2048 workgroups of 256 lanes, each reading 16 tiles one after another."""
+    2048 workgroups of 256 lanes, each reading 16 tiles one after another. The HBM reads are
+    also measured with the non-temporal cache policy (the decode kernels' copies use it)."""
     import torch
     lib = _probe_lib()
     grid, per_wg, tile = 2048, 16, 32 << 10
@@ -239,8 +245,11 @@ def read_ceilings():
     for region_name, region, steps in (("hbm", 2 << 30, 20), ("infinity_cache", 128 << 20, 50)):
         buf = torch.empty(region, dtype=torch.uint8, device="cuda:0")
         nreg = region // tile
-        for kind in ("stream", "tile_gather"):
-            if kind == "stream":
+        kinds = ("stream", "tile_gather", "stream_nt", "tile_gather_nt") if region_name == "hbm" \
+            else ("stream", "tile_gather")
+        for kind in kinds:
+            probe = lib.probe_read_tiles_nt if kind.endswith("_nt") else lib.probe_read_tiles
+            if kind.startswith("stream"):
                 # workgroup g (XCD g % 8) reads 16 consecutive tiles; the XCDs start 1/8 of the
                 # region apart, so no XCD reads a tile twice in a launch (its L2 never hits)
                 g_ = torch.arange(grid, dtype=torch.int64).repeat_interleave(per_wg)
@@ -251,8 +260,8 @@ def read_ceilings():
             ids = ids.to("cuda:0")
 
             def step():
-                rc = lib.probe_read_tiles(buf.data_ptr(), ids.data_ptr(), per_wg, grid, tile,
-                                          sink.data_ptr(), stream)
+                rc = probe(buf.data_ptr(), ids.data_ptr(), per_wg, grid, tile,
+                           sink.data_ptr(), stream)
                 if rc != 0:
                     raise RuntimeError(f"read probe launch failed: hipError {rc}")
 
@@ -359,19 +368,25 @@ def decode_read_floor(w, nsp, ks, vs, kv_bytes, steps, warmup):
         assert t.is_contiguous() and t.shape == (w.B, w.Lk, w.Hkv, w.Dqk)
     it = [0]
 
-    def step():
-        i = it[0] % len(ks)
-        it[0] += 1
-        rc = lib.probe_read_rows(ks[i].data_ptr(), vs[i].data_ptr() if vs else None,
-                                 base.data_ptr(), lid.numel(), chunk, row_bytes, stride,
-                                 sink.data_ptr(), stream)
-        if rc != 0:
-            raise RuntimeError(f"read probe launch failed: hipError {rc}")
+    def timed(probe):
+        def step():
+            i = it[0] % len(ks)
+            it[0] += 1
+            rc = probe(ks[i].data_ptr(), vs[i].data_ptr() if vs else None, base.data_ptr(),
+                       lid.numel(), chunk, row_bytes, stride, sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"read probe launch failed: hipError {rc}")
+        ms, _ = time_steps(step, steps, warmup)
+        return ms
 
-    ms, _ = time_steps(step, steps, warmup)
+    # the split kernel's copies take the non-temporal policy; the default policy for reference
+    ms = timed(lib.probe_read_rows_nt)
+    ms_default = timed(lib.probe_read_rows)
     return {"ms": round(ms, 4), "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1),
-            "probe": (f"probe_read_rows: {lid.numel()} workgroups x {chunk} rows of {row_bytes} B "
-                      f"at stride {stride} B" + (", K and V" if vs else ", latent only"))}
+            "ms_default_policy": round(ms_default, 4),
+            "probe": (f"probe_read_rows_nt: {lid.numel()} workgroups x {chunk} rows of "
+                      f"{row_bytes} B at stride {stride} B" +
+                      (", K and V" if vs else ", latent only") + ", non-temporal loads")}
 
 
 def bench_blocksparse(w, steps, warmup, dynamic=True):

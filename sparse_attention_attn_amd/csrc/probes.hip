@@ -12,6 +12,7 @@
 //
 // probe_read_rows: every workgroup reads strided rows of one or two buffers, as one split-KV
 // workgroup reads its keys' K and V rows; the decode kernels' step time is compared with it.
+// The _nt entry points make the same reads with the non-temporal cache policy.
 //
 // probe_mfma_stream: back-to-back bf16 MFMAs on random operands, the rate the matrix cores
 // sustain at the power limit (the prefill kernels' compute ceiling in practice).
@@ -30,29 +31,37 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr uint32_t kNever = 0x9e3779b9u;
 
-__device__ inline uint32_t fold(uint4 v) { return v.x ^ (v.y * 3u) ^ (v.z * 5u) ^ (v.w * 7u); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a register-operand type for asm
 __device__ inline uint32_t fold(u32x4 v) { return v.x ^ (v.y * 3u) ^ (v.z * 5u) ^ (v.w * 7u); }
 
+// A 16-byte load with the default cache policy, or (NT) the non-temporal one, which the
+// decode kernel's copies use.
+template <bool NT>
+__device__ inline u32x4 load16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // Tiles of tile16 16-byte chunks; workgroup g reads tiles ids[g * per_wg + t], t < per_wg.
-__global__ __launch_bounds__(kThreads) void read_tiles_kernel(const uint4* __restrict__ buf,
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void read_tiles_kernel(const u32x4* __restrict__ buf,
                                                               const int32_t* __restrict__ ids,
                                                               int per_wg, int tile16,
                                                               uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
   const int32_t* my = ids + (size_t)blockIdx.x * per_wg;
   for (int t = 0; t < per_wg; ++t) {
-    const uint4* tile = buf + (size_t)my[t] * tile16;
+    const u32x4* tile = buf + (size_t)my[t] * tile16;
     int j = threadIdx.x;
     for (; j + (kUnroll - 1) * kThreads < tile16; j += kUnroll * kThreads) {
-      uint4 v[kUnroll];
+      u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = tile[j + u * kThreads];
+      for (int u = 0; u < kUnroll; ++u) v[u] = load16<NT>(tile + j + u * kThreads);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) acc += fold(v[u]);
     }
-    for (; j < tile16; j += kThreads) acc += fold(tile[j]);
+    for (; j < tile16; j += kThreads) acc += fold(load16<NT>(tile + j));
   }
   if (acc == kNever) sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
@@ -65,6 +74,7 @@ __global__ __launch_bounds__(kThreads) void read_tiles_kernel(const uint4* __res
 // The index is clamped rather than the load made conditional, so the loads stay independent.
 constexpr int kRowsUnroll = 32;
 
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void read_rows_kernel(const char* __restrict__ a,
                                                              const char* __restrict__ b,
                                                              const int64_t* __restrict__ base,
@@ -86,8 +96,8 @@ __global__ __launch_bounds__(kThreads) void read_rows_kernel(const char* __restr
       const int jj = second ? rem - per_t : rem;
       const int r = jj / row16, c = jj - r * row16;
       const char* src = second ? b : a;
-      v[u] = *reinterpret_cast<const u32x4*>(src + b0 + (int64_t)(t * 64 + r) * stride +
-                                             (int64_t)c * 16);
+      v[u] = load16<NT>(reinterpret_cast<const u32x4*>(src + b0 + (int64_t)(t * 64 + r) * stride +
+                                                       (int64_t)c * 16));
     }
     // Every load of the batch is issued before the first fold waits for one: the empty asm
     // statements take the loaded registers as operands after a scheduling barrier, so the folds
@@ -153,8 +163,18 @@ int probe_read_tiles(const void* buf, const int32_t* ids, int per_wg, int grid, 
                      uint32_t* sink, void* stream) {
   if (!buf || !ids || !sink || grid <= 0 || per_wg <= 0 || tile_bytes <= 0 || tile_bytes % 16)
     return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(read_tiles_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
-                     (const uint4*)buf, ids, per_wg, tile_bytes / 16, sink);
+  hipLaunchKernelGGL(read_tiles_kernel<false>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, ids, per_wg, tile_bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// probe_read_tiles with non-temporal loads.
+int probe_read_tiles_nt(const void* buf, const int32_t* ids, int per_wg, int grid, int tile_bytes,
+                        uint32_t* sink, void* stream) {
+  if (!buf || !ids || !sink || grid <= 0 || per_wg <= 0 || tile_bytes <= 0 || tile_bytes % 16)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_tiles_kernel<true>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, ids, per_wg, tile_bytes / 16, sink);
   return (int)hipGetLastError();
 }
 
@@ -170,7 +190,18 @@ int probe_read_rows(const void* a, const void* b, const int64_t* base, int grid,
   if (!a || !base || !sink || grid <= 0 || nrows <= 0 || nrows % 64 || row_bytes <= 0 ||
       row_bytes % 16 || stride < row_bytes)
     return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(read_rows_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(read_rows_kernel<false>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const char*)a, (const char*)b, base, nrows, row_bytes / 16, stride, sink);
+  return (int)hipGetLastError();
+}
+
+// probe_read_rows with non-temporal loads (the cache policy of the decode kernel's copies).
+int probe_read_rows_nt(const void* a, const void* b, const int64_t* base, int grid, int nrows,
+                       int row_bytes, int64_t stride, uint32_t* sink, void* stream) {
+  if (!a || !base || !sink || grid <= 0 || nrows <= 0 || nrows % 64 || row_bytes <= 0 ||
+      row_bytes % 16 || stride < row_bytes)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_rows_kernel<true>, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                      (const char*)a, (const char*)b, base, nrows, row_bytes / 16, stride, sink);
   return (int)hipGetLastError();
 }
