@@ -645,12 +645,16 @@ hipError_t launch_splitkv(const SplitArgs& a, int dqk, int dv, hipStream_t strea
     if (split_cols(dqk, a.g * a.Lq) == 32) return launch_split_t<576, 512, 32, 4, 2>(a, stream);
     return launch_split_t<576, 512, 32, 4, 1>(a, stream);
   }
-  // D = 128: a 2-stage ring (64 KiB of LDS) so that two workgroups share a CU; measured on
-  // B 16, Hq 32, Hkv 8, Lk 4096 against 4 stages at one workgroup per CU: 49.7 vs 52.5 us.
+  // D = 128: grids of at most one workgroup per CU take a 4-stage ring of 32-key tiles (three
+  // tiles in flight); larger grids a 2-stage ring of 64-key tiles (64 KiB of LDS) so that two
+  // workgroups share a CU (split_ring32 states the rule and its measurements).
   const bool two = split_cols(dqk, a.g * a.Lq) == 32;
-  if (dqk == 128)
+  if (dqk == 128) {
+    const int64_t nwg = (int64_t)a.B * a.Hkv * a.ncolblk * a.num_splits;
+    if (split_ring32(dqk, a.g * a.Lq, nwg)) return launch_split_t<128, 128, 32, 4, 1>(a, stream);
     return two ? launch_split_t<128, 128, 64, 2, 2>(a, stream)
                : launch_split_t<128, 128, 64, 2, 1>(a, stream);
+  }
   return two ? launch_split_t<64, 64, 64, 4, 2>(a, stream)
              : launch_split_t<64, 64, 64, 4, 1>(a, stream);
 }

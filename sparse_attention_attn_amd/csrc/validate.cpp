@@ -100,31 +100,10 @@ int check_num_splits(const char* fn, int num_splits, int Lk) {
   return ATTN_OK;
 }
 
-int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
-  (void)Dv;
-  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
-  if (dense_split_shape(Dqk, Dv, Lq, Lk)) {
-    // the dense kernel's split form: one round of two 128-row workgroups per CU, splits of at
-    // least 1024 keys, none empty
-    const int64_t units = (int64_t)B * Hq * ((Lq + 127) / 128);
-    int64_t s = std::max<int64_t>(1, 512 / units);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, Lk / 1024));
-    s = std::min<int64_t>(s, 256);
-    const int chunk = split_chunk(Lk, (int)s);
-    return (int)((Lk + chunk - 1) / chunk);
-  }
-  const int g = Hq / Hkv;
-  const int cols = split_cols(Dqk, g * Lq);
-  const int64_t colblk = ((int64_t)g * Lq + cols - 1) / cols;
-  const int64_t units = (int64_t)B * Hkv * colblk;
-  // Grid size and keys per split, measured over B 1..64, 512..131072 keys and the three head
-  // shapes (GPU time per call, splits forced from 1 to 512): the best grids hold one round of
-  // two D = 128 workgroups per CU (512), one D = 64 or latent workgroup per CU (256); a split
-  // keeps at least one 64-key tile (two for the latent, whose 1152-byte rows make short splits
-  // pay for their partials), and more than 256 splits only adds combine work (B 1, one KV head,
-  // 131072 keys: 24.4 us at 256 splits, 26.1 at 512).
-  const int64_t grid = (Dqk == 128) ? 512 : 256;
-  const int min_keys = (Dqk == 576) ? 128 : 64;
+namespace {
+
+// Split count for `units` split-KV work units aiming at `grid` workgroups (see pick_num_splits).
+int splits_for_grid(int64_t units, int64_t grid, int Lk, int min_keys) {
   int64_t s = (grid + units - 1) / units;
   // A grid just past a whole number of rounds leaves a short last round (B 24 at D = 128:
   // 3 splits, 576 workgroups, 36.1 / 97.5 / 353.2 us at 1K / 4K / 16K keys). Take instead the
@@ -150,6 +129,41 @@ int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
   // splits are whole 64-key tiles: drop those the rounding of the split length leaves empty
   const int chunk = split_chunk(Lk, (int)s);
   return (int)((Lk + chunk - 1) / chunk);
+}
+
+}  // namespace
+
+int pick_num_splits(int B, int Hq, int Hkv, int Lq, int Lk, int Dqk, int Dv) {
+  (void)Dv;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (dense_split_shape(Dqk, Dv, Lq, Lk)) {
+    // the dense kernel's split form: one round of two 128-row workgroups per CU, splits of at
+    // least 1024 keys, none empty
+    const int64_t units = (int64_t)B * Hq * ((Lq + 127) / 128);
+    int64_t s = std::max<int64_t>(1, 512 / units);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, Lk / 1024));
+    s = std::min<int64_t>(s, 256);
+    const int chunk = split_chunk(Lk, (int)s);
+    return (int)((Lk + chunk - 1) / chunk);
+  }
+  const int g = Hq / Hkv;
+  const int cols = split_cols(Dqk, g * Lq);
+  const int64_t colblk = ((int64_t)g * Lq + cols - 1) / cols;
+  const int64_t units = (int64_t)B * Hkv * colblk;
+  // Grid size and keys per split, measured over B 1..64, 512..131072 keys and the three head
+  // shapes (GPU time per call, splits forced from 1 to 512): the best grids hold one round of
+  // one D = 64 or latent workgroup per CU (256); a split keeps at least one 64-key tile (two for
+  // the latent, whose 1152-byte rows make short splits pay for their partials), and more than
+  // 256 splits only adds combine work (B 1, one KV head, 131072 keys: 24.4 us at 256 splits,
+  // 26.1 at 512). D = 128 with one 16-column block per workgroup: one round of one workgroup
+  // per CU (the 4-stage ring of 32-key tiles, split_ring32) when the units fit it, else one
+  // round of two per CU (512, the 2-stage ring of 64-key tiles).
+  const int min_keys = (Dqk == 576) ? 128 : 64;
+  if (Dqk == 128 && cols == 16) {
+    const int s = splits_for_grid(units, 256, Lk, min_keys);
+    if (split_ring32(Dqk, g * Lq, units * s)) return s;
+  }
+  return splits_for_grid(units, Dqk == 128 ? 512 : 256, Lk, min_keys);
 }
 
 int split_chunk(int Lk, int num_splits) {

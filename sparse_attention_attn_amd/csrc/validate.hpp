@@ -34,6 +34,17 @@ int check_num_splits(const char* fn, int num_splits, int Lk);
 // heads, 8 heads with 4 query tokens, the latent shape with 2 tokens), 16 otherwise.
 inline int split_cols(int dqk, int ncols) { (void)dqk; return ncols > 16 ? 32 : 16; }
 
+// D = 128 split-KV grids of one 16-column block per workgroup and at most one workgroup per CU
+// (256) run the decode kernel with a 4-stage ring of 32-key tiles (64 KiB of LDS); larger grids
+// run it with a 2-stage ring of 64-key tiles, two workgroups per CU. Measured per call over
+// D = 128 decode shapes (B 1..64, 512..131072 keys): the 32-key ring at one round of one
+// workgroup per CU against the 64-key ring at its best grid, 2-15% faster (B 16, 4K keys: 48.1
+// -> 45.3 us at 2 splits instead of 4); at two workgroups per CU it is the slower one (B 64,
+// one split: 24.3 -> 26.2 us at 512 keys), and so it is with two column blocks per workgroup.
+inline bool split_ring32(int dqk, int ncols, int64_t nwg) {
+  return dqk == 128 && split_cols(dqk, ncols) == 16 && nwg <= 256;
+}
+
 // Split-KV of a prefill-shaped query block (D = 64 or 128; at least 128 query rows, or 64 over
 // at least 8192 keys): the dense kernel's split form computes the partials (128-row workgroups
 // per key range) instead of the decode kernel, whose workgroups take at most 32 query columns of

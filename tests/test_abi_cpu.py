@@ -161,10 +161,16 @@ def test_decode_entry_validation_and_workspace():
 
 
 def test_num_splits_heuristic_is_pure_and_in_range():
-    # the decode workloads: 128 (b, kv-head) units -> 4 splits (one round of two workgroups
-    # per CU); 8 units of MLA -> 32 splits
-    assert S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128) == 4
+    # the decode workloads: 128 (b, kv-head) units -> 2 splits (one round of one D = 128
+    # workgroup per CU, the 4-stage ring of 32-key tiles); 8 units of MLA -> 32 splits
+    assert S.attn_splitkv_num_splits(16, 32, 8, 1, 4096, 128, 128) == 2
     assert S.attn_splitkv_num_splits(8, 16, 1, 1, 65536, 576, 512) == 32
+    # D = 128 grids beyond one workgroup per CU keep the rule of two per CU (512 workgroups):
+    # 512 units -> one split; 192 units -> 8 splits (whole rounds of 512); two column blocks
+    # per workgroup (64 query columns per KV head) -> 32 splits over 16 units
+    assert S.attn_splitkv_num_splits(64, 32, 8, 1, 2048, 128, 128) == 1
+    assert S.attn_splitkv_num_splits(24, 32, 8, 1, 4096, 128, 128) == 8
+    assert S.attn_splitkv_num_splits(4, 64, 2, 2, 16384, 128, 128) == 32
     for args in [(1, 1, 1, 1, 1, 64, 64), (1, 8, 1, 1, 100, 128, 128), (64, 64, 8, 1, 30, 64, 64),
                  (1, 16, 1, 2, 1 << 20, 576, 512)]:
         s = S.attn_splitkv_num_splits(*args)
