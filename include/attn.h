@@ -106,8 +106,9 @@ int attn_fwd(attn_tensor_t q, attn_tensor_t k, attn_tensor_t v, attn_tensor_t o,
  * columns of a KV head per workgroup). Both write the same partials.
  */
 
-/* Split count the library would pick for MI355X (256 CUs): one round of workgroups over the
- * chip (two per CU for D = 128, one otherwise), or whole rounds when one round cannot be filled
+/* Split count the library would pick for MI355X (256 CUs): one round of one workgroup per CU
+ * (for D = 128 when the work units fit that round; otherwise, and with more than 16 query
+ * columns per KV head, one round of two per CU), or whole rounds when one round cannot be filled
  * exactly, each split at least one 64-key tile (two for the latent shape), at most 256 splits,
  * none empty; for query chunks of at least 128 rows, one round of two 128-row prefill
  * workgroups per CU with splits of at least 1024 keys. Pure function of its arguments; returns
